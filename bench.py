@@ -1,0 +1,307 @@
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = sd_verify_attn (append + causal attention over the paged cache)
+-> sd_lm_head -> sd_accept -> sd_kv_rollback, on one stream, over one batch
+of seeded synthetic inputs already resident in HBM.  The steps form a decode
+loop: each rollback advances seq_lens, so the next step appends after the
+accepted tokens (the logits repeat because the hidden rows are fixed).
+
+Prints one JSON line: verified positions/s (B*(K+1) per step) as `value`,
+accepted (emitted) tokens/s, per-call times from HIP events on the launch
+stream, the roofline fraction of the dominant call, and the CPU oracle timed
+on a bounded sample of the same workload on the host cores.
+
+Workloads (--config): 1 tiny fp32 greedy, 2 GQA bf16 sampling, 4 long-context
+top-p, 5 ragged paged serving batch (default; the largest configuration and
+the one the attention/LM-head roofline targets are stated on).  The draft
+model is out of scope: drafts are synthesised from the step's own target
+logits the way the workload recipe states (greedy requests copy the target
+argmax for a truncated-geometric prefix, sampled requests draw from
+softmax((logits + N(0, 0.5^2)) / T)).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=2)
+    return ap.parse_args()
+
+
+def attention_bytes(cfg, seq_lens_before):
+    """Algorithmic HBM bytes of one sd_verify_attn call: every cached and new
+    key/value read once, the new rows written once, q read, fp32 out written."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    B, NQ = cfg.batch, cfg.num_q
+    keys = float(np.sum(seq_lens_before.astype(np.float64) + NQ))
+    if cfg.mla:
+        kv = keys * cfg.d_qk * es
+        new = B * NQ * cfg.d_qk * es * 2
+    else:
+        kv = keys * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * es
+        new = B * NQ * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * es * 2
+    q = B * NQ * cfg.n_q_heads * cfg.d_qk * es
+    out = B * NQ * cfg.n_q_heads * cfg.d_v * 4
+    return kv + new + q + out
+
+
+def lm_head_work(cfg):
+    es = 2 if cfg.dtype == "bf16" else 4
+    M = cfg.batch * cfg.num_q
+    flops = 2.0 * M * cfg.hidden * cfg.vocab
+    byts = (cfg.vocab * cfg.hidden + M * cfg.hidden + M * cfg.vocab) * es
+    return flops, byts
+
+
+def synthesize_drafts(cfg, seed, logits_host_f32, temperature, top_p):
+    """Draft-model stand-in from the target logits (see module docstring)."""
+    import sdsynth
+    B, Q, V = logits_host_f32.shape
+    K = Q - 1
+    greedy = temperature == 0
+    drafts = np.full((B, K), -1, np.int32)
+    pd = np.zeros((B, K, V), np.float32)
+    if greedy.any():
+        tt = np.argmax(logits_host_f32, axis=-1)  # draft copies the target's top token
+        dg = sdsynth.greedy_drafts(tt, K, V, seed, p=cfg.geom_p)
+        drafts[greedy] = dg[greedy]
+    st = np.nonzero(~greedy)[0]
+    if len(st) and K > 0:
+        T = float(temperature[st[0]])
+        tp = float(top_p[st[0]])
+        pd_st = sdsynth.draft_probs(logits_host_f32[st, :K], seed, cfg.draft_noise, T, tp)
+        pd[st] = pd_st
+        drafts[st] = sdsynth.sample_drafts(pd_st, seed)
+    return drafts, pd
+
+
+def cpu_baseline(cfg, seed, wl, host_inputs, n_req):
+    """The oracle, as it stands, timed on a bounded sample of the workload:
+    the first n_req requests through append + attention, LM head, accept and
+    rollback.  Inputs were copied from the generator's tensors before any
+    library call touched them."""
+    import oracle
+    import sdsynth
+    t0 = time.perf_counter()
+    sel = host_inputs
+    timings = {}
+    B = n_req
+    Q = cfg.num_q
+    kc, vc = sel["k_cache"], sel["v_cache"]
+    s = time.perf_counter()
+    oracle.kv_append(sel["seq_lens"], sel["page_table"], sel["num_pages"], sel["k_new"],
+                     sel["v_new"], kc, vc, mla=cfg.mla)
+    ref_o = oracle.verify_attn(sel["q"], kc, vc, sel["page_table"], sel["seq_lens"],
+                               sel["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
+                               mla=cfg.mla)
+    timings["attention"] = time.perf_counter() - s
+    H = sel["H"] if sel["H"] is not None else ref_o.reshape(B * Q, -1)
+    W = sel["W"]
+    if H.dtype != W.dtype:
+        W = oracle.bf16_to_f64(W) if W.dtype == np.uint16 else W.astype(np.float64)
+        H = H.astype(np.float64)
+    s = time.perf_counter()
+    exact = oracle.lm_head(H, W)
+    timings["lm_head"] = time.perf_counter() - s
+    logits = (oracle.round_bf16(exact) if cfg.dtype == "bf16" else exact.astype(np.float32))
+    logits = logits.reshape(B, Q, cfg.vocab)
+    lf = oracle.bf16_to_f64(logits) if cfg.dtype == "bf16" else logits.astype(np.float64)
+    temp, top_p = wl.temperature[:B], wl.top_p[:B]
+    drafts, pd = synthesize_drafts(cfg, seed, lf.astype(np.float32), temp, top_p)
+    s = time.perf_counter()
+    acc = oracle.accept(logits, drafts, temp, top_p if (top_p < 1).any() else None, pd,
+                        wl.u_accept[:B], wl.u_sample[:B])
+    timings["accept"] = time.perf_counter() - s
+    s = time.perf_counter()
+    oracle.kv_rollback(sel["page_table"], acc["num_accepted"], sel["seq_lens"], cfg.K)
+    timings["rollback"] = time.perf_counter() - s
+    total = sum(timings.values())
+    return {"value": B * Q / total, "unit": "verified positions/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {B} request(s) of the same workload ({B * Q} positions) through "
+                      f"append+attention, LM head, accept and rollback; per-call seconds "
+                      + ", ".join(f"{k} {v:.3f}" for k, v in timings.items()),
+            "wall_s": time.perf_counter() - t0}
+
+
+def to_host(t):
+    """Oracle-format host copy: uint16 bit patterns for bf16, float32 otherwise."""
+    import torch
+    import sdsynth
+    if t.dtype == torch.bfloat16:
+        return sdsynth.bf16_bits(t)
+    return t.detach().contiguous().cpu().numpy()
+
+
+def gather_sample(cfg, wl, n_req):
+    """Host copies (oracle formats) of the first n_req requests' inputs, with
+    their pages renumbered into a compact pool."""
+    import torch
+    t = wl.tensors
+    Q = cfg.num_q
+    pt = wl.page_table[:n_req]
+    used = pt[pt >= 0]
+    remap = {int(p): i for i, p in enumerate(used.tolist())}
+    new_pt = np.vectorize(lambda x: remap.get(int(x), -1))(pt).astype(np.int32)
+    idx = torch.tensor(used, dtype=torch.long, device=t["k_cache"].device)
+    out = {"page_table": new_pt, "num_pages": len(used),
+           "seq_lens": wl.seq_lens[:n_req].copy(),
+           "q": to_host(t["q"][:n_req]), "k_new": to_host(t["k_new"][:n_req]),
+           "v_new": to_host(t["v_new"][:n_req]) if t["v_new"] is not None else None,
+           "k_cache": to_host(t["k_cache"].index_select(0, idx)),
+           "v_cache": to_host(t["v_cache"].index_select(0, idx)) if t["v_cache"] is not None else None,
+           "H": to_host(t["H"][: n_req * Q]) if "H" in t else None,
+           "W": to_host(t["W"])}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not "
+                                   "part of it (the sharding plan is documented in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import sdsynth
+    import speculative_decoding_sd_amd as sdv
+
+    sdv.lib()  # fail loudly if the HIP library is missing
+    cfg = sdsynth.CONFIGS[args.config]
+    if cfg.mla:
+        raise SystemExit("MLA verify attention is not built yet")
+    seed = sdsynth.config_seed(args.config)
+    dev = torch.device("cuda", 0)
+    extra = (args.warmup + args.steps + 2) * cfg.num_q
+    wl = sdsynth.make_workload(cfg, seed, device=dev, extra_tokens=extra)
+    sample = None
+    if not args.no_cpu_baseline:
+        sample = gather_sample(cfg, wl, args.cpu_sample_requests)
+    t = wl.tensors
+    L0 = wl.seq_lens.copy()
+    seq_lens = torch.tensor(wl.seq_lens, device=dev)
+    page_table = torch.tensor(wl.page_table, device=dev)
+    temp = torch.tensor(wl.temperature, device=dev)
+    top_p = torch.tensor(wl.top_p, device=dev) if (wl.top_p < 1).any() else None
+    ua = torch.tensor(wl.u_accept, device=dev)
+    us = torch.tensor(wl.u_sample, device=dev)
+    drafts = torch.full((cfg.batch, cfg.K), -1, dtype=torch.int32, device=dev)
+    pd = torch.zeros((cfg.batch, cfg.K, cfg.vocab), dtype=torch.float32, device=dev)
+    step = sdv.VerifyStep(q=t["q"], k_cache=t["k_cache"], v_cache=t["v_cache"],
+                          page_table=page_table, seq_lens=seq_lens, num_pages=wl.num_pages,
+                          max_seq_len=int(L0.max()) + extra - cfg.num_q,
+                          n_kv_heads=cfg.n_kv_heads, W=t["W"], drafts=drafts, temperature=temp,
+                          u_accept=ua, u_sample=us, k_new=t["k_new"], v_new=t["v_new"],
+                          mla=cfg.mla, d_v=cfg.d_v, H=t.get("H"), top_p=top_p,
+                          draft_probs=pd if (wl.temperature > 0).any() else None)
+    # Target logits of the first step -> synthetic drafts (outside the timed region).
+    step.attention()
+    step.lm_head()
+    torch.cuda.synchronize()
+    lg = step.logits.float().cpu().numpy()
+    d_h, pd_h = synthesize_drafts(cfg, seed, lg, wl.temperature, wl.top_p)
+    drafts.copy_(torch.from_numpy(d_h))
+    pd.copy_(torch.from_numpy(pd_h))
+    del lg, pd_h
+    seq_lens.copy_(torch.from_numpy(L0))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    L_start = seq_lens.cpu().numpy().copy()
+    names = ["attention", "lm_head", "accept", "rollback"]
+    calls = [step.attention, step.lm_head, step.accept, step.rollback]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    acc_total = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        for c, fn in enumerate(calls):
+            fn()
+            ev[k][c + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    per_call = {n: float(np.mean([ev[k][c].elapsed_time(ev[k][c + 1]) for k in range(args.steps)]))
+                for c, n in enumerate(names)}
+    ev_step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][4]) for k in range(args.steps)]))
+    L_end = seq_lens.cpu().numpy()
+    emitted = int(step.out_offsets[-1].item())
+    acc_total = (L_end - L_start).sum()  # j_b + 1 per request per step
+    n_err = int(step.dev_error.item())
+    ms = wall_ms
+    B, Q = cfg.batch, cfg.num_q
+    pos_per_s = B * Q / (ms * 1e-3)
+    tok_per_s = acc_total / args.steps / (ms * 1e-3)
+    # Rooflines per call (attention bytes at the mean lengths seen in the timed steps).
+    L_mid = (L_start + L_end) / 2.0
+    a_bytes = attention_bytes(cfg, L_mid)
+    f, lm_bytes = lm_head_work(cfg)
+    lm_bound = "mfma" if f / lm_bytes > MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    kernels = {
+        "attention": {"bound": "hbm", "achieved": a_bytes / (per_call["attention"] * 1e-3) / 1e9,
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes": a_bytes},
+        "lm_head": ({"bound": "mfma", "achieved": f / (per_call["lm_head"] * 1e-3) / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFS,
+                     "unit": "TFLOP/s", "flops": f}
+                    if lm_bound == "mfma" else
+                    {"bound": "hbm", "achieved": lm_bytes / (per_call["lm_head"] * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes": lm_bytes}),
+    }
+    for k, v in kernels.items():
+        v["frac"] = v["achieved"] / v["peak"]
+        v["ms"] = per_call[k]
+    dom = max(("attention", "lm_head"), key=lambda k: per_call[k])
+    roof = dict(kernels[dom])
+    roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],
+            "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": None}
+    line = {
+        "metric": "verified positions/sec", "value": pos_per_s, "unit": "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"C{args.config} {cfg.name}", "batch": B, "K": cfg.K,
+                   "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.d_qk, "kv_len": (int(cfg.seq_len) if cfg.seq_len
+                                                    else list(cfg.seq_len_range)),
+                   "mean_kv_len": float(L_mid.mean()), "hidden": cfg.hidden,
+                   "vocab": cfg.vocab, "temperature": cfg.temperature or cfg.mixed_modes,
+                   "top_p": cfg.top_p, "page_size": cfg.page_size},
+        "accepted_tokens_per_sec": tok_per_s,
+        "mean_emitted_per_request": acc_total / args.steps / B,
+        "event_ms_per_step": ev_step_ms,
+        "per_call_ms": per_call,
+        "roofline": roof,
+        "kernels": kernels,
+        "device_error": n_err,
+        "last_step_emitted": emitted,
+    }
+    if sample is not None:
+        line["cpu_baseline"] = cpu_baseline(cfg, seed, wl, sample, args.cpu_sample_requests)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

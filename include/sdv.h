@@ -1,0 +1,301 @@
+/*
+ * sdv.h -- C ABI of the MI355X (gfx950) speculative-decoding verify step.
+ *
+ * One verify step of a draft chain runs four calls on one HIP stream:
+ *   sd_verify_attn   append the K+1 new keys/values, causal attention of the
+ *                    root token plus K drafts over the paged KV cache
+ *   sd_lm_head       project every position's hidden vector to vocab logits
+ *   sd_accept        greedy longest-prefix match or rejection sampling, with
+ *                    the correction/bonus token and a packed token list
+ *   sd_kv_rollback   drop the rejected positions from the cache bookkeeping
+ *
+ * Pages cited (titles and sections; the text is Chinese):
+ *   [TRT-MTP]     TensorRT-LLM MTP implementation/optimisation article
+ *                 (makelele.cn/d/6983435): "背景" Fig. 1, "MTP Vanilla",
+ *                 "MTP Eagle", "基本實現方式" Fig. 4, "支持 MTP 的注意力機制".
+ *   [SD-PRACTICE] "推测解码与MTP：大模型推理加速的核心技术与工程实践"
+ *                 (mlqm.cn/news/1017475): s2.2, s2.3, s4.3, s4.4.
+ *   [CSDN-MTP]    CSDN article on the two meanings of "MTP"
+ *                 (gitcode.csdn.net/69b64a3354b52172bc617fab): "整体计算流程
+ *                 （以 K=3 草稿 Token 为例）" steps 2, 4, 5, 6; "回滚机制".
+ *   [VLLM-MTP]    "MPT (MTP, Multi-Token Prediction) 原理详解"
+ *                 (mqxn.cn/news/75683): s3 stages 3-4, s4, s5.
+ *
+ * Conventions shared by every call
+ *   - Pointers marked "device" are HIP device pointers; descriptors and size
+ *     outputs are host memory.  The caller owns every buffer; the library
+ *     allocates nothing and keeps no pointer after a call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and never synchronises the host.  Buffers must stay
+ *     alive until the stream has passed the call.
+ *   - Arrays are dense and row-major; element counts, not bytes, unless
+ *     stated.  Tensor data pointers must be 16-byte aligned; workspaces
+ *     256-byte aligned.
+ *   - Status codes: arguments are checked on the host before anything is
+ *     launched (SD_EINVAL, SD_EUNSUPPORTED, SD_EWORKSPACE); SD_EDEVICE
+ *     reports a HIP launch error.  sd_last_error() returns this thread's
+ *     text for the last non-OK status.  No exception crosses the ABI.
+ *   - Faults only the device can see (a bad page-table entry, a sequence
+ *     over capacity, an out-of-range draft id, non-finite logits, bad
+ *     sampling parameters) are OR-ed as SD_DERR_* bits into the optional
+ *     device int `dev_error` (clear it to 0 before the step) and make the
+ *     offending request produce the documented "invalid" outputs; the
+ *     kernels never read or write outside the buffers described here.
+ *   - Calls hold no global mutable state and are re-entrant across streams
+ *     when given distinct workspaces.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SD_ABI_VERSION 1
+
+/* status codes */
+#define SD_OK 0
+#define SD_EINVAL 1
+#define SD_EUNSUPPORTED 2
+#define SD_EWORKSPACE 3
+#define SD_EDEVICE 4
+
+/* element types */
+#define SD_F32 0
+#define SD_BF16 1
+
+/* attention layouts */
+#define SD_ATTN_GQA 0
+#define SD_ATTN_MLA 1
+
+/* device error bits */
+#define SD_DERR_PAGE 1          /* a page-table entry the step needs is out of range */
+#define SD_DERR_CAPACITY 2      /* L_b < 0, L_b > max_seq_len, or L_b+K+1 > max_pages*page_size */
+#define SD_DERR_TOKEN 4         /* a draft id >= vocab */
+#define SD_DERR_NONFINITE 8     /* a logits row with NaN/+inf or no finite entry */
+#define SD_DERR_PARAM 16        /* temperature < 0 or NaN; top_p <= 0 or NaN while sampling;
+                                   sampling with K > 0 but no draft_probs */
+#define SD_DERR_ACCEPT_COUNT 32 /* rollback given num_accepted > K */
+
+/* Version of this header the library was built from (SD_ABI_VERSION). */
+int sd_abi_version(void);
+
+/* Text of this thread's last non-OK status ("" if none).  Valid until the
+ * thread's next call into the library. */
+const char* sd_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Verify attention.
+ * [TRT-MTP] "支持 MTP 的注意力機制": in generation the chain gives K+1 input
+ * tokens per request and a causal mask over them is all the attention needs.
+ * [CSDN-MTP] step 2: the queries of the new tokens are batched into one
+ * matrix against the cached keys, softmax(Q K^T / sqrt(d_k)) V, and each
+ * new key/value is written into the cache as it is produced.
+ *
+ * For request b with cached length L_b = seq_lens[b]:
+ *   1. k_new/v_new row i is written to position L_b+i (i = 0..K) of the
+ *      paged cache (skipped when k_new is NULL: already appended);
+ *   2. query i of head h attends to positions 0 .. L_b+i (its own key
+ *      included):  out = softmax(scale * q k^T) v.
+ * seq_lens is read only; sd_kv_rollback advances it.
+ *
+ * Layouts (device; dtype = SD_BF16 or SD_F32 for q, k_new, v_new, caches):
+ *   q          [B][K+1][n_q_heads][d_qk]
+ *   GQA: k_new [B][K+1][n_kv_heads][d_qk],  v_new [B][K+1][n_kv_heads][d_v]
+ *        k_cache [num_pages][n_kv_heads][page_size][d_qk]
+ *        v_cache [num_pages][n_kv_heads][page_size][d_v]
+ *        query head h reads kv head h / (n_q_heads / n_kv_heads)
+ *   MLA: one latent row per position shared by every head; k_new
+ *        [B][K+1][d_qk], k_cache [num_pages][page_size][d_qk]; keys are the
+ *        whole latent row, values its first d_v entries; v_new and v_cache
+ *        must be NULL, n_kv_heads must be 1
+ *   page_table int32 [B][max_pages]: logical page p/page_size of request b
+ *        -> physical page; entries past the step's last position are unread
+ *   seq_lens   int32 [B]
+ *   out        float32 [B][K+1][n_q_heads][d_v]
+ *   out_lowp   optional, out rounded to nearest-even in `dtype`, laid out
+ *              [B*(K+1)][n_q_heads*d_v] (ready as LM-head input); may be NULL
+ * A request with a capacity or page-table fault gets NaN outputs.
+ *
+ * Supported: page_size 64; GQA bf16 with d_qk = d_v in {64, 128} and
+ * (n_q_heads/n_kv_heads)*(K+1) <= 64; GQA f32 with d_qk = d_v <= 256;
+ * MLA bf16 with d_qk = 576, d_v = 512.  Others return SD_EUNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+typedef struct sd_attn_desc {
+    int batch;
+    int num_q;          /* K + 1 */
+    int n_q_heads;
+    int n_kv_heads;
+    int d_qk;
+    int d_v;
+    int kind;           /* SD_ATTN_GQA or SD_ATTN_MLA */
+    int dtype;          /* SD_F32 or SD_BF16 */
+    int page_size;
+    int max_pages;      /* row length of page_table */
+    int num_pages;      /* pages in the physical pool */
+    int max_seq_len;    /* host upper bound on every L_b (sizes the launch) */
+    float softmax_scale;/* 0 selects 1/sqrt(d_qk) */
+    const void* q;
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    float* out;
+    void* out_lowp;
+    int32_t* dev_error; /* optional */
+} sd_attn_desc;
+
+/* Bytes of device workspace sd_verify_attn needs for this descriptor
+ * (depends on shapes and max_seq_len only). */
+int sd_verify_attn_workspace_size(const sd_attn_desc* d, size_t* bytes);
+
+/* Runs the append and the attention.  workspace: device, >= the size above,
+ * 256-byte aligned, contents need no initialisation. */
+int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * LM head.  [CSDN-MTP] step 4: the hidden vectors of all verified positions
+ * are stacked into one matrix and multiplied by the output-layer weights,
+ * mapping hidden size to vocabulary size: logits = H x W_o.
+ *   H      device [M][hidden]      (M = B*(K+1) rows)
+ *   W      device [vocab][hidden]  (one row per token)
+ *   logits device [M][vocab]; every element is sum_k H[m][k] W[v][k]
+ *          accumulated in float32 and stored in `dtype` (bf16: round to
+ *          nearest even).
+ * dtype: SD_BF16 or SD_F32 for all three.  hidden must be a multiple of 8.
+ * ---------------------------------------------------------------------- */
+int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const void* W,
+               void* logits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Acceptance.  [VLLM-MTP] s3 stages 3-4; [SD-PRACTICE] s2.3, s4.4;
+ * [TRT-MTP] Fig. 1.  Logits row i of request b predicts position i+1; draft
+ * n (1-based) is judged by row n-1.
+ *
+ * Greedy (temperature[b] == 0): t_i = argmax of row i, smallest id on ties;
+ *   draft n is accepted while d_n == t_{n-1}; the first mismatch ends the
+ *   chain; the final token is t_j.
+ * Sampling (temperature[b] > 0): p_t of row i is softmax(l / T) restricted,
+ *   when top_p[b] < 1, to the shortest prefix of tokens ordered by (logit
+ *   desc, id asc) whose mass reaches top_p, extended to every token tied
+ *   with the prefix's last logit, and renormalised.  Draft n is accepted
+ *   iff u_accept[b][n-1] < min(1, p_t(d_n) / p_d(d_n)) (row n-1 of both;
+ *   p_d = 0 counts as ratio +inf when p_t > 0, 0 when p_t = 0).  At the
+ *   first rejection the final token is drawn from norm(max(0, p_t - p_d))
+ *   of row n-1 (from p_t if that residual is all zero); if every draft is
+ *   accepted it is drawn from p_t of row K.  Draws take the smallest v whose
+ *   running sum over token ids exceeds u_sample[b][row] * (total); the
+ *   statistics and sums are kept in float64.
+ * A draft id < 0 ends the chain early (the final token is then drawn from,
+ *   or is the argmax of, the row that draft would have been judged by).
+ * Each request emits j_b + 1 tokens: accepted drafts, then the final token.
+ *
+ * Layouts (device):
+ *   logits       [B][K+1][vocab], logits_dtype SD_BF16 or SD_F32
+ *   draft_tokens int32 [B][K]
+ *   temperature  float32 [B]
+ *   top_p        float32 [B], or NULL: no nucleus filtering for any request
+ *   draft_probs  float32 [B][K][vocab] (row n-1 is the draft distribution
+ *                draft n was drawn from), or NULL when every request is greedy
+ *                or K == 0
+ *   u_accept, u_sample  float32 [B][K+1], uniforms in [0, 1)
+ * Outputs (device):
+ *   num_accepted int32 [B]         j_b, or -1 for an invalid request
+ *   out_tokens   int32 [B][K+1]    j_b+1 emitted tokens, then -1
+ *   next_token   int32 [B]         the final token (or -1)
+ *   out_offsets  int32 [B+1]       exclusive scan of emitted counts
+ *   packed_tokens int32 [B*(K+1)]  emitted tokens back to back, then -1
+ * Invalid requests (see SD_DERR_TOKEN/NONFINITE/PARAM) emit nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct sd_accept_desc {
+    int batch;
+    int K;
+    int vocab;
+    int logits_dtype;
+    const void* logits;
+    const int32_t* draft_tokens;
+    const float* temperature;
+    const float* top_p;
+    const float* draft_probs;
+    const float* u_accept;
+    const float* u_sample;
+    int32_t* num_accepted;
+    int32_t* out_tokens;
+    int32_t* next_token;
+    int32_t* out_offsets;
+    int32_t* packed_tokens;
+    int32_t* dev_error; /* optional */
+} sd_accept_desc;
+
+int sd_accept_workspace_size(const sd_accept_desc* d, size_t* bytes);
+
+/* workspace: device, >= sd_accept_workspace_size, 256-byte aligned. */
+int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * KV rollback.  [TRT-MTP] "MTP Vanilla"/"MTP Eagle": the keys/values of
+ * discarded drafts are cleared so later steps stay correct; "基本實現方式"
+ * Fig. 4: rollback is the one step run outside the engine forward.
+ * [CSDN-MTP] "回滚机制": the verified prefix is kept and nothing is
+ * recomputed.
+ *
+ * new_len = L_b + j_b + 1 (the root and the j_b accepted drafts stay).
+ * Positions new_len .. L_b+K are rejected.  j_b < 0 (an invalid request)
+ * keeps nothing of the step (new_len = L_b); j_b > K is treated the same
+ * and sets SD_DERR_ACCEPT_COUNT.
+ *
+ *   page_table   int32 [B][max_pages]  (read)
+ *   num_accepted int32 [B]             (read)
+ *   seq_lens     int32 [B]             (read L_b, write new_len)
+ *   rollback_slots   int32 [B*(K+1)]: physical slot page*page_size+offset
+ *                    of every rejected position, in (request, position)
+ *                    order; entries past the total are -1
+ *   rollback_offsets int32 [B+1]
+ *   freed_pages      int32 [B*(K/page_size+2)]: physical pages of the
+ *                    logical pages the step wrote that hold no kept position
+ *                    (logical page >= ceil(new_len/page_size)), in (request,
+ *                    logical page) order; entries past the total are -1
+ *   freed_offsets    int32 [B+1]
+ *   poison_rejected: when non-zero, the rejected slots of k_cache/v_cache
+ *                    (every kv head; the latent row for MLA) are zeroed;
+ *                    kind, dtype, n_kv_heads, d_k, d_v describe the caches
+ *                    exactly as in sd_attn_desc and are read only then.
+ * The page table itself is left unchanged: the caller returns freed pages
+ * to its pool.
+ * ---------------------------------------------------------------------- */
+typedef struct sd_rollback_desc {
+    int batch;
+    int K;
+    int page_size;
+    int max_pages;
+    const int32_t* page_table;
+    const int32_t* num_accepted;
+    int32_t* seq_lens;
+    int32_t* rollback_slots;
+    int32_t* rollback_offsets;
+    int32_t* freed_pages;
+    int32_t* freed_offsets;
+    int poison_rejected;
+    int kind;
+    int dtype;
+    int n_kv_heads;
+    int d_k;
+    int d_v;
+    int num_pages;
+    void* k_cache;
+    void* v_cache;
+    int32_t* dev_error; /* optional */
+} sd_rollback_desc;
+
+int sd_kv_rollback(const sd_rollback_desc* d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

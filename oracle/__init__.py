@@ -168,7 +168,7 @@ def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample):
     K = Q - 1
     drafts = _c(drafts, np.int32).reshape(B, K) if K > 0 else np.zeros((B, 0), np.int32)
     temperature = _c(temperature, np.float32)
-    top_p = _c(top_p, np.float32)
+    top_p = np.ones(B, np.float32) if top_p is None else _c(top_p, np.float32)
     draft_probs = _c(draft_probs, np.float32) if draft_probs is not None else None
     u_accept = _c(u_accept, np.float32)
     u_sample = _c(u_sample, np.float32)
@@ -183,6 +183,18 @@ def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample):
         _ptr(out["out_offsets"]), _ptr(out["packed"]), _ptr(out["diag"]))
     out["n_invalid"] = n_bad
     return out
+
+
+def argmax(logits):
+    """Greedy target token per row (smallest id on ties) and top-2 margin.
+    logits: [..., V]; returns (int32 [...], float64 [...])."""
+    logits = _c(logits)
+    V = logits.shape[-1]
+    n = logits.size // V
+    out = np.empty(n, np.int32)
+    mg = np.empty(n, np.float64)
+    lib().orc_argmax_rows(n, V, _dtype_code(logits), _ptr(logits), _ptr(out), _ptr(mg))
+    return out.reshape(logits.shape[:-1]), mg.reshape(logits.shape[:-1])
 
 
 def kv_rollback(page_table, num_accepted, seq_lens, K, *, page_size=64, poison=False,

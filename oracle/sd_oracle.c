@@ -312,6 +312,17 @@ static int row_argmax(const void* row, int dtype, int V, double* margin) {
     return best;
 }
 
+/* Greedy target token of each of n rows (smallest id among equal maxima,
+ * [SD-PRACTICE] s4.4 argmax rule) and its margin over the runner-up. */
+int orc_argmax_rows(int n, int V, int dtype, const void* logits, int* out, double* margin) {
+    size_t es = elem_size(dtype);
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < n; ++r)
+        out[r] = row_argmax((const char*)logits + (size_t)r * V * es, dtype, V,
+                            margin ? margin + r : NULL);
+    return ORC_OK;
+}
+
 /* A row the acceptance rule can use: no NaN or +inf, not all -inf. */
 static int row_valid(const void* row, int dtype, int V) {
     int finite = 0;
@@ -447,7 +458,7 @@ static int inverse_cdf(const double* r, int V, double u, double* edge) {
  * and the final token is drawn from p_t of that row.
  *
  * Invalid requests (temperature < 0 or NaN, top_p <= 0 or NaN when sampling,
- * a draft id >= V, a row with NaN/+inf or no finite entry) emit nothing:
+ * sampling with K > 0 but no draft distribution, a draft id >= V, a row with NaN/+inf or no finite entry) emit nothing:
  * num_accepted = next_token = -1 and all out_tokens -1.
  *
  * Outputs: num_accepted[B] = j_b; out_tokens[B][K+1] (first j_b+1 valid,
@@ -476,7 +487,7 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
         double dg[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
         int ok = !(isnan(T) || T < 0);
         if (ok && T > 0 && (isnan(tp) || tp <= 0)) ok = 0;
-        if (ok && T > 0 && !draft_probs) ok = 0;
+        if (ok && T > 0 && K > 0 && !draft_probs) ok = 0;
         for (int n = 0; ok && n < K; ++n)
             if (drafts[(size_t)b * K + n] >= V) ok = 0;
         for (int i = 0; ok && i < Q; ++i)

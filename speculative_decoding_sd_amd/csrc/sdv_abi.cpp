@@ -1,0 +1,31 @@
+// Library-wide entry points of libsdv: version and error text.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "sdv_internal.h"
+
+namespace sdv {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SD_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return SD_OK;
+}
+
+}  // namespace sdv
+
+extern "C" int sd_abi_version(void) { return SD_ABI_VERSION; }
+
+extern "C" const char* sd_last_error(void) { return sdv::g_last_error; }

@@ -1,0 +1,27 @@
+// Host-side helpers shared by the libsdv entry points (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sdv.h"
+
+namespace sdv {
+
+// Records a formatted message as this thread's last error and returns code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Clears this thread's last error.
+void clear_error();
+
+// SD_EDEVICE with the HIP error text if the last launch failed, else SD_OK.
+int check_launch(const char* what);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace sdv

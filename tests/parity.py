@@ -1,0 +1,103 @@
+"""Shared helpers of the GPU parity tests: moving synthetic inputs between
+torch and the oracle's numpy formats, and the tolerance rules.
+
+Tolerances (the rule each parity test applies):
+  attention (fp32 output): per output row (b, i, h), max |gpu - oracle| <=
+      2e-3 * max |oracle row|;
+  bf16 logits: |gpu - exact| <= max(2e-2, one bf16 spacing at |exact|), i.e.
+      within 2e-2 or a faithful rounding of the exact fp64 value where the
+      bf16 grid is coarser than 2e-2 (|x| >= 4);
+  fp32 logits: |gpu - exact| <= 1e-4;
+  integer outputs (accepted counts, token ids, offsets, slots, pages): equal;
+  sampling decisions: excluded only where the oracle's own diagnostics show
+      |u - min(1, p_t/p_d)| < 1e-3, an inverse-CDF draw within 1e-9 of a
+      bucket edge, or a top-p mass within 1e-9 of top_p.
+"""
+import numpy as np
+import torch
+
+import oracle
+import speculative_decoding_sd_amd as sdv
+
+DEV = torch.device("cuda", 0)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> host uint16 bit patterns (the oracle's bf16 format)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Oracle-format copy: uint16 bits for bf16, float32 otherwise."""
+    if t.dtype == torch.bfloat16:
+        return bits(t)
+    return t.detach().contiguous().cpu().numpy()
+
+
+def check_attention(out_gpu: np.ndarray, ref: np.ndarray, rel=2e-3, where=""):
+    o = out_gpu.reshape(-1, out_gpu.shape[-1]).astype(np.float64)
+    r = ref.reshape(-1, ref.shape[-1])
+    assert np.isfinite(o).all(), f"non-finite attention output {where}"
+    err = np.abs(o - r).max(axis=1)
+    scale = np.abs(r).max(axis=1)
+    bad = err > rel * scale
+    assert not bad.any(), (f"{where}: {bad.sum()} rows over tolerance; worst ratio "
+                           f"{(err / np.maximum(scale, 1e-30)).max():.3e}")
+    return float((err / np.maximum(scale, 1e-30)).max())
+
+
+def bf16_spacing(x: np.ndarray) -> np.ndarray:
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    e = np.floor(np.log2(ax))
+    return 2.0 ** (e - 7)
+
+
+def check_logits_bf16(gpu_bits: np.ndarray, exact: np.ndarray, where=""):
+    g = oracle.bf16_to_f64(gpu_bits).reshape(exact.shape)
+    tol = np.maximum(2e-2, bf16_spacing(exact))
+    err = np.abs(g - exact)
+    bad = err > tol
+    assert not bad.any(), f"{where}: {bad.sum()} logits over tolerance, max err {err.max():.4g}"
+    return float(err.max())
+
+
+def check_logits_f32(gpu: np.ndarray, exact: np.ndarray, atol=1e-4, where=""):
+    err = np.abs(gpu.astype(np.float64).reshape(exact.shape) - exact)
+    assert err.max() <= atol, f"{where}: max err {err.max():.3g}"
+    return float(err.max())
+
+
+def excluded_requests(diag: np.ndarray) -> np.ndarray:
+    """Requests whose sampling decision sits inside the exclusion windows."""
+    return (diag[:, 1] < 1e-3) | (diag[:, 2] < 1e-9) | (diag[:, 3] < 1e-9)
+
+
+def run_accept(logits_t, drafts_t, temp_t, top_p_t, pd_t, ua_t, us_t):
+    B, Q, V = logits_t.shape
+    i32 = dict(dtype=torch.int32, device=DEV)
+    out = dict(num_accepted=torch.full((B,), -7, **i32), out_tokens=torch.full((B, Q), -7, **i32),
+               next_token=torch.full((B,), -7, **i32), out_offsets=torch.full((B + 1,), -7, **i32),
+               packed_tokens=torch.full((B * Q,), -7, **i32))
+    err = torch.zeros(1, **i32)
+    d = sdv.accept_desc(logits=logits_t, draft_tokens=drafts_t, temperature=temp_t,
+                        u_accept=ua_t, u_sample=us_t, top_p=top_p_t, draft_probs=pd_t,
+                        dev_error=err, **out)
+    sdv.accept(d)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    res["dev_error"] = int(err.item())
+    return res
+
+
+def compare_accept(gpu: dict, ref: dict, allow_excluded=True, where=""):
+    excl = excluded_requests(ref["diag"]) if allow_excluded else np.zeros(len(ref["diag"]), bool)
+    keep = ~excl
+    for k_g, k_r in (("num_accepted", "num_accepted"), ("next_token", "next_token"),
+                     ("out_tokens", "out_tokens")):
+        g, r = gpu[k_g][keep], ref[k_r][keep]
+        assert np.array_equal(g, r), (f"{where}: {k_g} mismatch at requests "
+                                      f"{np.nonzero(keep)[0][np.any((g != r).reshape(len(g), -1), 1)][:10]}")
+    if not excl.any():
+        assert np.array_equal(gpu["out_offsets"], ref["out_offsets"]), where
+        assert np.array_equal(gpu["packed_tokens"], ref["packed"]), where
+    return int(excl.sum())

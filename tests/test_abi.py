@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every symbol include/sdv.h declares, and
+rejects bad arguments on the host before launching anything (CPU only: no
+call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_sd_amd as sdv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "sdv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("sd_verify_attn", "sd_lm_head", "sd_accept", "sd_kv_rollback"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = sdv.lib()
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(sdv.EXPORTS)
+
+
+def test_abi_version_matches_header():
+    src = open(os.path.join(ROOT, "include", "sdv.h")).read()
+    ver = int(re.search(r"#define SD_ABI_VERSION (\d+)", src).group(1))
+    assert sdv.lib().sd_abi_version() == ver
+
+
+def test_struct_layouts_match_header():
+    """Field names and order of the ctypes mirrors follow the C structs."""
+    src = open(os.path.join(ROOT, "include", "sdv.h")).read()
+    for struct, cls in (("sd_attn_desc", sdv.AttnDesc), ("sd_accept_desc", sdv.AcceptDesc),
+                        ("sd_rollback_desc", sdv.RollbackDesc)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), src, re.S).group(1)
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        fields = re.findall(r"(\w+)\s*;", body)
+        assert fields == [f[0] for f in cls._fields_], struct
+
+
+def _attn_desc(**kw):
+    base = dict(batch=2, num_q=4, n_q_heads=8, n_kv_heads=2, d_qk=128, d_v=128, kind=0, dtype=1,
+                page_size=64, max_pages=4, num_pages=8, max_seq_len=100, softmax_scale=0.0,
+                q=256, k_new=0, v_new=0, k_cache=512, v_cache=768, page_table=1024,
+                seq_lens=1280, out=1536, out_lowp=0, dev_error=0)
+    base.update(kw)
+    return sdv.AttnDesc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), sdv.SD_EINVAL),
+    (dict(n_q_heads=7), sdv.SD_EINVAL),
+    (dict(dtype=5), sdv.SD_EINVAL),
+    (dict(page_size=32), sdv.SD_EUNSUPPORTED),
+    (dict(d_qk=96, d_v=96), sdv.SD_EUNSUPPORTED),
+    (dict(max_seq_len=1000), sdv.SD_EINVAL),            # exceeds max_pages * 64
+    (dict(n_q_heads=64, n_kv_heads=2), sdv.SD_EUNSUPPORTED),  # 32 heads x 4 rows > 64
+])
+def test_attention_host_validation(kw, code):
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_verify_attn_workspace_size(_attn_desc(**kw))
+    assert e.value.code == code
+    assert sdv.last_error()
+
+
+def test_attention_workspace_and_pointer_checks():
+    d = _attn_desc()
+    n = sdv.sd_verify_attn_workspace_size(d)
+    assert n > 0 and n % 256 == 0
+    with pytest.raises(sdv.SdvError) as e:      # workspace too small
+        sdv.sd_verify_attn(d, 4096, n - 1, 0)
+    assert e.value.code == sdv.SD_EWORKSPACE
+    with pytest.raises(sdv.SdvError) as e:      # misaligned workspace
+        sdv.sd_verify_attn(d, 4096 + 8, n, 0)
+    assert e.value.code == sdv.SD_EINVAL
+    with pytest.raises(sdv.SdvError) as e:      # misaligned tensor
+        sdv.sd_verify_attn(_attn_desc(q=258), 4096, n, 0)
+    assert e.value.code == sdv.SD_EINVAL
+    with pytest.raises(sdv.SdvError) as e:      # NULL output
+        sdv.sd_verify_attn(_attn_desc(out=0), 4096, n, 0)
+    assert e.value.code == sdv.SD_EINVAL
+
+
+def test_lm_head_host_validation():
+    for args, code in [((0, 64, 10, 1, 16, 32, 48), sdv.SD_EINVAL),
+                       ((4, 60, 10, 1, 16, 32, 48), sdv.SD_EUNSUPPORTED),
+                       ((4, 64, 10, 3, 16, 32, 48), sdv.SD_EINVAL),
+                       ((4, 64, 10, 1, 0, 32, 48), sdv.SD_EINVAL),
+                       ((4, 64, 10, 1, 17, 32, 48), sdv.SD_EINVAL)]:
+        with pytest.raises(sdv.SdvError) as e:
+            sdv.sd_lm_head(*args, 0)
+        assert e.value.code == code
+
+
+def test_accept_and_rollback_host_validation():
+    d = sdv.AcceptDesc(batch=2, K=3, vocab=100, logits_dtype=1, logits=256, draft_tokens=512,
+                       temperature=768, top_p=0, draft_probs=0, u_accept=1024, u_sample=1280,
+                       num_accepted=1536, out_tokens=1792, next_token=2048, out_offsets=2304,
+                       packed_tokens=2560, dev_error=0)
+    n = sdv.sd_accept_workspace_size(d)
+    assert n >= 2 * 4 * 32
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_accept(d, 4096, n - 256, 0)
+    assert e.value.code == sdv.SD_EWORKSPACE
+    d.logits_dtype = 7
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_accept_workspace_size(d)
+    assert e.value.code == sdv.SD_EINVAL
+    r = sdv.RollbackDesc(batch=2, K=3, page_size=64, max_pages=4, page_table=0,
+                         num_accepted=256, seq_lens=512, rollback_slots=768,
+                         rollback_offsets=1024, freed_pages=1280, freed_offsets=1536)
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_kv_rollback(r, 0)
+    assert e.value.code == sdv.SD_EINVAL
+    r.page_table = 4096
+    r.poison_rejected = 1
+    with pytest.raises(sdv.SdvError) as e:     # poisoning without a cache description
+        sdv.sd_kv_rollback(r, 0)
+    assert e.value.code == sdv.SD_EINVAL

@@ -268,3 +268,11 @@ def test_rejection_sampling_is_lossless_chi2(orc, seed, T, top_p):
     ej = sum(np.prod(alpha[:n]) for n in range(1, K + 1))
     js = out["num_accepted"].astype(np.float64)
     assert abs(js.mean() - ej) < 4 * js.std() / math.sqrt(N)
+
+
+def test_argmax_rows_ties_and_margin(orc):
+    x = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, -1.0, 4.5, 5.0], [-np.inf, -2.0, -3.0, -2.5]],
+                 np.float32)
+    idx, mg = orc.argmax(x)
+    assert list(idx) == [1, 0, 1]
+    assert list(mg) == [0.0, 0.0, 0.5]
