@@ -85,8 +85,9 @@ __device__ double block_sum(double x, double* s4) {
     return r;
 }
 
-__device__ __forceinline__ double tempered(float x, float m, float T) {
-    return exp(((double)x - (double)m) / (double)T);
+// exp((x - m) / T) in fp64, with 1/T precomputed once per row.
+__device__ __forceinline__ double tempered(float x, float m, double invT) {
+    return exp(((double)x - (double)m) * invT);
 }
 
 template <typename T>
@@ -147,10 +148,11 @@ __global__ __launch_bounds__(256) void accept_rowstats(
     if (stoch && !flags) {
         double part = 0.0;
         const float m = best;
-        for_row(lr, V, vec_ok != 0, [&](float x, int) { part += tempered(x, m, Tb); });
+        const double invT = 1.0 / (double)Tb;
+        for_row(lr, V, vec_ok != 0, [&](float x, int) { part += tempered(x, m, invT); });
         z = block_sum(part, s_sum);
         const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
-        if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), m, Tb) / z;
+        if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), m, invT) / z;
     }
     if (threadIdx.x == 0) {
         RowStat st;
@@ -190,6 +192,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
     const uint16_t* lr = logits + (size_t)row * V;
     const double target = (double)tp * st.zkeep;
     const float m = st.m;
+    const double invT = 1.0 / (double)Tb;
     const int tid = threadIdx.x;
     double cum = 0.0;
     int lkey = -1;
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
             const int idx = tid * nl + j;
             const uint32_t c = s_hist[idx];
             if (c && top - idx >= bottom)
-                part += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, Tb);
+                part += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT);
         }
         s_part[tid] = part;
         __syncthreads();
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
                 const int idx = tid * nl + j;
                 const uint32_t c = s_hist[idx];
                 if (!c || top - idx < bottom) continue;
-                run += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, Tb);
+                run += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT);
                 last = top - idx;
                 at_last = run;
                 if (run >= target) break;
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
         out.pt_d = 0.0;
         if (d >= 0 && d < V) {
             const float xd = bf16_to_f32(lr[d]);
-            if (xd >= out.lambda) out.pt_d = tempered(xd, m, Tb) / out.zkeep;
+            if (xd >= out.lambda) out.pt_d = tempered(xd, m, invT) / out.zkeep;
         }
         stats[row] = out;
     }
@@ -284,6 +287,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
     const float* lr = logits + (size_t)row * V;
     const double target = (double)tp * st.zkeep;
     const float m = st.m;
+    const double invT = 1.0 / (double)Tb;
     // Invariant: mass(key >= lo) >= target, mass(key >= hi) < target.
     uint64_t lo = 0, hi = (uint64_t)f32_key(__float_as_uint(m)) + 1;
     double mass_lo = st.zkeep;
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
         const uint64_t mid = (lo + hi) / 2;
         double part = 0.0;
         for_row(lr, V, vec_ok != 0, [&](float x, int) {
-            if (f32_key(__float_as_uint(x)) >= mid) part += tempered(x, m, Tb);
+            if (f32_key(__float_as_uint(x)) >= mid) part += tempered(x, m, invT);
         });
         const double mass = block_sum(part, s_sum);
         if (mass >= target) {
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
         out.zkeep = mass_lo;
         const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
         out.pt_d = 0.0;
-        if (d >= 0 && d < V && lr[d] >= out.lambda) out.pt_d = tempered(lr[d], m, Tb) / out.zkeep;
+        if (d >= 0 && d < V && lr[d] >= out.lambda) out.pt_d = tempered(lr[d], m, invT) / out.zkeep;
         stats[row] = out;
     }
 }
@@ -315,23 +319,45 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
 enum { kModeInvalid = 0, kModeDone = 1, kModeResidual = 2, kModeTarget = 3 };
 
 // ---------------------------------------------------------------------------
-// Per-request decision and final-token draw.
+// Per-request decision and final-token draw.  One block of 1024 threads (16
+// waves) per request.  Thread 0 takes the sequential accept decision from the
+// row statistics.  A sampled final token is an inverse-CDF draw in token-id
+// order: wave w owns a contiguous run of ids, read 64 at a time (one id per
+// lane, coalesced); each 64-id chunk's fp64 weight sum is reduced in a fixed
+// lane order and kept in LDS.  A fixed-order scan over waves, then over the
+// crossing wave's chunks, finds the chunk whose running sum first exceeds
+// u * total; a lane-order prefix scan inside that chunk picks the token.
 // ---------------------------------------------------------------------------
+constexpr int kDecThreads = 1024;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kDecMaxChunks = 160;  // per wave: V <= 16 * 160 * 64 = 163840
+
 template <typename T>
-__global__ __launch_bounds__(256) void accept_decide(
+__device__ __forceinline__ double draw_weight(const T* lr, const float* pd, int v, bool resid,
+                                             float lambda, float m, double invT, double invZ) {
+    const float x = Logit<T>::at(lr, v);
+    const double p = (x >= lambda) ? tempered(x, m, invT) * invZ : 0.0;
+    if (!resid) return p;
+    const double r = p - (double)pd[v];
+    return r > 0.0 ? r : 0.0;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDecThreads) void accept_decide(
     const T* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ draft_probs,
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
     const RowStat* __restrict__ stats, int32_t* __restrict__ num_accepted,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_token, int32_t* err, int K,
     int V) {
-    __shared__ int s_mode, s_j, s_row, s_f;
-    __shared__ double s_u;
-    __shared__ double s_pre[257];
-    __shared__ int s_cand[4];
+    __shared__ int s_mode, s_j, s_row, s_f, s_wave, s_chunk;
+    __shared__ double s_u, s_pre, s_total;
+    __shared__ double s_wsum[kDecWaves];
+    __shared__ double s_chunk_sum[kDecWaves * kDecMaxChunks];
+    __shared__ int s_cand[kDecWaves];
     const int Q = K + 1;
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) {
         int flags = 0;
         for (int r = 0; r < Q; ++r) flags |= stats[(size_t)b * Q + r].flags;
@@ -385,79 +411,92 @@ __global__ __launch_bounds__(256) void accept_decide(
         const RowStat st = stats[(size_t)b * Q + row];
         const T* lr = logits + ((size_t)b * Q + row) * V;
         const float* pd = draft_probs ? draft_probs + ((size_t)b * K + row) * V : nullptr;
-        const float Tb = temperature[b];
-        // Contiguous chunk of token ids per thread, summed in id order.
-        const int per = (V + 255) / 256;
-        const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
-        auto weight = [&](int v, bool resid) -> double {
-            const float x = Logit<T>::at(lr, v);
-            const double p = (x >= st.lambda) ? tempered(x, st.m, Tb) / st.zkeep : 0.0;
-            if (!resid) return p;
-            const double r = p - (double)pd[v];
-            return r > 0.0 ? r : 0.0;
-        };
+        const double invT = 1.0 / (double)temperature[b];
+        const double invZ = 1.0 / st.zkeep;
+        const int nchunks = (V + 63) / 64;
+        const int cpw = (nchunks + kDecWaves - 1) / kDecWaves;  // chunks per wave
+        const int c_begin = wave * cpw, c_end = min(nchunks, c_begin + cpw);
         bool resid = mode == kModeResidual;
-        double part = 0.0;
-        for (int v = v0; v < v1; ++v) part += weight(v, resid);
-        s_pre[tid] = part;
-        __syncthreads();
-        if (tid == 0) {
-            double run = 0.0;
-            for (int t = 0; t < 256; ++t) {
-                const double p = s_pre[t];
-                s_pre[t] = run;
-                run += p;
+        for (int pass = 0; pass < 2; ++pass) {
+            double wsum = 0.0;
+            for (int c = c_begin; c < c_end; ++c) {
+                const int v = c * 64 + lane;
+                double w = v < V ? draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) : 0.0;
+                w = wave_sum(w);
+                if (lane == 0) s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = w;
+                wsum += w;
             }
-            s_pre[256] = run;
-        }
-        __syncthreads();
-        if (resid && s_pre[256] == 0.0) {  // residual empty: draw from p_t itself
-            resid = false;
-            __syncthreads();
-            part = 0.0;
-            for (int v = v0; v < v1; ++v) part += weight(v, false);
-            s_pre[tid] = part;
+            if (lane == 0) s_wsum[wave] = wsum;
             __syncthreads();
             if (tid == 0) {
-                double run = 0.0;
-                for (int t = 0; t < 256; ++t) {
-                    const double p = s_pre[t];
-                    s_pre[t] = run;
-                    run += p;
-                }
-                s_pre[256] = run;
+                double tot = 0.0;
+                for (int w = 0; w < kDecWaves; ++w) tot += s_wsum[w];
+                s_total = tot;
             }
             __syncthreads();
+            if (!(resid && s_total == 0.0)) break;
+            resid = false;  // residual empty: draw from p_t itself
+            __syncthreads();
         }
-        const double target = s_u * s_pre[256];
-        if (tid == 0) s_f = -1;
-        __syncthreads();
-        const double pre = s_pre[tid], nxt = s_pre[tid + 1];
-        if (pre <= target && nxt > target) {
-            double run = pre;
-            for (int v = v0; v < v1; ++v) {
-                run += weight(v, resid);
-                if (run > target) {
-                    s_f = v;
-                    break;
+        if (tid == 0) {
+            // Locate the first chunk whose running sum exceeds u * total.
+            const double target = s_u * s_total;
+            double run = 0.0;
+            int fw = -1, fc = -1;
+            for (int w = 0; w < kDecWaves && fw < 0; ++w) {
+                if (run + s_wsum[w] > target) {
+                    const int cb = w * cpw, ce = min(nchunks, cb + cpw);
+                    for (int c = cb; c < ce; ++c) {
+                        const double cs = s_chunk_sum[w * kDecMaxChunks + (c - cb)];
+                        if (run + cs > target) {
+                            fw = w;
+                            fc = c;
+                            break;
+                        }
+                        run += cs;
+                    }
+                    if (fw < 0) fw = -2;  // rounding: fall back below
+                } else {
+                    run += s_wsum[w];
                 }
             }
+            s_wave = fw;
+            s_chunk = fc;
+            s_pre = run;
         }
         __syncthreads();
-        if (s_f < 0) {
+        if (s_chunk >= 0 && wave == 0) {
+            const int v = s_chunk * 64 + lane;
+            const double w = v < V ? draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) : 0.0;
+            double incl = w;  // lane-order inclusive scan
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const double y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            const double target = s_u * s_total;
+            const bool hit = v < V && s_pre + incl > target;
+            const unsigned long long mask = __ballot(hit);
+            if (lane == 0) s_f = mask ? s_chunk * 64 + __ffsll((long long)mask) - 1 : -1;
+        }
+        __syncthreads();
+        if (s_chunk < 0 || s_f < 0) {
             // Rounding left no bucket above the target: the largest id with
             // positive weight.
             int cand = -1;
-            for (int v = v1 - 1; v >= v0; --v)
-                if (weight(v, resid) > 0.0) {
-                    cand = v;
-                    break;
-                }
-#pragma unroll
-            for (int msk = 32; msk >= 1; msk >>= 1) cand = max(cand, shfl_xor(cand, msk));
-            if ((tid & 63) == 0) s_cand[tid >> 6] = cand;
+            for (int c = c_end - 1; c >= c_begin && cand < 0; --c) {
+                const int v = c * 64 + lane;
+                const bool pos = v < V && draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) > 0.0;
+                const unsigned long long mask = __ballot(pos);
+                if (mask) cand = c * 64 + 63 - __clzll((long long)mask);
+            }
+            if (lane == 0) s_cand[wave] = cand;
             __syncthreads();
-            if (tid == 0) s_f = max(max(s_cand[0], s_cand[1]), max(s_cand[2], s_cand[3]));
+            if (tid == 0) {
+                int f = -1;
+                for (int w = 0; w < kDecWaves; ++w) f = max(f, s_cand[w]);
+                s_f = f;
+            }
             __syncthreads();
         }
     }
@@ -534,6 +573,8 @@ int check_accept(const sd_accept_desc* d) {
         return fail(SD_EINVAL, "sd_accept: unknown logits dtype %d", d->logits_dtype);
     if ((long)d->batch * (d->K + 1) > 0x7fffffffL)
         return fail(SD_EUNSUPPORTED, "sd_accept: too many rows");
+    if ((long)d->vocab > (long)kDecWaves * kDecMaxChunks * 64)
+        return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d", kDecWaves * kDecMaxChunks * 64);
     return SD_OK;
 }
 
@@ -580,7 +621,7 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
                 lg, d->draft_tokens, d->temperature, d->top_p, stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_bf16")) != SD_OK) return rc;
         }
-        accept_decide<uint16_t><<<B, 256, 0, s>>>(lg, d->draft_tokens, d->temperature,
+        accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(lg, d->draft_tokens, d->temperature,
                                                   d->draft_probs, d->u_accept, d->u_sample, stats,
                                                   d->num_accepted, d->out_tokens, d->next_token,
                                                   d->dev_error, K, V);
@@ -594,7 +635,7 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
                                                  stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_f32")) != SD_OK) return rc;
         }
-        accept_decide<float><<<B, 256, 0, s>>>(lg, d->draft_tokens, d->temperature,
+        accept_decide<float><<<B, kDecThreads, 0, s>>>(lg, d->draft_tokens, d->temperature,
                                                d->draft_probs, d->u_accept, d->u_sample, stats,
                                                d->num_accepted, d->out_tokens, d->next_token,
                                                d->dev_error, K, V);
