@@ -172,19 +172,29 @@ def _aligned(ws) -> int:
     return (p + 255) // 256 * 256
 
 
+def _keeping(tensors, desc):
+    """Attaches the tensors whose device pointers desc holds, so that they
+    stay allocated as long as the descriptor does (a temporary passed in would
+    otherwise return its memory to torch's caching allocator while the
+    descriptor still points at it)."""
+    desc._keep = tuple(t for t in tensors if t is not None)
+    return desc
+
+
 def attn_desc(*, q, k_cache, v_cache, page_table, seq_lens, out, n_kv_heads, num_pages,
               max_seq_len, k_new=None, v_new=None, mla=False, out_lowp=None,
               softmax_scale=0.0, dev_error=None, page_size=64) -> AttnDesc:
     B, NQ, Hq, dqk = q.shape
     d_v = out.shape[-1]
-    return AttnDesc(
+    return _keeping((q, k_cache, v_cache, page_table, seq_lens, out, k_new, v_new, out_lowp,
+                     dev_error), AttnDesc(
         batch=B, num_q=NQ, n_q_heads=Hq, n_kv_heads=n_kv_heads, d_qk=dqk, d_v=d_v,
         kind=SD_ATTN_MLA if mla else SD_ATTN_GQA, dtype=sd_dtype(q), page_size=page_size,
         max_pages=page_table.shape[1], num_pages=num_pages, max_seq_len=max_seq_len,
         softmax_scale=softmax_scale, q=_ptr(q), k_new=_ptr(k_new), v_new=_ptr(v_new),
         k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), page_table=_ptr(page_table),
         seq_lens=_ptr(seq_lens), out=_ptr(out), out_lowp=_ptr(out_lowp),
-        dev_error=_ptr(dev_error))
+        dev_error=_ptr(dev_error)))
 
 
 def verify_attn(desc: AttnDesc, ws=None, stream=None):
@@ -209,13 +219,15 @@ def accept_desc(*, logits, draft_tokens, temperature, u_accept, u_sample, num_ac
                 out_tokens, next_token, out_offsets, packed_tokens, top_p=None,
                 draft_probs=None, dev_error=None) -> AcceptDesc:
     B, Q, V = logits.shape
-    return AcceptDesc(
+    return _keeping((logits, draft_tokens, temperature, u_accept, u_sample, num_accepted,
+                     out_tokens, next_token, out_offsets, packed_tokens, top_p, draft_probs,
+                     dev_error), AcceptDesc(
         batch=B, K=Q - 1, vocab=V, logits_dtype=sd_dtype(logits), logits=_ptr(logits),
         draft_tokens=_ptr(draft_tokens), temperature=_ptr(temperature), top_p=_ptr(top_p),
         draft_probs=_ptr(draft_probs), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
         num_accepted=_ptr(num_accepted), out_tokens=_ptr(out_tokens),
         next_token=_ptr(next_token), out_offsets=_ptr(out_offsets),
-        packed_tokens=_ptr(packed_tokens), dev_error=_ptr(dev_error))
+        packed_tokens=_ptr(packed_tokens), dev_error=_ptr(dev_error)))
 
 
 def accept(desc: AcceptDesc, ws=None, stream=None):
@@ -233,14 +245,15 @@ def rollback_desc(*, page_table, num_accepted, seq_lens, K, rollback_slots, roll
                   mla=False, n_kv_heads=1, d_k=0, d_v=0, num_pages=0, dev_error=None,
                   page_size=64) -> RollbackDesc:
     dtype = sd_dtype(k_cache) if k_cache is not None else SD_BF16
-    return RollbackDesc(
+    return _keeping((page_table, num_accepted, seq_lens, rollback_slots, rollback_offsets,
+                     freed_pages, freed_offsets, k_cache, v_cache, dev_error), RollbackDesc(
         batch=seq_lens.shape[0], K=K, page_size=page_size, max_pages=page_table.shape[1],
         page_table=_ptr(page_table), num_accepted=_ptr(num_accepted), seq_lens=_ptr(seq_lens),
         rollback_slots=_ptr(rollback_slots), rollback_offsets=_ptr(rollback_offsets),
         freed_pages=_ptr(freed_pages), freed_offsets=_ptr(freed_offsets),
         poison_rejected=int(poison), kind=SD_ATTN_MLA if mla else SD_ATTN_GQA, dtype=dtype,
         n_kv_heads=n_kv_heads, d_k=d_k, d_v=d_v, num_pages=num_pages, k_cache=_ptr(k_cache),
-        v_cache=_ptr(v_cache), dev_error=_ptr(dev_error))
+        v_cache=_ptr(v_cache), dev_error=_ptr(dev_error)))
 
 
 def kv_rollback(desc: RollbackDesc, stream=None):

@@ -21,6 +21,15 @@ HIPCC_FLAGS = [
     "-I", os.path.join(HERE, "..", "include"),
 ]
 
+# Per-source extras.  attn_mla.hip keeps 256 fp32 accumulators plus the
+# resident Q^T fragments per lane: MFMA results in VGPRs (A/B operands may then
+# sit in AGPRs) is the register assignment that fits without spilling.  Its LDS
+# DMA sets M0 in inline asm; the kernel has no other M0 use, so the reserved-
+# register clobber warning is silenced there.
+EXTRA_FLAGS = {
+    "attn_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"],
+}
+
 
 def _hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -39,7 +48,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             continue
         obj = os.path.join(BUILD_DIR, src + ".o")
         objs.append(obj)
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", path, "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

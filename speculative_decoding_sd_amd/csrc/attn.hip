@@ -367,19 +367,25 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void attn_gqa_bf16(
 // M = max m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // Invalid requests get NaN rows.
 // ---------------------------------------------------------------------------
+constexpr int kCombineRows = 64;
 constexpr int kCombineCache = 8192;
 
+// grid (kv head, request, block of 64 rows).  With `direct_single`, requests
+// whose keys fit one chunk were written by the attention kernel already.
 __global__ __launch_bounds__(256) void attn_combine(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     float* __restrict__ out, uint16_t* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int G,
-    int R, int D, int chunk, int max_splits) {
-    __shared__ float s_m[64], s_inv[64];
+    int R, int D, int chunk, int max_splits, int direct_single) {
+    __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
     __shared__ float s_w[kCombineCache];
     const int kvh = blockIdx.x, b = blockIdx.y;
+    const int r0 = blockIdx.z * kCombineRows;
+    const int nr = min(kCombineRows, R - r0);
+    if (nr <= 0) return;
     if (!valid[b]) {
-        for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-            const int row = idx / D, d = idx - row * D;
+        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+            const int row = r0 + idx / D, d = idx % D;
             const int i = row / G, g = row - i * G;
             const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
             out[oi] = NAN;
@@ -388,8 +394,10 @@ __global__ __launch_bounds__(256) void attn_combine(
         return;
     }
     const int ns = (seq_lens[b] + NQ + chunk - 1) / chunk;
+    if (direct_single && ns == 1) return;
     const size_t pbase = ((size_t)b * Hkv + kvh) * max_splits;
-    for (int row = threadIdx.x; row < R; row += blockDim.x) {
+    for (int lr = threadIdx.x; lr < nr; lr += blockDim.x) {
+        const int row = r0 + lr;
         float M = -INFINITY;
         for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(pbase + s) * R + row].x);
         float den = 0.f;
@@ -397,29 +405,30 @@ __global__ __launch_bounds__(256) void attn_combine(
             const float2 ml = part_ml[(pbase + s) * R + row];
             if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
         }
-        s_m[row] = M;
-        s_inv[row] = 1.f / den;
+        s_m[lr] = M;
+        s_inv[lr] = 1.f / den;
     }
     __syncthreads();
-    const bool cached = ns * R <= kCombineCache;
+    const bool cached = ns * nr <= kCombineCache;
     if (cached) {
-        for (int idx = threadIdx.x; idx < ns * R; idx += blockDim.x) {
-            const int s = idx / R, row = idx - s * R;
-            const float m = part_ml[(pbase + s) * R + row].x;
-            s_w[idx] = (m == -INFINITY) ? 0.f : exp2f(m - s_m[row]) * s_inv[row];
+        for (int idx = threadIdx.x; idx < ns * nr; idx += blockDim.x) {
+            const int s = idx / nr, lr = idx - s * nr;
+            const float m = part_ml[(pbase + s) * R + r0 + lr].x;
+            s_w[idx] = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
         }
         __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
-        const int d = idx / R, row = idx - d * R;
+    for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+        const int d = idx / nr, lr = idx - d * nr;
+        const int row = r0 + lr;
         float acc = 0.f;
         for (int s = 0; s < ns; ++s) {
             float w;
             if (cached) {
-                w = s_w[s * R + row];
+                w = s_w[s * nr + lr];
             } else {
                 const float m = part_ml[(pbase + s) * R + row].x;
-                w = (m == -INFINITY) ? 0.f : exp2f(m - s_m[row]) * s_inv[row];
+                w = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
             }
             acc += w * part_o[((pbase + s) * D + d) * R + row];
         }
@@ -539,13 +548,23 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         return fail(SD_EINVAL, "sd_verify_attn: max_seq_len + num_q exceeds max_pages * page_size");
     p->G = d->n_q_heads / d->n_kv_heads;
     p->R = p->G * d->num_q;
-    if (d->kind == SD_ATTN_MLA) {
-        return fail(SD_EUNSUPPORTED, "sd_verify_attn: MLA is not built yet");
-    }
-    if (d->d_qk != d->d_v)
-        return fail(SD_EUNSUPPORTED, "sd_verify_attn: GQA needs d_qk == d_v");
     const long maxkeys = (long)d->max_seq_len + d->num_q;
-    if (d->dtype == SD_BF16) {
+    if (d->kind == SD_ATTN_MLA) {
+        if (d->dtype != SD_BF16 || d->d_qk != 576 || d->d_v != 512 || d->n_kv_heads != 1)
+            return fail(SD_EUNSUPPORTED,
+                        "sd_verify_attn: MLA needs bf16, d_qk 576, d_v 512, one kv head");
+        p->path = 2;
+        p->G = d->n_q_heads;
+        p->R = d->n_q_heads * d->num_q;
+        const int rc = mla_plan(d->batch, d->num_q, d->n_q_heads, d->max_seq_len, &p->chunk,
+                                &p->max_splits);
+        if (rc != SD_OK) return rc;
+    }
+    if (d->kind == SD_ATTN_MLA) {
+        // planned above
+    } else if (d->d_qk != d->d_v) {
+        return fail(SD_EUNSUPPORTED, "sd_verify_attn: GQA needs d_qk == d_v");
+    } else if (d->dtype == SD_BF16) {
         if (d->d_qk != 64 && d->d_qk != 128)
             return fail(SD_EUNSUPPORTED, "sd_verify_attn: bf16 GQA needs head dim 64 or 128");
         if (p->R > 64)
@@ -567,7 +586,8 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
     p->off_valid = off;
     off = align_up(off + sizeof(int32_t) * d->batch, 256);
     p->off_po = off;
-    const size_t nparts = (size_t)d->batch * d->n_kv_heads * p->max_splits * p->R;
+    const size_t nparts = (size_t)d->batch * d->n_kv_heads *
+                          (p->path == 2 && p->max_splits == 1 ? 0 : p->max_splits) * p->R;
     off = align_up(off + nparts * d->d_v * sizeof(float), 256);
     p->off_pml = off;
     off = align_up(off + nparts * sizeof(float2), 256);
@@ -600,6 +620,8 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         return fail(SD_EINVAL, "sd_verify_attn: NULL q/k_cache/page_table/seq_lens/out");
     if (d->kind == SD_ATTN_GQA && (!d->v_cache || (d->k_new && !d->v_new)))
         return fail(SD_EINVAL, "sd_verify_attn: GQA needs v_cache (and v_new with k_new)");
+    if (d->kind == SD_ATTN_MLA && (d->v_cache || d->v_new))
+        return fail(SD_EINVAL, "sd_verify_attn: MLA takes the latent in k_cache/k_new only");
     if (!aligned16(d->q) || !aligned16(d->k_cache) || (d->v_cache && !aligned16(d->v_cache)) ||
         (d->k_new && !aligned16(d->k_new)) || (d->v_new && !aligned16(d->v_new)) ||
         (d->out_lowp && !aligned16(d->out_lowp)) || !aligned16(d->out))
@@ -637,6 +659,15 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     float* po = (float*)(ws + p.off_po);
     float2* pml = (float2*)(ws + p.off_pml);
     const float scale_log2 = scale * 1.4426950408889634f;
+    if (p.path == 2) {
+        if ((rc = mla_launch(d, valid, po, pml, p.chunk, p.max_splits, scale_log2, s)) != SD_OK)
+            return rc;
+        if (p.max_splits == 1) return SD_OK;
+        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows), 256, 0, s>>>(
+            po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads, 1,
+            p.G, p.R, d->d_v, p.chunk, p.max_splits, 1);
+        return check_launch("attn_combine");
+    }
     const dim3 grid(p.max_splits, d->n_kv_heads, B);
 #define SDV_LAUNCH_GQA(DD, RBB)                                                                  \
     attn_gqa_bf16<DD, RBB><<<grid, 256, 0, s>>>(                                                 \
@@ -650,8 +681,8 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     }
 #undef SDV_LAUNCH_GQA
     if ((rc = check_launch("attn_gqa_bf16")) != SD_OK) return rc;
-    attn_combine<<<dim3(d->n_kv_heads, B), 256, 0, s>>>(
+    attn_combine<<<dim3(d->n_kv_heads, B, (p.R + kCombineRows - 1) / kCombineRows), 256, 0, s>>>(
         po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
-        d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits);
+        d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0);
     return check_launch("attn_combine");
 }

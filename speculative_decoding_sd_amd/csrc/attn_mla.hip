@@ -1,0 +1,329 @@
+// MLA-shaped verify attention on gfx950 (one latent vector per position shared
+// by every query head; keys are the whole 576-wide latent row, values its first
+// 512 entries).  [TRT-MTP] "支持 MTP 的注意力機制": K+1 queries per request
+// under a causal mask (the article's Hopper kernel for this case is FP8
+// FlashMLA); [CSDN-MTP] "整体计算流程" step 2: softmax(QK^T/sqrt(d))V.
+//
+// With 128 query heads and K+1 = 4 positions a request has 512 query rows
+// that all read the same latent rows, so this path is bound by the MFMA pipe,
+// not by HBM (about 970 flop per latent byte).  Layout of the work:
+//   workgroup = 128 query rows of one request x one chunk of keys, 4 waves;
+//   wave      = 32 rows (one position i, 32 heads) and all 512 output dims,
+//               O^T in 16 MFMA 32x32 accumulators (256 AGPRs), Q^T of its
+//               rows resident in 144 VGPRs for the whole chunk.
+// Per 32-key tile:
+//   S^T = K Q^T   A = latent rows read from LDS with ds_read_b128, B = Q^T;
+//   online softmax lane-local (one query row per lane column).  The running
+//                 max is only raised when a tile's max exceeds it by more than
+//                 2^8, so the O rescale (256 accumulators) is rare; values of
+//                 P up to 2^8 are exact enough in the bf16 hi+lo split below;
+//   O^T += V^T P^T  A = V^T fragments read with ds_read_b64_tr_b16 (gfx950
+//                 transposing LDS read: in a group of 16 lanes, lane t receives
+//                 element t%4 of the 8-byte reads of lanes 4e + t/4, so lane s
+//                 reading 4 dims of key row key0 + s/4 gives lane t the 4-key
+//                 column of dim d0 + t); P split into bf16 hi + lo halves (two
+//                 MFMAs per fragment) to hold the fp32 output accuracy.
+// Latent tiles arrive by LDS DMA (global_load_lds_dwordx4) three tiles deep,
+// so no registers stage them.  The 16-byte chunks of each 1152-byte latent row
+// are XOR-swizzled so that both LDS read patterns are free of bank conflicts.
+// With one chunk per request the kernel writes the normalised output itself;
+// otherwise it writes chunk partials for attn_combine.
+#include <math.h>
+
+#include "sdv_device.h"
+#include "sdv_internal.h"
+
+namespace sdv {
+
+namespace {
+
+constexpr int kPage = 64;
+constexpr int kDqk = 576, kDv = 512;
+constexpr int kTileKeys = 32;
+constexpr int kRowChunks = kDqk / 8;                       // 72 chunks of 16 bytes
+constexpr int kRowBytes = kDqk * 2;                        // 1152
+constexpr int kTileElems = kTileKeys * kDqk;               // 18432 bf16 = 36 KiB
+constexpr int kStages = 3;
+constexpr int kDmaPerWave = kTileKeys * kRowChunks / 256;  // 9 x 1 KiB per wave
+constexpr float kRescaleSlack = 8.f;                       // log2 units
+constexpr int kRowsPerBlock = 128;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// XOR applied to the chunk index of latent row `key` (0..7, so chunks 0..63
+// and 64..71 each stay in their own range).
+__device__ __forceinline__ int chunk_xor(int key) { return 2 * (key & 3) + ((key >> 2) & 1); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte-per-lane LDS DMA: lane l's 16 bytes from gptr land at LDS byte
+// address m0 + 16 l.  Issued from inline asm so that the compiler does not see
+// the LDS write (it would otherwise wait for every DMA in flight before each
+// LDS read); callers order it with explicit vmcnt waits and barriers.  Nothing
+// else in this kernel uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ u32x2 lds_tr16(const char* p) {
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// bf16 bits of two finite floats (lo in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_finite(float lo, float hi) {
+    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    a += 0x7fffu + ((a >> 16) & 1u);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(256, 1) void attn_mla_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ valid, float* __restrict__ out, uint16_t* __restrict__ out_lowp,
+    float* __restrict__ part_o, float2* __restrict__ part_ml, int NQ, int Hq, int R,
+    int max_pages, int chunk, int max_splits, int rblks, int total, float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s_lat[kStages][kTileElems];
+    const int tile_id = xcd_tile(blockIdx.x, total);
+    const int rblk = tile_id % rblks;
+    const int split = (tile_id / rblks) % max_splits;
+    const int b = tile_id / rblks / max_splits;
+    if (!valid[b]) return;
+    const int L = seq_lens[b];
+    const int Ltot = L + NQ;
+    const int start = split * chunk;
+    if (start >= Ltot) return;
+    const int end = min(start + chunk, Ltot);
+    const int ntiles = (end - start + kTileKeys - 1) / kTileKeys;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ln = lane & 31, lh = lane >> 5;
+    const int row0 = rblk * kRowsPerBlock + wave * 32;  // the wave's 32 rows share position i
+    const bool rows_live = row0 < R;
+    const int pos_i = rows_live ? row0 / Hq : 0;
+    const int lim = L + pos_i;  // causal: keys 0 .. L_b + i
+
+    // Q^T fragments (B operand): lane (row ln, half lh), step s -> dims 16s+8lh..+8.
+    u32x4 qf[kDqk / 16];
+    if (rows_live) {
+        const int row = row0 + ln;
+        const int i = row / Hq, h = row - i * Hq;
+        const uint16_t* qp = q + (((size_t)b * NQ + i) * Hq + h) * kDqk + 8 * lh;
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) qf[s] = *(const u32x4*)(qp + 16 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
+    }
+
+    // DMA slots of this lane: instruction j of wave w fills LDS chunks
+    // n = 64 (4j + w) + lane of the tile; chunk n holds latent row n / 72,
+    // logical chunk (n % 72) ^ chunk_xor(row).
+    int goff[kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+        const int n = 64 * (4 * j + wave) + lane;
+        const int key = n / kRowChunks;
+        goff[j] = key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
+    }
+    const uint32_t lds0 = lds_addr(&s_lat[0][0]);
+    auto issue_tile = [&](int t) {
+        const int ks = start + kTileKeys * t;
+        const int pg = page_table[(size_t)b * max_pages + ks / kPage];
+        const uint16_t* base = lat + ((size_t)pg * kPage + (ks % kPage)) * kDqk;
+        const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileElems * 2);
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j)
+            dma16(base + goff[j],
+                  __builtin_amdgcn_readfirstlane(dst + (uint32_t)(1024 * (4 * j + wave))));
+    };
+
+    // Per-lane LDS byte offsets within a tile.
+    //  S^T reads: key ln, logical chunk 2s + lh -> slot 8(s/4) + (2(s%4) ^ kx).
+    const int kx = lh ^ chunk_xor(ln);
+    int koff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) koff[r] = ln * kRowBytes + 16 * ((2 * r) ^ kx);
+    //  V^T reads (16-lane group g, lane sl): key 16tt + 4(g/2) + sl/4 (+8),
+    //  logical chunk 4db + 2(g&1) + (sl&3)/2, byte 8(sl&1) of the chunk.
+    const int g = lane >> 4, sl = lane & 15;
+    const int vx = (2 * (g & 1) + ((sl & 3) >> 1)) ^ (2 * (sl >> 2) + ((g >> 1) & 1));
+    const int vrow = (4 * (g >> 1) + (sl >> 2)) * kRowBytes + 8 * (sl & 1);
+    const int voff_e = vrow + 16 * vx, voff_o = vrow + 16 * (4 ^ vx);
+
+    float m_r = -INFINITY, l_r = 0.f;
+    f32x16 o[kDv / 32];
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t has landed once at most the next tile's DMAs are in flight.
+        if (t + 1 < ntiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+        barrier_only();
+        // Stage (t+2)%3 was last read in iteration t-1, which every wave has
+        // left through the barrier above.
+        if (t + 2 < ntiles) issue_tile(t + 2);
+        const char* tile = (const char*)&s_lat[t % kStages][0];
+        const int ks = start + kTileKeys * t;
+        if (t == ntiles - 1 && end - ks < kTileKeys) {
+            // Rows past the chunk end may hold anything (NaN included): zero
+            // their value dims so that P = 0 contributes exactly nothing.
+            const int nv = end - ks;
+            for (int idx = tid; idx < (kTileKeys - nv) * 64; idx += 256) {
+                const int key = nv + (idx >> 6), c = idx & 63;
+                *(u32x4*)(tile + key * kRowBytes + 16 * (c ^ chunk_xor(key))) = u32x4{0, 0, 0, 0};
+            }
+            __syncthreads();
+        }
+        if (!rows_live) continue;
+
+        // S^T = K Q^T over 576 dims (one accumulator: with 256 output
+        // accumulators a second one does not fit the register file).
+        f32x16 sa;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s)
+            sa = mfma_32x32x16(*(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2)), qf[s], sa);
+        // Online softmax (lane holds 16 keys of query row ln).
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = ks + mfma_row(r, lane);
+            const float v = sa[r] * scale_log2;
+            sa[r] = (key >= end || key > lim) ? -INFINITY : v;
+            tmax = fmaxf(tmax, sa[r]);
+        }
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        const bool raise = tmax > m_r + kRescaleSlack;
+        if (__any(raise)) {
+            const float mnew = raise ? tmax : m_r;
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_r - mnew) : 1.f;  // 0 if m_r = -inf
+            l_r *= alpha;
+            m_r = mnew;
+            // One accumulator at a time: bounds the VGPR copies of AGPRs.
+#pragma unroll
+            for (int db = 0; db < kDv / 32; ++db) {
+                o[db] *= alpha;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const float msafe = (m_r == -INFINITY) ? 0.f : m_r;
+        float psum = 0.f;
+        uint32_t pk[8], pl[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(sa[r] - msafe);
+            const float p1 = __builtin_amdgcn_exp2f(sa[r + 1] - msafe);
+            const uint32_t hi = pack_bf16_finite(p0, p1);
+            psum += p0 + p1;
+            pk[r >> 1] = hi;
+            pl[r >> 1] = pack_bf16_finite(p0 - bf16_to_f32(hi & 0xffffu), p1 - bf16_to_f32(hi >> 16));
+        }
+        psum += shfl_xor(psum, 32);
+        l_r += psum;
+        const u32x4 pb[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
+        const u32x4 pbl[2] = {u32x4{pl[0], pl[1], pl[2], pl[3]},
+                              u32x4{pl[4], pl[5], pl[6], pl[7]}};
+        // O^T += V^T P^T.  Slot 8h + 4a + r of step tt is key 16tt + 8a + 4h + r.
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int db = 0; db < kDv / 32; ++db) {
+                const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1) +
+                                 ((db & 1) ? voff_o : voff_e);
+                const u32x2 v0 = lds_tr16(vp);
+                const u32x2 v1 = lds_tr16(vp + 8 * kRowBytes);
+                const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
+                o[db] = mfma_32x32x16(vf, pb[tt], o[db]);
+                o[db] = mfma_32x32x16(vf, pbl[tt], o[db]);
+            }
+        }
+    }
+    if (!rows_live) return;
+
+    const int nsplit = (Ltot + chunk - 1) / chunk;
+    const int row = row0 + ln;
+    if (nsplit == 1) {
+        // Lane (ln, lh) holds O^T[d = db*32 + 8j + 4lh + (0..3)][row ln].
+        const float inv = 1.f / l_r;
+        float* op = out + ((size_t)b * R + row) * kDv + 4 * lh;
+        uint16_t* lp = out_lowp ? out_lowp + ((size_t)b * R + row) * kDv + 4 * lh : nullptr;
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
+                                 o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv};
+                *(f32x4*)(op + db * 32 + 8 * j) = v;
+                if (lp)
+                    *(u32x2*)(lp + db * 32 + 8 * j) =
+                        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+        return;
+    }
+    const size_t pidx = (size_t)b * max_splits + split;
+    float* po = part_o + pidx * kDv * R;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[db][r];
+    if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r, l_r);
+}
+
+}  // namespace
+
+// Launch planning and dispatch for the MLA path (called by sd_verify_attn).
+// One workgroup per (request, 128-row block, key chunk) and one workgroup per
+// CU (the kernel holds 512 registers per lane and 108 KiB of LDS): split the
+// keys into chunks (multiples of the 32-key tile, at least 1024 keys) only
+// while the grid has fewer than 256 workgroups.
+int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits) {
+    if (n_q_heads % 32 != 0)
+        return fail(SD_EUNSUPPORTED, "sd_verify_attn: MLA needs n_q_heads %% 32 == 0");
+    const long maxkeys = (long)max_seq_len + num_q;
+    const int R = num_q * n_q_heads;
+    const long groups = (long)batch * ((R + kRowsPerBlock - 1) / kRowsPerBlock);
+    long c = (maxkeys + kTileKeys - 1) / kTileKeys * kTileKeys;
+    while (c > 1024 && groups * ((maxkeys + c - 1) / c) < 256)
+        c = (c / 2 + kTileKeys - 1) / kTileKeys * kTileKeys;
+    *chunk = (int)c;
+    *max_splits = (int)((maxkeys + c - 1) / c);
+    return SD_OK;
+}
+
+int mla_launch(const sd_attn_desc* d, const int32_t* valid, float* po, float2* pml, int chunk,
+               int max_splits, float scale_log2, hipStream_t s) {
+    const int R = d->num_q * d->n_q_heads;
+    const int rblks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
+    const long total = (long)d->batch * max_splits * rblks;
+    if (total > 0x7fffffff) return fail(SD_EUNSUPPORTED, "sd_verify_attn: MLA grid too large");
+    attn_mla_bf16<<<dim3((unsigned)total), 256, 0, s>>>(
+        (const uint16_t*)d->q, (const uint16_t*)d->k_cache, d->page_table, d->seq_lens, valid,
+        d->out, (uint16_t*)d->out_lowp, po, pml, d->num_q, d->n_q_heads, R, d->max_pages, chunk,
+        max_splits, rblks, (int)total, scale_log2);
+    return check_launch("attn_mla_bf16");
+}
+
+}  // namespace sdv

@@ -20,15 +20,6 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLdsStride = kBK + 8;  // bf16 per LDS row (144 bytes)
-constexpr int kXcds = 8;
-
-// Bijection from dispatch order to tile index when dispatch order i runs on
-// XCD i % 8: XCD x receives tiles [first(x), first(x) + count(x)).
-__device__ __forceinline__ int xcd_tile(int bid, int total) {
-    const int q = total / kXcds, r = total % kXcds;
-    const int x = bid % kXcds, idx = bid / kXcds;
-    return (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
-}
 
 __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ B,

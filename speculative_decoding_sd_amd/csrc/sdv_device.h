@@ -17,6 +17,18 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
+// MI355X has 8 XCDs (each with its own L2); workgroups are dispatched to
+// them round-robin, dispatch order i going to XCD i % 8.  xcd_tile maps the
+// dispatch order to a tile index so that XCD x receives the contiguous run
+// [first(x), first(x) + count(x)) of tiles; neighbouring tiles that share
+// operands then share an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+    const int q = total / kXcds, r = total % kXcds;
+    const int x = bid % kXcds, idx = bid / kXcds;
+    return (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

@@ -18,6 +18,11 @@ void clear_error();
 // SD_EDEVICE with the HIP error text if the last launch failed, else SD_OK.
 int check_launch(const char* what);
 
+// MLA verify attention (attn_mla.hip).
+int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits);
+int mla_launch(const sd_attn_desc* d, const int32_t* valid, float* po, float2* pml, int chunk,
+               int max_splits, float scale_log2, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

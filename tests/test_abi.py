@@ -129,3 +129,29 @@ def test_accept_and_rollback_host_validation():
     with pytest.raises(sdv.SdvError) as e:     # poisoning without a cache description
         sdv.sd_kv_rollback(r, 0)
     assert e.value.code == sdv.SD_EINVAL
+
+
+def test_descriptors_keep_their_tensors_alive():
+    """A descriptor holds raw device pointers; it must also hold the tensors,
+    or a temporary passed in would be freed (and its memory reused) while the
+    descriptor still points at it."""
+    import gc
+    import weakref
+
+    import torch
+
+    import speculative_decoding_sd_amd as sdv
+
+    pt = torch.zeros((2, 4), dtype=torch.int32)
+    ref = weakref.ref(pt)
+    d = sdv.attn_desc(q=torch.zeros((2, 4, 8, 576), dtype=torch.bfloat16),
+                      k_cache=torch.zeros((3, 64, 576), dtype=torch.bfloat16), v_cache=None,
+                      page_table=pt, seq_lens=torch.zeros(2, dtype=torch.int32),
+                      out=torch.zeros((2, 4, 8, 512)), n_kv_heads=1, num_pages=3,
+                      max_seq_len=10, mla=True)
+    del pt
+    gc.collect()
+    assert ref() is not None and d.page_table == ref().data_ptr()
+    del d
+    gc.collect()
+    assert ref() is None

@@ -361,3 +361,86 @@ def test_chained_tiny_fp32_step():
         assert np.array_equal(step.rb_slots.cpu().numpy()[: ref_rb["rb_offsets"][-1]],
                               ref_rb["rb_slots"][: ref_rb["rb_offsets"][-1]])
     assert int(step.dev_error.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# MLA-shaped attention (latent 576 = keys, first 512 = values, one kv head)
+# ---------------------------------------------------------------------------
+def _mla_case(B, K, Hq, seq_lens, seed):
+    cfg = sdsynth.Config(name="mla", batch=B, K=K, n_q_heads=Hq, n_kv_heads=1, d_qk=576,
+                         d_v=512, mla=True, hidden=7168, vocab=8, dtype="bf16", seq_len=None)
+    return sdsynth.make_workload(cfg, seed, device="cpu", seq_lens=np.array(seq_lens),
+                                 with_lm_head=False)
+
+
+def _run_gpu_mla(wl, max_seq_len=None):
+    t = wl.tensors
+    q, lat, kn = t["q"].to(DEV), t["k_cache"].to(DEV), t["k_new"].to(DEV)
+    B, Q, Hq, _ = q.shape
+    out = torch.full((B, Q, Hq, 512), -5.0, dtype=torch.float32, device=DEV)
+    lowp = torch.empty((B * Q, Hq * 512), dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    d = sdv.attn_desc(q=q, k_cache=lat, v_cache=None, page_table=torch.tensor(wl.page_table, device=DEV),
+                      seq_lens=torch.tensor(wl.seq_lens, device=DEV), out=out, n_kv_heads=1,
+                      num_pages=wl.num_pages, max_seq_len=int(max_seq_len or wl.seq_lens.max()),
+                      k_new=kn, mla=True, out_lowp=lowp, dev_error=err)
+    sdv.verify_attn(d)
+    torch.cuda.synchronize()
+    return out, lowp, lat, int(err.item())
+
+
+def _oracle_mla(wl, sel=None):
+    t = wl.tensors
+    lat = host(t["k_cache"]).copy()
+    oracle.kv_append(wl.seq_lens, wl.page_table, wl.num_pages, host(t["k_new"]), None, lat,
+                     None, mla=True)
+    ref = oracle.verify_attn(host(t["q"]), lat, None, wl.page_table, wl.seq_lens, wl.num_pages,
+                             n_kv_heads=1, d_v=512, mla=True, sel=sel)
+    return ref, lat
+
+
+@pytest.mark.parametrize("B,K,Hq,lens", [
+    (2, 3, 32, [40, 1000]),       # one 128-row block, chunked keys, ragged
+    (1, 3, 128, [300]),           # four row blocks (the MLA head count)
+    (3, 1, 64, [0, 65, 2000]),    # L = 0 and a page-straddling append
+])
+def test_attention_mla_bf16(B, K, Hq, lens):
+    wl = _mla_case(B, K, Hq, lens, seed=30 + B + Hq)
+    out, lowp, lat, err = _run_gpu_mla(wl)
+    ref, lat_ref = _oracle_mla(wl)
+    assert err == 0
+    check_attention(out.cpu().numpy(), ref, where=f"mla {B},{K},{Hq}")
+    assert np.array_equal(bits(lat), lat_ref)
+    exp_lowp = oracle.round_bf16(out.cpu().numpy().astype(np.float64)).reshape(B * (K + 1), -1)
+    assert np.array_equal(bits(lowp), exp_lowp)
+
+
+def test_attention_mla_full_config_sampled():
+    """The MLA-shaped greedy configuration at full size (B=64, K=3, 128 heads,
+    L=8192): every output of 8 requests' sampled rows against the oracle."""
+    cfg = sdsynth.CONFIGS[3]
+    wl = sdsynth.make_workload(cfg, sdsynth.config_seed(3), device=DEV, with_lm_head=False)
+    out, _, _, err = _run_gpu_mla(wl)
+    assert err == 0
+    rng = np.random.default_rng(3)
+    bs = rng.choice(cfg.batch, 2, replace=False)
+    sel = np.stack([np.repeat(bs, 8), np.tile(rng.integers(0, cfg.num_q, 8), 2),
+                    np.tile(rng.integers(0, cfg.n_q_heads, 8), 2)], 1)
+    # Host copies of just the sampled requests' pages (renumbered).
+    t = wl.tensors
+    pt = wl.page_table[bs]
+    used = np.unique(pt[pt >= 0])
+    remap = {int(p): i for i, p in enumerate(used)}
+    new_pt = np.vectorize(lambda x: remap.get(int(x), -1))(pt).astype(np.int32)
+    lat = bits(t["k_cache"].index_select(0, torch.tensor(used, dtype=torch.long, device=DEV)))
+    kn = bits(t["k_new"][torch.tensor(bs, device=DEV)])
+    seq = wl.seq_lens[bs]
+    oracle.kv_append(seq, new_pt, len(used), kn, None, lat, None, mla=True)
+    sel_local = sel.copy()
+    sel_local[:, 0] = np.searchsorted(bs, sel[:, 0]) if (np.diff(bs) > 0).all() else \
+        np.array([list(bs).index(b) for b in sel[:, 0]])
+    ref = oracle.verify_attn(bits(t["q"][torch.tensor(bs, device=DEV)]), lat, None, new_pt, seq,
+                             len(used), n_kv_heads=1, d_v=512, mla=True, sel=sel_local)
+    o = out.cpu().numpy()
+    got = np.stack([o[b, i, h] for b, i, h in sel])
+    check_attention(got, ref, where="mla full config")
