@@ -101,3 +101,27 @@ def compare_accept(gpu: dict, ref: dict, allow_excluded=True, where=""):
         assert np.array_equal(gpu["out_offsets"], ref["out_offsets"]), where
         assert np.array_equal(gpu["packed_tokens"], ref["packed"]), where
     return int(excl.sum())
+
+
+def gather_requests(wl, reqs):
+    """Host copies (oracle formats) of the inputs of requests `reqs` of a
+    device-resident workload, pages renumbered into a compact pool.  Taken
+    before any library call touches the cache."""
+    t = wl.tensors
+    reqs = np.asarray(reqs)
+    pt = wl.page_table[reqs]
+    used = pt[pt >= 0]
+    remap = np.full(wl.num_pages, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    new_pt = np.where(pt >= 0, remap[np.maximum(pt, 0)], -1).astype(np.int32)
+    idx = torch.tensor(used, dtype=torch.long, device=t["k_cache"].device)
+    ridx = torch.tensor(reqs, dtype=torch.long, device=t["q"].device)
+    return {
+        "reqs": reqs, "page_table": new_pt, "num_pages": int(len(used)),
+        "seq_lens": wl.seq_lens[reqs].copy(),
+        "q": host(t["q"].index_select(0, ridx)),
+        "k_new": host(t["k_new"].index_select(0, ridx)),
+        "v_new": host(t["v_new"].index_select(0, ridx)) if t.get("v_new") is not None else None,
+        "k_cache": host(t["k_cache"].index_select(0, idx)),
+        "v_cache": host(t["v_cache"].index_select(0, idx)) if t.get("v_cache") is not None else None,
+    }

@@ -1,0 +1,122 @@
+"""Parity at the full sizes of the four GPU configurations, in the launch
+configuration that bench.py times (VerifyStep over device-resident inputs).
+The oracle cannot redo these in seconds, so each call is checked on samples
+it can compute one by one: attention rows of a few requests (their pages
+copied to the host before the step), LM-head rows against exact fp64 dot
+products, and acceptance plus rollback over the whole batch, with the GPU's
+own logits as the acceptance input."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sdsynth
+import speculative_decoding_sd_amd as sdv
+from parity import (DEV, bits, host, check_attention, check_logits_bf16, compare_accept,
+                    gather_requests)
+
+pytestmark = pytest.mark.gpu
+
+
+def _drafts(cfg, seed, lg, temperature, top_p):
+    """Draft stand-in from the target logits: greedy requests copy the
+    target's argmax for a Geometric(p) prefix; sampled requests draw from
+    softmax((logits + noise) / T) (the recipe bench.py uses)."""
+    B, Q, V = lg.shape
+    K = Q - 1
+    greedy = temperature == 0
+    drafts = np.full((B, K), -1, np.int32)
+    pd = np.zeros((B, K, V), np.float32)
+    if greedy.any():
+        tt = np.argmax(lg, axis=-1)
+        drafts[greedy] = sdsynth.greedy_drafts(tt, K, V, seed, p=cfg.geom_p)[greedy]
+    st = np.nonzero(~greedy)[0]
+    if len(st) and K > 0:
+        pd_st = sdsynth.draft_probs(lg[st, :K], seed, cfg.draft_noise, float(temperature[st[0]]),
+                                    float(top_p[st[0]]))
+        pd[st] = pd_st
+        drafts[st] = sdsynth.sample_drafts(pd_st, seed)
+    return drafts, pd
+
+
+@pytest.mark.parametrize("ci", [2, 3, 4, 5])
+def test_full_config_step(ci):
+    cfg = sdsynth.CONFIGS[ci]
+    seed = sdsynth.config_seed(ci)
+    torch.cuda.empty_cache()
+    wl = sdsynth.make_workload(cfg, seed, device=DEV, extra_tokens=cfg.num_q)
+    t = wl.tensors
+    B, Q = cfg.batch, cfg.num_q
+    rng = np.random.default_rng(ci)
+    reqs = np.sort(rng.choice(B, min(B, 2), replace=False))
+    sample = gather_requests(wl, reqs)
+    print(f"config {ci}: sampled requests {reqs.tolist()}", flush=True)
+
+    L0 = wl.seq_lens.copy()
+    seq_lens = torch.tensor(L0, device=DEV)
+    page_table = torch.tensor(wl.page_table, device=DEV)
+    temp = torch.tensor(wl.temperature, device=DEV)
+    top_p = torch.tensor(wl.top_p, device=DEV) if (wl.top_p < 1).any() else None
+    drafts = torch.full((B, cfg.K), -1, dtype=torch.int32, device=DEV)
+    pd = torch.zeros((B, cfg.K, cfg.vocab), dtype=torch.float32, device=DEV)
+    step = sdv.VerifyStep(q=t["q"], k_cache=t["k_cache"], v_cache=t["v_cache"],
+                          page_table=page_table, seq_lens=seq_lens, num_pages=wl.num_pages,
+                          max_seq_len=int(L0.max()), n_kv_heads=cfg.n_kv_heads, W=t["W"],
+                          drafts=drafts, temperature=temp,
+                          u_accept=torch.tensor(wl.u_accept, device=DEV),
+                          u_sample=torch.tensor(wl.u_sample, device=DEV), k_new=t["k_new"],
+                          v_new=t["v_new"], mla=cfg.mla, d_v=cfg.d_v, H=t.get("H"), top_p=top_p,
+                          draft_probs=pd if (wl.temperature > 0).any() else None)
+    step.attention()
+    step.lm_head()
+    torch.cuda.synchronize()
+    assert int(step.dev_error.item()) == 0
+
+    # Attention: 24 sampled rows of the sampled requests.
+    kc, vc = sample["k_cache"], sample["v_cache"]
+    oracle.kv_append(sample["seq_lens"], sample["page_table"], sample["num_pages"],
+                     sample["k_new"], sample["v_new"], kc, vc, mla=cfg.mla)
+    sel = np.stack([rng.integers(0, len(reqs), 24), rng.integers(0, Q, 24),
+                    rng.integers(0, cfg.n_q_heads, 24)], 1)
+    ref = oracle.verify_attn(sample["q"], kc, vc, sample["page_table"], sample["seq_lens"],
+                             sample["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
+                             mla=cfg.mla, sel=sel)
+    o = step.out.cpu().numpy()
+    got = np.stack([o[reqs[b], i, h] for b, i, h in sel])
+    check_attention(got, ref, where=f"config {ci} attention")
+
+    # LM head: 6 sampled rows, exact fp64 logits from the kernel's own input.
+    rows = rng.choice(B * Q, 6, replace=False).astype(np.int32)
+    hin = bits(step.hin.index_select(0, torch.tensor(rows, dtype=torch.long, device=DEV)))
+    exact = oracle.lm_head(hin, bits(t["W"]))
+    lg_rows = bits(step.logits.view(B * Q, -1).index_select(
+        0, torch.tensor(rows, dtype=torch.long, device=DEV)))
+    check_logits_bf16(lg_rows, exact, where=f"config {ci} lm head")
+
+    # Acceptance and rollback over the whole batch on the GPU's logits.
+    lg_bits = bits(step.logits)
+    lf = oracle.bf16_to_f64(lg_bits)
+    d_h, pd_h = _drafts(cfg, seed, lf.astype(np.float32), wl.temperature, wl.top_p)
+    drafts.copy_(torch.from_numpy(d_h))
+    pd.copy_(torch.from_numpy(pd_h))
+    del lf
+    step.accept()
+    step.rollback()
+    torch.cuda.synchronize()
+    ref_acc = oracle.accept(lg_bits, d_h, wl.temperature,
+                            wl.top_p if (wl.top_p < 1).any() else None, pd_h, wl.u_accept,
+                            wl.u_sample)
+    gpu = {"num_accepted": step.num_accepted.cpu().numpy(),
+           "out_tokens": step.out_tokens.cpu().numpy(),
+           "next_token": step.next_token.cpu().numpy(),
+           "out_offsets": step.out_offsets.cpu().numpy(),
+           "packed_tokens": step.packed.cpu().numpy()}
+    n_excl = compare_accept(gpu, ref_acc, where=f"config {ci} accept")
+    assert n_excl <= max(1, B // 16)
+    assert int(step.dev_error.item()) == 0
+    rb = oracle.kv_rollback(wl.page_table, ref_acc["num_accepted"], L0, cfg.K)
+    keep = ref_acc["num_accepted"] >= 0
+    assert np.array_equal(seq_lens.cpu().numpy()[keep], rb["seq_lens"][keep])
+    if n_excl == 0:
+        assert np.array_equal(step.rb_offsets.cpu().numpy(), rb["rb_offsets"])
+        assert np.array_equal(step.rb_slots.cpu().numpy(), rb["rb_slots"])
