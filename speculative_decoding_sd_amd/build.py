@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libsdv.so")
-SOURCES = ["sdv_abi.cpp", "attn.hip", "attn_mla.hip", "lm_head.hip", "accept.hip", "rollback.hip"]
+SOURCES = ["sdv_abi.cpp", "attn.hip", "attn_gqa.hip", "attn_mla.hip", "lm_head.hip", "accept.hip", "rollback.hip"]
 ARCH = "gfx950"
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops keeps the compiler from
@@ -21,13 +21,15 @@ HIPCC_FLAGS = [
     "-I", os.path.join(HERE, "..", "include"),
 ]
 
-# Per-source extras.  attn_mla.hip keeps 256 fp32 accumulators plus the
-# resident Q^T fragments per lane: MFMA results in VGPRs (A/B operands may then
-# sit in AGPRs) is the register assignment that fits without spilling.  Its LDS
-# DMA sets M0 in inline asm; the kernel has no other M0 use, so the reserved-
-# register clobber warning is silenced there.
+# Per-source extras.  The attention kernels keep many fp32 accumulators and
+# resident Q^T fragments per lane (attn_mla.hip: 256 + 144 registers): MFMA
+# results in VGPRs (A/B operands may then sit in AGPRs) is the register
+# assignment that fits them without spilling to scratch.  The
+# attention kernels' LDS DMA sets M0 in inline asm; they have no other M0 use,
+# so the reserved-register clobber warning is silenced for them.
 EXTRA_FLAGS = {
     "attn_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"],
+    "attn_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"],
 }
 
 

@@ -96,296 +96,37 @@ __global__ void attn_append(const uint8_t* __restrict__ k_new, const uint8_t* __
     }
 }
 
-// Position of key kappa (0..31 within a tile) in a V^T row of LDS.  The
-// PV MFMA's k-slot e of fragment half h at step t is key
-// 16t + 8(e/4) + 4h + e%4 (that is where the softmax registers put it), so
-// storing key kappa at this position makes each half's 8 keys contiguous.
-__device__ __forceinline__ int vt_pos(int kappa) {
-    return 16 * (kappa >> 4) + 8 * ((kappa & 7) >> 2) + 4 * ((kappa & 15) >> 3) + (kappa & 3);
-}
-
-__device__ __forceinline__ uint32_t half16(u32x4 v, int e) {
-    return (v[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-constexpr int kVtStride = 36;  // bf16 per V^T row in LDS (72 bytes: 8-byte aligned rows)
-
-template <int D, int RB>
-struct GqaSmem {
-    static constexpr int kVt = 4 * D * kVtStride * 2;
-    static constexpr int kRed = 2 * RB * 32 * D * 4 + 2 * RB * 32 * 8;
-    static constexpr int kBytes = kVt > kRed ? kVt : kRed;
-};
-
-// ---------------------------------------------------------------------------
-// Split-KV verify attention, bf16 in, fp32 accumulation.
-// grid (split, kv head, request); 256 threads = 4 waves; wave w handles the
-// chunk's 32-key tiles w, w+4, ...  Query rows of the group: row = i*G + g
-// (position i, head kvh*G + g); RB blocks of 32 rows.
-// Writes the chunk's unnormalised O^T (part_o [.][d][row]) and (m, l) per row.
-// ---------------------------------------------------------------------------
-template <int D, int RB>
-__global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void attn_gqa_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
-    float* __restrict__ part_o, float2* __restrict__ part_ml, int NQ, int Hq, int Hkv, int G,
-    int R, int max_pages, int chunk, int max_splits, float scale_log2) {
-    constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
-    constexpr int NDB = D / 32;  // 32-row blocks of O^T
-    constexpr int CPL = D / 8;   // 16-byte chunks per key row
-    constexpr int NU = D / 16;   // keys per lane when a wave loads a 32-key V tile
-    __shared__ __attribute__((aligned(16))) unsigned char smem[GqaSmem<D, RB>::kBytes];
-
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    if (!valid[b]) return;
-    const int L = seq_lens[b];
-    const int Ltot = L + NQ;
-    const int start = split * chunk;
-    if (start >= Ltot) return;
-    const int end = min(start + chunk, Ltot);
-    const int ntiles = (end - start + 31) >> 5;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ln = lane & 31, lh = lane >> 5;
-
-    // Q fragments: B operand of S^T = K Q^T (column = query row, k = d).
-    u32x4 qf[RB][NS];
-    int lim[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 32 + ln;
-        if (row < R) {
-            const int i = row / G, g = row - i * G;
-            const uint16_t* qp = q + (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + 8 * lh;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) qf[rb][s] = *(const u32x4*)(qp + 16 * s);
-            lim[rb] = L + i;  // causal: keys 0 .. L_b + i
-        } else {
-#pragma unroll
-            for (int s = 0; s < NS; ++s) qf[rb][s] = u32x4{0, 0, 0, 0};
-            lim[rb] = Ltot - 1;
-        }
-    }
-
-    float m_r[RB], l_r[RB];
-    f32x16 o[RB][NDB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m_r[rb] = -INFINITY;
-        l_r[rb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
-    }
-
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * D * kVtStride;
-    const size_t head_elems = (size_t)kPage * D;
-    const int vc = lane % CPL, vg = lane / CPL;
-
-    auto tile_base = [&](int t) -> size_t {
-        const int ks = start + 32 * t;
-        const int pg = page_table[(size_t)b * max_pages + (ks >> 6)];
-        return ((size_t)pg * Hkv + kvh) * head_elems + (size_t)(ks & 63) * D;
-    };
-
-    u32x4 kf[NS], vf[NU];
-    auto load_k = [&](size_t base) {
-        const uint16_t* p = k_cache + base + (size_t)ln * D + 8 * lh;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) kf[s] = *(const u32x4*)(p + 16 * s);
-    };
-    auto load_v = [&](size_t base) {
-        const uint16_t* p = v_cache + base + (size_t)(NU * vg) * D + 8 * vc;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) vf[u] = *(const u32x4*)(p + (size_t)u * D);
-    };
-
-    int t = wave;
-    if (t < ntiles) {
-        const size_t base = tile_base(t);
-        load_k(base);
-        load_v(base);
-    }
-    for (; t < ntiles; t += 4) {
-        // V tile -> LDS, transposed: V^T[d][vt_pos(key)].
-#pragma unroll
-        for (int qd = 0; qd < NU / 4; ++qd) {
-            const int pos0 = vt_pos(NU * vg + 4 * qd);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x2 w;
-                w.x = half16(vf[4 * qd + 0], e) | (half16(vf[4 * qd + 1], e) << 16);
-                w.y = half16(vf[4 * qd + 2], e) | (half16(vf[4 * qd + 3], e) << 16);
-                *(u32x2*)(vt + (8 * vc + e) * kVtStride + pos0) = w;
-            }
-        }
-        const bool has_next = t + 4 < ntiles;
-        const size_t nbase = has_next ? tile_base(t + 4) : 0;
-        if (has_next) load_v(nbase);
-
-        f32x16 sacc[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) sacc[rb] = mfma_32x32x16(kf[s], qf[rb][s], sacc[rb]);
-        }
-        if (has_next) load_k(nbase);
-
-        // Online softmax; lane (ln, lh) holds 16 keys of query row ln.
-        const int ks = start + 32 * t;
-        u32x4 pb[RB][2], pbl[RB][2];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float x[16];
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = ks + mfma_row(r, lane);
-                float v = sacc[rb][r] * scale_log2;
-                if (key >= end || key > lim[rb]) v = -INFINITY;
-                x[r] = v;
-                tmax = fmaxf(tmax, v);
-            }
-            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-            const float mnew = fmaxf(m_r[rb], tmax);
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = exp2f(m_r[rb] - msafe);
-            // P = P_hi + P_lo with both halves in bf16: the PV product runs as
-            // two MFMAs, leaving a relative error of about 2^-17 in P.
-            float psum = 0.f;
-            uint32_t pk[8], pl[8];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2f(x[r] - msafe), p1 = exp2f(x[r + 1] - msafe);
-                const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-                const uint32_t l0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
-                const uint32_t l1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
-                psum += p0 + p1;
-                pk[r >> 1] = h0 | (h1 << 16);
-                pl[r >> 1] = l0 | (l1 << 16);
-            }
-            psum += shfl_xor(psum, 32);
-            l_r[rb] = l_r[rb] * alpha + psum;
-            m_r[rb] = mnew;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
-            pb[rb][0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            pb[rb][1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
-            pbl[rb][0] = u32x4{pl[0], pl[1], pl[2], pl[3]};
-            pbl[rb][1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
-        }
-
-        wave_lds_sync();
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint16_t* vp = vt + (db * 32 + ln) * kVtStride + 16 * tt + 8 * lh;
-                const u32x2 a0 = *(const u32x2*)vp;
-                const u32x2 a1 = *(const u32x2*)(vp + 4);
-                const u32x4 af = u32x4{a0.x, a0.y, a1.x, a1.y};
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    o[rb][db] = mfma_32x32x16(af, pb[rb][tt], o[rb][db]);
-                    o[rb][db] = mfma_32x32x16(af, pbl[rb][tt], o[rb][db]);
-                }
-            }
-        }
-        wave_lds_sync();
-    }
-
-    // Merge the four waves: 2,3 -> 0,1 through LDS, then 1 -> 0.
-    float* red_o = reinterpret_cast<float*>(smem);
-    float2* red_ml = reinterpret_cast<float2*>(red_o + 2 * RB * 32 * D);
-    auto put = [&](int slot) {
-        float* ro = red_o + slot * RB * 32 * D;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    ro[(rb * 32 + ln) * D + db * 32 + mfma_row(r, lane)] = o[rb][db][r];
-            if (lh == 0) red_ml[slot * RB * 32 + rb * 32 + ln] = make_float2(m_r[rb], l_r[rb]);
-        }
-    };
-    auto merge = [&](int slot) {
-        const float* ro = red_o + slot * RB * 32 * D;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const float2 oth = red_ml[slot * RB * 32 + rb * 32 + ln];
-            const float M = fmaxf(m_r[rb], oth.x);
-            const float ws = (m_r[rb] == -INFINITY) ? 0.f : exp2f(m_r[rb] - M);
-            const float wo = (oth.x == -INFINITY) ? 0.f : exp2f(oth.x - M);
-            l_r[rb] = l_r[rb] * ws + oth.y * wo;
-            m_r[rb] = M;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    o[rb][db][r] = o[rb][db][r] * ws +
-                                   ro[(rb * 32 + ln) * D + db * 32 + mfma_row(r, lane)] * wo;
-        }
-    };
-    __syncthreads();
-    if (wave >= 2) put(wave - 2);
-    __syncthreads();
-    if (wave < 2) merge(wave);
-    __syncthreads();
-    if (wave == 1) put(0);
-    __syncthreads();
-    if (wave != 0) return;
-    merge(0);
-
-    const size_t pidx = ((size_t)b * Hkv + kvh) * max_splits + split;
-    float* po = part_o + pidx * D * R;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 32 + ln;
-        if (row >= R) continue;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[rb][db][r];
-        if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Merge of the chunk partials of one (request, kv head): for each row,
 // M = max m_s, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // Invalid requests get NaN rows.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = 64;
-constexpr int kCombineCache = 8192;
+constexpr int kCombineDims = 32;
+constexpr int kCombineCache = 12288;  // split weights cached per block (48 KiB)
 
-// grid (kv head, request, block of 64 rows).  With `direct_single`, requests
-// whose keys fit one chunk were written by the attention kernel already.
+// grid (kv head, request, row block x 32-dim block).  With `direct_single`,
+// requests whose keys fit one chunk were written by the attention kernel
+// already.  Each block weighs its rows' chunk partials once (weights cached in
+// LDS when ns * rows fits), then reads the partial planes [d][R] with
+// consecutive threads on consecutive rows.
 __global__ __launch_bounds__(256) void attn_combine(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     float* __restrict__ out, uint16_t* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int G,
     int R, int D, int chunk, int max_splits, int direct_single) {
     __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
-    __shared__ float s_w[kCombineCache];
+    __shared__ float s_red[4][kCombineRows];
+    __shared__ __attribute__((aligned(16))) float s_w[kCombineCache];
     const int kvh = blockIdx.x, b = blockIdx.y;
-    const int r0 = blockIdx.z * kCombineRows;
+    const int ndb = D / kCombineDims;
+    const int r0 = (blockIdx.z / ndb) * kCombineRows;
+    const int d0 = (blockIdx.z % ndb) * kCombineDims;
     const int nr = min(kCombineRows, R - r0);
     if (nr <= 0) return;
     if (!valid[b]) {
-        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-            const int row = r0 + idx / D, d = idx % D;
+        for (int idx = threadIdx.x; idx < nr * kCombineDims; idx += blockDim.x) {
+            const int row = r0 + idx % nr, d = d0 + idx / nr;
             const int i = row / G, g = row - i * G;
             const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
             out[oi] = NAN;
@@ -396,18 +137,35 @@ __global__ __launch_bounds__(256) void attn_combine(
     const int ns = (seq_lens[b] + NQ + chunk - 1) / chunk;
     if (direct_single && ns == 1) return;
     const size_t pbase = ((size_t)b * Hkv + kvh) * max_splits;
-    for (int lr = threadIdx.x; lr < nr; lr += blockDim.x) {
-        const int row = r0 + lr;
+    // Row statistics: four threads per row, each over every fourth split,
+    // merged in a fixed order.
+    const int lr4 = threadIdx.x % kCombineRows, q4 = threadIdx.x / kCombineRows;
+    {
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[(pbase + s) * R + row].x);
-        float den = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float2 ml = part_ml[(pbase + s) * R + row];
-            if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
-        }
-        s_m[lr] = M;
-        s_inv[lr] = 1.f / den;
+        if (lr4 < nr)
+            for (int s = q4; s < ns; s += 4) M = fmaxf(M, part_ml[(pbase + s) * R + r0 + lr4].x);
+        s_red[q4][lr4] = M;
     }
+    __syncthreads();
+    if (threadIdx.x < nr)
+        s_m[threadIdx.x] = fmaxf(fmaxf(s_red[0][threadIdx.x], s_red[1][threadIdx.x]),
+                                 fmaxf(s_red[2][threadIdx.x], s_red[3][threadIdx.x]));
+    __syncthreads();
+    {
+        float den = 0.f;
+        if (lr4 < nr) {
+            const float M = s_m[lr4];
+            for (int s = q4; s < ns; s += 4) {
+                const float2 ml = part_ml[(pbase + s) * R + r0 + lr4];
+                if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
+            }
+        }
+        s_red[q4][lr4] = den;
+    }
+    __syncthreads();
+    if (threadIdx.x < nr)
+        s_inv[threadIdx.x] = 1.f / ((s_red[0][threadIdx.x] + s_red[1][threadIdx.x]) +
+                                    (s_red[2][threadIdx.x] + s_red[3][threadIdx.x]));
     __syncthreads();
     const bool cached = ns * nr <= kCombineCache;
     if (cached) {
@@ -418,9 +176,42 @@ __global__ __launch_bounds__(256) void attn_combine(
         }
         __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-        const int d = idx / nr, lr = idx - d * nr;
-        const int row = r0 + lr;
+    const size_t sstride = (size_t)D * R;
+    auto emit = [&](int row, int d, float acc) {
+        const int i = row / G, g = row - i * G;
+        const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
+        out[oi] = acc;
+        if (out_lowp) out_lowp[oi] = (uint16_t)f32_to_bf16_rne(acc);
+    };
+    if (cached && (R & 3) == 0 && (nr & 3) == 0) {
+        // Four consecutive rows per thread (16-byte loads), eight splits in
+        // flight per step.
+        const int nq = nr >> 2;
+        for (int idx = threadIdx.x; idx < nq * kCombineDims; idx += blockDim.x) {
+            const int dl = idx / nq, lq = 4 * (idx - dl * nq);
+            const float* po = part_o + (pbase * D + d0 + dl) * R + r0 + lq;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            int s = 0;
+            for (; s + 8 <= ns; s += 8) {
+                f32x4 v[8], w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(po + (s + u) * sstride);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(s_w + (s + u) * nr + lq);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += w[u] * v[u];
+            }
+            for (; s < ns; ++s)
+                acc += *(const f32x4*)(s_w + s * nr + lq) * *(const f32x4*)(po + s * sstride);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) emit(r0 + lq + j, d0 + dl, acc[j]);
+        }
+        return;
+    }
+    for (int idx = threadIdx.x; idx < nr * kCombineDims; idx += blockDim.x) {
+        const int dl = idx / nr, lr = idx - dl * nr;
+        const int row = r0 + lr, d = d0 + dl;
+        const float* po = part_o + (pbase * D + d) * R + row;
         float acc = 0.f;
         for (int s = 0; s < ns; ++s) {
             float w;
@@ -430,12 +221,9 @@ __global__ __launch_bounds__(256) void attn_combine(
                 const float m = part_ml[(pbase + s) * R + row].x;
                 w = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
             }
-            acc += w * part_o[((pbase + s) * D + d) * R + row];
+            acc += w * po[s * sstride];
         }
-        const int i = row / G, g = row - i * G;
-        const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
-        out[oi] = acc;
-        if (out_lowp) out_lowp[oi] = (uint16_t)f32_to_bf16_rne(acc);
+        emit(row, d, acc);
     }
 }
 
@@ -527,7 +315,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
 struct AttnPlan {
     int G = 0, R = 0, chunk = 0, max_splits = 0;
     int path = 0;  // 0 gqa bf16 (MFMA), 1 gqa f32, 2 mla bf16
-    size_t off_valid = 0, off_po = 0, off_pml = 0, total = 0;
+    size_t off_valid = 0, off_first = 0, off_po = 0, off_pml = 0, total = 0;
 };
 
 int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
@@ -570,9 +358,11 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         if (p->R > 64)
             return fail(SD_EUNSUPPORTED, "sd_verify_attn: (Hq/Hkv)*(K+1) = %d > 64", p->R);
         p->path = 0;
+        // Chunks small enough that the persistent waves (4 per CU) get about
+        // sixteen items each at the longest length, within [128, 1024] keys.
         const long pairs = (long)d->batch * d->n_kv_heads;
         int chunk = 1024;
-        while (chunk > 128 && pairs * ((maxkeys + chunk - 1) / chunk) < 2048) chunk >>= 1;
+        while (chunk > 128 && pairs * ((maxkeys + chunk - 1) / chunk) < 16L * 4 * 256) chunk >>= 1;
         p->chunk = chunk;
         p->max_splits = (int)((maxkeys + chunk - 1) / chunk);
     } else {
@@ -585,6 +375,8 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
     size_t off = 0;
     p->off_valid = off;
     off = align_up(off + sizeof(int32_t) * d->batch, 256);
+    p->off_first = off;
+    off = align_up(off + sizeof(int32_t) * (d->batch + 1), 256);
     p->off_po = off;
     const size_t nparts = (size_t)d->batch * d->n_kv_heads *
                           (p->path == 2 && p->max_splits == 1 ? 0 : p->max_splits) * p->R;
@@ -663,25 +455,19 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         if ((rc = mla_launch(d, valid, po, pml, p.chunk, p.max_splits, scale_log2, s)) != SD_OK)
             return rc;
         if (p.max_splits == 1) return SD_OK;
-        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows), 256, 0, s>>>(
+        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),
+                       256, 0, s>>>(
             po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads, 1,
             p.G, p.R, d->d_v, p.chunk, p.max_splits, 1);
         return check_launch("attn_combine");
     }
-    const dim3 grid(p.max_splits, d->n_kv_heads, B);
-#define SDV_LAUNCH_GQA(DD, RBB)                                                                  \
-    attn_gqa_bf16<DD, RBB><<<grid, 256, 0, s>>>(                                                 \
-        (const uint16_t*)d->q, (const uint16_t*)d->k_cache, (const uint16_t*)d->v_cache,         \
-        d->page_table, d->seq_lens, valid, po, pml, NQ, d->n_q_heads, d->n_kv_heads, p.G, p.R, \
-        d->max_pages, p.chunk, p.max_splits, scale_log2)
-    if (d->d_qk == 128) {
-        if (p.R <= 32) SDV_LAUNCH_GQA(128, 1); else SDV_LAUNCH_GQA(128, 2);
-    } else {
-        if (p.R <= 32) SDV_LAUNCH_GQA(64, 1); else SDV_LAUNCH_GQA(64, 2);
-    }
-#undef SDV_LAUNCH_GQA
-    if ((rc = check_launch("attn_gqa_bf16")) != SD_OK) return rc;
-    attn_combine<<<dim3(d->n_kv_heads, B, (p.R + kCombineRows - 1) / kCombineRows), 256, 0, s>>>(
+    int32_t* first = (int32_t*)(ws + p.off_first);
+    if ((rc = gqa_launch(d, valid, first, po, pml, p.R, p.chunk, p.max_splits, scale_log2, s)) !=
+        SD_OK)
+        return rc;
+    attn_combine<<<dim3(d->n_kv_heads, B,
+                        (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),
+                   256, 0, s>>>(
         po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
         d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0);
     return check_launch("attn_combine");

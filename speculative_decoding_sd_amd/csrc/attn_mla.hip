@@ -32,6 +32,7 @@
 
 #include "sdv_device.h"
 #include "sdv_internal.h"
+#include "sdv_lds.h"
 
 namespace sdv {
 
@@ -47,53 +48,6 @@ constexpr int kStages = 3;
 constexpr int kDmaPerWave = kTileKeys * kRowChunks / 256;  // 9 x 1 KiB per wave
 constexpr float kRescaleSlack = 8.f;                       // log2 units
 constexpr int kRowsPerBlock = 128;
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-
-// XOR applied to the chunk index of latent row `key` (0..7, so chunks 0..63
-// and 64..71 each stay in their own range).
-__device__ __forceinline__ int chunk_xor(int key) { return 2 * (key & 3) + ((key >> 2) & 1); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One 16-byte-per-lane LDS DMA: lane l's 16 bytes from gptr land at LDS byte
-// address m0 + 16 l.  Issued from inline asm so that the compiler does not see
-// the LDS write (it would otherwise wait for every DMA in flight before each
-// LDS read); callers order it with explicit vmcnt waits and barriers.  Nothing
-// else in this kernel uses M0.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(m0), "v"(gptr)
-                 : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void barrier_only() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ u32x2 lds_tr16(const char* p) {
-    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s*)(p));
-    return __builtin_bit_cast(u32x2, r);
-}
-
-// bf16 bits of two finite floats (lo in the low half), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16_finite(float lo, float hi) {
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    a += 0x7fffu + ((a >> 16) & 1u);
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (a >> 16) | (b & 0xffff0000u);
-}
 
 __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
@@ -143,7 +97,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         const int key = n / kRowChunks;
         goff[j] = key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
     }
-    const uint32_t lds0 = lds_addr(&s_lat[0][0]);
+    const uint32_t lds0 = lds_byte_addr(&s_lat[0][0]);
     auto issue_tile = [&](int t) {
         const int ks = start + kTileKeys * t;
         const int pg = page_table[(size_t)b * max_pages + ks / kPage];
@@ -180,6 +134,9 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     for (int t = 0; t < ntiles; ++t) {
         // Tile t has landed once at most the next tile's DMAs are in flight.
         if (t + 1 < ntiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+        // This wave's reads of tile t-1 must have returned before another
+        // wave refills that stage after the barrier.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         barrier_only();
         // Stage (t+2)%3 was last read in iteration t-1, which every wave has
         // left through the barrier above.
@@ -253,8 +210,8 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             for (int db = 0; db < kDv / 32; ++db) {
                 const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1) +
                                  ((db & 1) ? voff_o : voff_e);
-                const u32x2 v0 = lds_tr16(vp);
-                const u32x2 v1 = lds_tr16(vp + 8 * kRowBytes);
+                const u32x2 v0 = lds_read_tr16(vp);
+                const u32x2 v1 = lds_read_tr16(vp + 8 * kRowBytes);
                 const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
                 o[db] = mfma_32x32x16(vf, pb[tt], o[db]);
                 o[db] = mfma_32x32x16(vf, pbl[tt], o[db]);

@@ -18,6 +18,10 @@ void clear_error();
 // SD_EDEVICE with the HIP error text if the last launch failed, else SD_OK.
 int check_launch(const char* what);
 
+// GQA verify attention (attn_gqa.hip): persistent streaming kernel.
+int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, float* po,
+               float2* pml, int R, int chunk, int max_splits, float scale_log2, hipStream_t s);
+
 // MLA verify attention (attn_mla.hip).
 int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits);
 int mla_launch(const sd_attn_desc* d, const int32_t* valid, float* po, float2* pml, int chunk,

@@ -1,0 +1,69 @@
+// Device helpers for the attention kernels' LDS traffic on gfx950: direct
+// global->LDS DMA issued outside the compiler's view, explicit vmcnt waits,
+// the transposing 8-byte LDS read, and the chunk swizzle of a K/V tile.
+#pragma once
+
+#include "sdv_device.h"
+
+namespace sdv {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte-per-lane LDS DMA (global_load_lds_dwordx4): lane l's 16 bytes
+// from gptr land at LDS byte address m0 + 16 l.  Issued from inline asm so that
+// the compiler does not see the LDS write (it would otherwise wait for every
+// DMA in flight before each LDS read); callers order it with explicit vmcnt
+// waits (and barriers when other waves read the data).  The kernels that use
+// it have no other M0 use.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// make the compiler wait for all memory operations in flight).
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane t receives element t%4
+// of the 8-byte reads of lanes 4e + t/4 (e = 0..3).  With lane s reading four
+// consecutive dims d0 + 4(s%4) .. +3 of key row key0 + s/4 of a row-major
+// [key][dim] tile, lane t receives V[key0 .. key0+3][d0 + t]: the transposed
+// operand of O^T += V^T P^T.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// XOR applied to the 16-byte chunk index of tile row `row` (values 0..7, so
+// each aligned group of 8 chunks maps onto itself).  With it, the eight rows a
+// ds_read_b128 phase touches (same chunk, rows r..r+7) and the 4 rows x 2
+// chunks of a ds_read_b64_tr_b16 phase each land in distinct bank groups.
+__device__ __forceinline__ int chunk_xor(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// bf16 bits of two finite floats (lo in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_finite(float lo, float hi) {
+    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    a += 0x7fffu + ((a >> 16) & 1u);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+}  // namespace sdv
