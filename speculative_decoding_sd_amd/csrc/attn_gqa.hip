@@ -6,11 +6,11 @@
 // The query rows of one (request, kv head) are the G heads of the group at
 // each of the K+1 positions (row = i*G + g, at most 64), so every key/value
 // row fetched from HBM serves all of them: the kernel is bound by streaming
-// the cache.  Work items are (key chunk, request, kv head) triples; each wave
+// the cache.  Work items are (kv head, request, key chunk) triples; each wave
 // runs its own items start to finish (no workgroup barriers) and streams their
-// 32-key tiles through a private two-stage LDS ring filled by LDS DMA, the
-// next tile always in flight while the current one is computed (also across
-// item boundaries).  The grid holds one workgroup of 4 waves per CU; each wave
+// 32-key tiles through private LDS rings filled by LDS DMA (three K stages,
+// two V stages: 40 KiB per wave at head dim 128), so that about two tiles per
+// wave are in flight while one is computed, also across item boundaries.  The grid holds one workgroup of 4 waves per CU; each wave
 // takes an equal contiguous range of the non-empty items.
 // Per tile and 32-row block:
 //   S^T = K Q^T    A = K rows from LDS (ds_read_b128), B = Q^T in registers;
@@ -37,10 +37,10 @@ template <int D>
 struct GqaTile {
     static constexpr int kRowBytes = D * 2;
     static constexpr int kRowChunks = D / 8;
-    static constexpr int kHalfBytes = kTile * kRowBytes;    // K (or V) part of a tile
-    static constexpr int kBytes = 2 * kHalfBytes;           // K then V
-    static constexpr int kDma = kBytes / 1024;              // 1 KiB DMA ops per tile
-    static constexpr int kRingBytes = 2 * kBytes;           // two stages per wave
+    static constexpr int kHalfBytes = kTile * kRowBytes;  // the K (or V) rows of a tile
+    static constexpr int kDmaHalf = kHalfBytes / 1024;    // 1 KiB DMA ops per half tile
+    static constexpr int kKStages = 3, kVStages = 2;      // K runs one tile further ahead
+    static constexpr int kRingBytes = (kKStages + kVStages) * kHalfBytes;
 };
 
 // Work items are (kv head, request, key chunk) triples of non-empty chunks,
@@ -119,35 +119,35 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     const int ln = lane & 31, lh = lane >> 5;
     const int nw = gridDim.x * 4;
     char* ring = s_ring[wave];
-    const uint32_t ring_lds = lds_byte_addr(ring);
 
-    // DMA op j of a tile fills LDS bytes [1024 j, 1024 j + 1024): chunk slot
-    // n = 64 j + lane, K rows first.  Slot n of a half holds logical chunk
-    // (n % kRowChunks) ^ chunk_xor(row) of row n / kRowChunks.
-    int goff[T::kDma];
+    // DMA op j of a half tile fills LDS bytes [1024 j, 1024 j + 1024): chunk
+    // slot n = 64 j + lane, holding logical chunk (n % kRowChunks) ^
+    // chunk_xor(row) of row n / kRowChunks.
+    int goff[T::kDmaHalf];
 #pragma unroll
-    for (int j = 0; j < T::kDma; ++j) {
-        const int n = (64 * j + lane) % (kTile * T::kRowChunks);
+    for (int j = 0; j < T::kDmaHalf; ++j) {
+        const int n = 64 * j + lane;
         const int row = n / T::kRowChunks;
         goff[j] = row * D + 8 * ((n % T::kRowChunks) ^ chunk_xor(row));
     }
     const size_t head_elems = (size_t)kPage * D;
-    auto issue = [&](const ItemCursor& c, int stage) {
+    char* const k_ring = ring;
+    char* const v_ring = ring + T::kKStages * T::kHalfBytes;
+    auto issue = [&](const uint16_t* __restrict__ cache, const ItemCursor& c, const char* dst_p) {
         const int ks = c.start + kTile * c.t;
         const int pg = page_table[(size_t)c.b * max_pages + ks / kPage];
-        const size_t base = ((size_t)pg * Hkv + c.kvh) * head_elems + (size_t)(ks % kPage) * D;
-        const uint32_t dst = ring_lds + (uint32_t)(stage * T::kBytes);
+        const uint16_t* src =
+            cache + ((size_t)pg * Hkv + c.kvh) * head_elems + (size_t)(ks % kPage) * D;
+        const uint32_t dst = lds_byte_addr(dst_p);
         // The stage's previous tile was read by this wave's ds_reads; make
         // sure they have returned before the DMA may overwrite it.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < T::kDma; ++j) {
-            const uint16_t* src = (j < T::kDma / 2 ? k_cache : v_cache) + base + goff[j];
-            dma16(src, __builtin_amdgcn_readfirstlane(dst + 1024u * j));
-        }
+        for (int j = 0; j < T::kDmaHalf; ++j)
+            dma16(src + goff[j], __builtin_amdgcn_readfirstlane(dst + 1024u * j));
     };
 
-    // Per-lane LDS byte offsets within a tile half.
+    // Per-lane LDS byte offsets within a half tile.
     //  K reads: row ln, logical chunk 2s + lh -> slot 8(s/4) + (2(s%4) ^ kx).
     const int kx = lh ^ chunk_xor(ln);
     int koff[4];
@@ -158,33 +158,61 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     const int g4 = lane >> 4, sl = lane & 15;
     const int vx = (2 * (g4 & 1) + ((sl & 3) >> 1)) ^ (2 * (sl >> 2) + ((g4 >> 1) & 1));
     const int vrow = (4 * (g4 >> 1) + (sl >> 2)) * T::kRowBytes + 8 * (sl & 1);
-    const int voff_e = T::kHalfBytes + vrow + 16 * vx;
-    const int voff_o = T::kHalfBytes + vrow + 16 * (4 ^ vx);
+    const int voff_e = vrow + 16 * vx;
+    const int voff_o = vrow + 16 * (4 ^ vx);
 
+    // Three cursors over the wave's tile stream: K DMA (three tiles ahead of
+    // the compute), V DMA (two ahead) and compute.  Issue order: K0 K1 V0 K2
+    // V1, then after computing tile c: K(c+3) V(c+2).  nk / nv count the
+    // halves issued; vmcnt waits count the 1 KiB ops issued after the one
+    // needed (DMAs complete in issue order).
     const int NRC = first[B];
     const long n_items = (long)NRC * Hkv;
     const int gw = blockIdx.x * 4 + wave;
-    ItemCursor ic;
-    cursor_begin(ic, (int)(n_items * gw / nw), (int)(n_items * (gw + 1) / nw), B, NRC, NQ, chunk,
+    ItemCursor kc;
+    cursor_begin(kc, (int)(n_items * gw / nw), (int)(n_items * (gw + 1) / nw), B, NRC, NQ, chunk,
                  first, seq_lens);
-    ItemCursor cc = ic;
-    int iseq = 0, cseq = 0;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        if (ic.item < ic.hi) {
-            issue(ic, iseq & 1);
-            ++iseq;
-            cursor_next(ic, NRC, NQ, chunk, first, seq_lens);
+    ItemCursor vc = kc, cc = kc;
+    int nk = 0, nv = 0;
+    auto issue_k = [&]() {
+        if (kc.item < kc.hi) {
+            issue(k_cache, kc, k_ring + (nk % T::kKStages) * T::kHalfBytes);
+            ++nk;
+            cursor_next(kc, NRC, NQ, chunk, first, seq_lens);
         }
-    }
+    };
+    auto issue_v = [&]() {
+        if (vc.item < vc.hi) {
+            issue(v_cache, vc, v_ring + (nv % T::kVStages) * T::kHalfBytes);
+            ++nv;
+            cursor_next(vc, NRC, NQ, chunk, first, seq_lens);
+        }
+    };
+    auto wait_groups = [&](int g) {  // at most g half tiles still in flight
+        switch (g) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<1 * T::kDmaHalf>(); break;
+            case 2: wait_vmcnt<2 * T::kDmaHalf>(); break;
+            case 3: wait_vmcnt<3 * T::kDmaHalf>(); break;
+            case 4: wait_vmcnt<4 * T::kDmaHalf>(); break;
+            default: wait_vmcnt<5 * T::kDmaHalf>(); break;
+        }
+    };
+    issue_k();
+    issue_k();
+    issue_v();
+    issue_k();
+    issue_v();
+    int cseq = 0;
 
     u32x4 qf[RB][NS];
     int lim[RB];
     float m_r[RB], l_r[RB];
     f32x16 o[RB][NDB];
     while (cc.item < cc.hi) {
-        // Tile cseq has landed once at most the next tile's DMAs are in flight.
-        if (iseq - cseq > 1) wait_vmcnt<T::kDma>(); else wait_vmcnt<0>();
+        // K(cseq) has landed once at most the halves issued after it are in
+        // flight: K(j > cseq) and V(j >= max(cseq - 1, 0)).
+        wait_groups((nk - 1 - cseq) + (nv - max(cseq - 1, 0)));
         if (cc.t == 0) {
             // New item: Q fragments (B operand; column = query row, k = d).
 #pragma unroll
@@ -210,19 +238,9 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
                     for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
             }
         }
-        char* tile = ring + (cseq & 1) * T::kBytes;
+        const char* ktile = k_ring + (cseq % T::kKStages) * T::kHalfBytes;
+        char* vtile = v_ring + (cseq % T::kVStages) * T::kHalfBytes;
         const int ks = cc.start + kTile * cc.t;
-        if (ks + kTile > cc.end) {
-            // Rows past the chunk end may hold anything (NaN included): zero
-            // their values so that P = 0 contributes exactly nothing.
-            const int nv = cc.end - ks;
-            for (int idx = lane; idx < (kTile - nv) * T::kRowChunks; idx += 64) {
-                const int row = nv + idx / T::kRowChunks, c = idx % T::kRowChunks;
-                *(u32x4*)(tile + T::kHalfBytes + row * T::kRowBytes + 16 * (c ^ chunk_xor(row))) =
-                    u32x4{0, 0, 0, 0};
-            }
-        }
-
         // S^T = K Q^T.
         f32x16 sacc[RB];
 #pragma unroll
@@ -231,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const u32x4 kf = *(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2));
+            const u32x4 kf = *(const u32x4*)(ktile + koff[s & 3] + 128 * (s >> 2));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma_32x32x16(kf, qf[rb][s], sacc[rb]);
         }
@@ -279,12 +297,26 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             pbl[rb][1] = u32x4{pl[4], pl[5], pl[6], pl[7]};
         }
 
+        // V(cseq) has landed once at most V(j > cseq) and K(j >= cseq + 2) are
+        // in flight.
+        wait_groups((nv - 1 - cseq) + max(0, nk - (cseq + 2)));
+        if (ks + kTile > cc.end) {
+            // Rows past the chunk end may hold anything (NaN included): zero
+            // their values so that P = 0 contributes exactly nothing.
+            const int nv = cc.end - ks;
+            for (int idx = lane; idx < (kTile - nv) * T::kRowChunks; idx += 64) {
+                const int row = nv + idx / T::kRowChunks, c = idx % T::kRowChunks;
+                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ chunk_xor(row))) =
+                    u32x4{0, 0, 0, 0};
+            }
+        }
+
         // O^T += V^T P^T.  Slot 8h + 4a + r of step tt is key 16tt + 8a + 4h + r.
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = tile + 16 * tt * T::kRowBytes + 128 * (db >> 1) +
+                const char* vp = vtile + 16 * tt * T::kRowBytes + 128 * (db >> 1) +
                                  ((db & 1) ? voff_o : voff_e);
                 const u32x2 v0 = lds_read_tr16(vp);
                 const u32x2 v1 = lds_read_tr16(vp + 8 * T::kRowBytes);
@@ -297,13 +329,10 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             }
         }
 
-        // This stage's reads are done (their MFMAs have consumed them): refill
-        // it with the tile two ahead in the wave's stream.
-        if (ic.item < ic.hi) {
-            issue(ic, iseq & 1);
-            ++iseq;
-            cursor_next(ic, NRC, NQ, chunk, first, seq_lens);
-        }
+        // This tile's stages are read: refill them three (K) and two (V)
+        // tiles ahead in the wave's stream.
+        issue_k();
+        issue_v();
         if (cc.t == cc.ntiles - 1) {
             const size_t pidx = ((size_t)cc.b * Hkv + cc.kvh) * max_splits + cc.split;
             float* po = part_o + pidx * D * R;
