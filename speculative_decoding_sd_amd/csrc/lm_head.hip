@@ -112,29 +112,41 @@ __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restric
 // Main bf16 path.  Computes the transposed tile D[v][m] = sum_k W[v][k] H[m][k]
 // (A = W rows, B = H rows) so that each lane's MFMA accumulator holds four
 // consecutive vocab entries of one output row: the epilogue stores 8 bytes.
-// TN x TM tile (vocab x rows), k in stages of 32, four LDS stages filled by
-// direct global->LDS DMA (global_load_lds_dwordx4) up to four stages ahead.  Each
-// stage has its own __shared__ array, so the compiler's wait tracking sees
-// which in-flight DMA a fragment read depends on; each wave waits for its own
-// oldest stage (s_waitcnt vmcnt) before the workgroup barrier.
-// LDS layout per stage: row r (W rows then H rows) holds 4 granules of 16
-// bytes (8 k values); chunk c sits at slot c ^ ((r >> 2) & 3), so the 16 lanes
-// of a quarter-wave reading 16 consecutive rows hit 16 distinct bank groups.
+// TN x TM tile (vocab x rows); k advances in stages of BK, staged in LDS by
+// direct global->LDS DMA (global_load_lds_dwordx4): NST stage buffers
+// (BK = 32: four, refilled up to three stages ahead; BK = 64: two).  With
+// BK = 64 every DMA request covers whole 128-byte rows of W and H (full L2
+// lines); with BK = 32 each request is half a line.
+// LDS layout per stage: row r (W rows then H rows) holds BK/8 granules of 16
+// bytes; granule c sits at slot c ^ f(r) (f(r) = (r/4)%4 for BK = 32, r%8 for
+// BK = 64), so the rows of one ds_read_b128 phase hit distinct bank groups.
 // ---------------------------------------------------------------------------
-constexpr int kStages = 4;
-constexpr int kBKs = 32;
+constexpr int kLmBK = 64;       // k per LDS stage of the DMA GEMM
 constexpr int kStageRows = 512;  // largest TN + TM
-__shared__ __attribute__((aligned(16))) uint16_t g_st0[kStageRows * kBKs];
-__shared__ __attribute__((aligned(16))) uint16_t g_st1[kStageRows * kBKs];
-__shared__ __attribute__((aligned(16))) uint16_t g_st2[kStageRows * kBKs];
-__shared__ __attribute__((aligned(16))) uint16_t g_st3[kStageRows * kBKs];
+constexpr int kLdsElems = 65536; // 128 KiB: 4 x 512 x 32 or 2 x 512 x 64 bf16
+__shared__ __attribute__((aligned(1024))) uint16_t g_lds[kLdsElems];
 
-template <int S>
-__device__ __forceinline__ uint16_t* stage_buf() {
-    return S == 0 ? g_st0 : S == 1 ? g_st1 : S == 2 ? g_st2 : g_st3;
+template <int TN, int TM, int WN, int WM, int BK>
+struct LmTile {
+    static constexpr int kRows = TN + TM;
+    static constexpr int kGran = BK / 8;                       // 16-byte granules per row
+    static constexpr int kStages = BK == 32 ? 4 : 2;
+    static constexpr int kSteps = BK / 16;                     // MFMA k-steps per stage
+    static constexpr int kStageElems = kStageRows * BK;
+    static constexpr int kDmaPerWave = kRows * kGran / 64 / 4; // 1 KiB DMA ops per wave
+    static constexpr int FN = TN / WN / 32;                    // 32-row MFMA blocks (vocab)
+    static constexpr int FM = TM / WM / 32;                    // 32-col MFMA blocks (rows)
+    static_assert(kRows * kGran % 256 == 0, "stage must split into whole wave DMAs");
+    static_assert(kRows <= kStageRows, "stage buffer too small");
+    static_assert(kStages * kStageElems <= kLdsElems, "stages exceed the LDS buffer");
+    static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
+};
+
+template <int BK>
+__device__ __forceinline__ int swz(int row, int c) {
+    if constexpr (BK == 32) return row * 4 + (c ^ ((row >> 2) & 3));
+    else return row * 8 + (c ^ (row & 7));
 }
-
-__device__ __forceinline__ int swz(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
 // s_waitcnt vmcnt(n) (expcnt and lgkmcnt left free), gfx9 encoding.
 template <int N>
@@ -148,40 +160,45 @@ __device__ __forceinline__ void block_barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
-template <int TN, int TM, int WN, int WM>
-struct LmTile {
-    static constexpr int kRows = TN + TM;
-    static constexpr int kDmaPerWave = kRows * 4 / 64 / 4;  // 64-granule DMA ops per wave per stage
-    static constexpr int FN = TN / WN / 32;                  // 32-row MFMA blocks per wave (vocab)
-    static constexpr int FM = TM / WM / 32;                  // 32-col MFMA blocks per wave (rows)
-    static_assert(kRows * 4 % 256 == 0, "stage must split into whole wave DMAs");
-    static_assert(kRows <= kStageRows, "stage buffer too small");
-};
-
-template <int TN, int TM, int WN, int WM, int S>
-__device__ __forceinline__ void lm_issue(const uint16_t* __restrict__ W,
-                                         const uint16_t* __restrict__ H, int n0, int m0, int M,
-                                         int N, int K, int kt, int wave, int lane) {
-    using T = LmTile<TN, TM, WN, WM>;
-    uint16_t* buf = stage_buf<S>();
-    const int k0 = kt * kBKs;
+// Per-lane DMA sources for k = 0: op i of a stage covers LDS granules
+// g = 64 (4i + wave) + lane, i.e. row g / kGran (W rows, then H rows),
+// logical granule c with swz(row, c) = g.  Rows past the matrix ends re-read
+// the last row (their results are never stored).
+template <int TN, int TM, int WN, int WM, int BK>
+__device__ __forceinline__ void lm_dma_bases(const uint16_t* __restrict__ W,
+                                             const uint16_t* __restrict__ H, int n0, int m0,
+                                             int M, int N, int K, int wave, int lane,
+                                             const uint16_t** src) {
+    using T = LmTile<TN, TM, WN, WM, BK>;
 #pragma unroll
     for (int i = 0; i < T::kDmaPerWave; ++i) {
-        const int g0 = (i * 4 + wave) * 64;
-        const int g = g0 + lane;
-        const int row = g >> 2;
-        const int c = (g & 3) ^ ((row >> 2) & 3);
-        const uint16_t* src;
-        if (row < TN) {
-            const int n = min(n0 + row, N - 1);
-            src = W + (size_t)n * K + k0 + 8 * c;
-        } else {
-            const int m = min(m0 + row - TN, M - 1);
-            src = H + (size_t)m * K + k0 + 8 * c;
-        }
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + g0 * 8),
-                                         16, 0, 0);
+        const int g = (i * 4 + wave) * 64 + lane;
+        const int row = g / T::kGran;
+        const int slot = g % T::kGran;
+        const int c = BK == 32 ? (slot ^ ((row >> 2) & 3)) : (slot ^ (row & 7));
+        if (row < TN)
+            src[i] = W + (size_t)min(n0 + row, N - 1) * K + 8 * c;
+        else
+            src[i] = H + (size_t)min(m0 + row - TN, M - 1) * K + 8 * c;
     }
+}
+
+// DMA op i into stage buffer S for k-slice kt.
+template <int TN, int TM, int WN, int WM, int BK, int S>
+__device__ __forceinline__ void lm_dma(const uint16_t* const* src, int i, int kt, int wave) {
+    using T = LmTile<TN, TM, WN, WM, BK>;
+    uint16_t* buf = g_lds + S * T::kStageElems;
+    const int g0 = (i * 4 + wave) * 64;
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * BK,
+                                     (__attribute__((address_space(3))) void*)(buf + g0 * 8), 16, 0,
+                                     0);
+}
+
+template <int TN, int TM, int WN, int WM, int BK, int S>
+__device__ __forceinline__ void lm_issue(const uint16_t* const* src, int kt, int wave) {
+#pragma unroll
+    for (int i = 0; i < LmTile<TN, TM, WN, WM, BK>::kDmaPerWave; ++i)
+        lm_dma<TN, TM, WN, WM, BK, S>(src, i, kt, wave);
 }
 
 // LDS byte address of a __shared__ element (for the inline-asm reads).
@@ -216,77 +233,113 @@ __device__ __forceinline__ void wait_frags(u32x4 (&a)[NA], u32x4 (&b)[NB]) {
         static_assert(NA < 0, "unsupported fragment counts");
 }
 
-template <int TN, int TM, int WN, int WM, int S>
+// Fragments of k-step `step` from stage buffer S.
+template <int TN, int TM, int WN, int WM, int BK, int S>
 __device__ __forceinline__ void lm_read_frags(u32x4 (&fa)[TN / WN / 32],
-                                              u32x4 (&fb)[TM / WM / 32], int s, int wn, int wm,
+                                              u32x4 (&fb)[TM / WM / 32], int step, int wn, int wm,
                                               int lane) {
-    const uint16_t* buf = stage_buf<S>();
+    const uint16_t* buf = g_lds + S * LmTile<TN, TM, WN, WM, BK>::kStageElems;
     const int ln = lane & 31, lh = lane >> 5;
-    const int c = 2 * s + lh;
+    const int c = 2 * step + lh;
 #pragma unroll
     for (int i = 0; i < TN / WN / 32; ++i)
-        fa[i] = ds_read16(lds_addr(buf + swz(wn * (TN / WN) + i * 32 + ln, c) * 8));
+        fa[i] = ds_read16(lds_addr(buf + swz<BK>(wn * (TN / WN) + i * 32 + ln, c) * 8));
 #pragma unroll
     for (int j = 0; j < TM / WM / 32; ++j)
-        fb[j] = ds_read16(lds_addr(buf + swz(TN + wm * (TM / WM) + j * 32 + ln, c) * 8));
+        fb[j] = ds_read16(lds_addr(buf + swz<BK>(TN + wm * (TM / WM) + j * 32 + ln, c) * 8));
 }
 
-template <int TN, int TM, int WN, int WM, int S>
-__device__ __forceinline__ void lm_mfma(f32x16 (&acc)[TN / WN / 32][TM / WM / 32],
-                                        const u32x4 (&fa)[TN / WN / 32],
-                                        const u32x4 (&fb)[TM / WM / 32]) {
+template <int FN, int FM>
+__device__ __forceinline__ void lm_mfma(f32x16 (&acc)[FN][FM], const u32x4 (&fa)[FN],
+                                        const u32x4 (&fb)[FM]) {
 #pragma unroll
-    for (int i = 0; i < TN / WN / 32; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM / WM / 32; ++j) acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
+}
+
+// A k-step's MFMAs with the refill DMAs of buffer SD (k-slice kt)
+// interleaved, so the matrix pipe keeps working while they issue.
+template <int TN, int TM, int WN, int WM, int BK, int SD>
+__device__ __forceinline__ void lm_mfma_dma(f32x16 (&acc)[TN / WN / 32][TM / WM / 32],
+                                            const u32x4 (&fa)[TN / WN / 32],
+                                            const u32x4 (&fb)[TM / WM / 32],
+                                            const uint16_t* const* src, int kt, int wave) {
+    using T = LmTile<TN, TM, WN, WM, BK>;
+    constexpr int NM = T::FN * T::FM;
+    constexpr int per = NM / T::kDmaPerWave > 0 ? NM / T::kDmaPerWave : 1;
+    constexpr int ndma = NM / per < T::kDmaPerWave ? NM / per : T::kDmaPerWave;
+#pragma unroll
+    for (int idx = 0; idx < NM; ++idx) {
+        const int i = idx / T::FM, j = idx % T::FM;
+        acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
+        if ((idx + 1) % per == 0 && (idx + 1) / per <= ndma)
+            lm_dma<TN, TM, WN, WM, BK, SD>(src, (idx + 1) / per - 1, kt, wave);
+    }
+#pragma unroll
+    for (int i = ndma; i < T::kDmaPerWave; ++i) lm_dma<TN, TM, WN, WM, BK, SD>(src, i, kt, wave);
+    // Scheduling groups: `per` MFMAs, then one VMEM (the DMA), repeated.
+#pragma unroll
+    for (int i = 0; i < ndma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
 }
 
 // One pipeline stage kt (buffer S).  On entry fa0/fb0 hold the stage's step-0
-// fragments.  The workgroup barrier for stage kt+1 sits after step 0's MFMAs
-// are queued, so the matrix pipe keeps working through the barrier and the
-// next stage's step-0 fragment reads; the freed buffer S is refilled with
-// stage kt+4 right after the barrier.
+// fragments.  Each k-step's MFMAs run while the next step's fragments load;
+// before the last step the workgroup waits for stage kt+1 (barrier), starts
+// reading its step-0 fragments, and runs the last step's MFMAs with the refill
+// of buffer S (stage kt + kStages) interleaved.
 // No branch may separate an asm fragment read from its lgkmcnt wait: at a
 // control-flow merge the compiler may copy the (not yet loaded) registers.
-// So the reads are unconditional (the last stage reads a spent buffer whose
-// values are never used) and K is a multiple of 4 stages.
-template <int TN, int TM, int WN, int WM, int S>
-__device__ __forceinline__ void lm_stage(
-    const uint16_t* __restrict__ W, const uint16_t* __restrict__ H,
-    f32x16 (&acc)[TN / WN / 32][TM / WM / 32], u32x4 (&fa0)[TN / WN / 32],
-    u32x4 (&fb0)[TM / WM / 32], int n0, int m0, int M, int N, int K, int kt, int nk, int wave,
-    int wn, int wm, int lane) {
-    using T = LmTile<TN, TM, WN, WM>;
-    u32x4 fa1[T::FN], fb1[T::FM];
-    lm_read_frags<TN, TM, WN, WM, S>(fa1, fb1, 1, wn, wm, lane);
-    // sched_barrier(0) keeps the scheduler from moving the MFMA blocks across
-    // the waits and barriers (they do not depend on the asm operands).
-    __builtin_amdgcn_sched_barrier(0);
-    lm_mfma<TN, TM, WN, WM, S>(acc, fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_frags(fa1, fb1);
-    // Stage kt+1 must have landed; kt+2 and kt+3 may still be in flight.
-    const int later = max(0, min(2, nk - 2 - kt));
-    if (later == 2) wait_vmcnt<2 * T::kDmaPerWave>();
-    else if (later == 1) wait_vmcnt<T::kDmaPerWave>();
-    else wait_vmcnt<0>();
-    block_barrier_lds();
-    if (kt + kStages < nk)
-        lm_issue<TN, TM, WN, WM, S>(W, H, n0, m0, M, N, K, kt + kStages, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    lm_read_frags<TN, TM, WN, WM, (S + 1) % kStages>(fa0, fb0, 0, wn, wm, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    lm_mfma<TN, TM, WN, WM, S>(acc, fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_frags(fa0, fb0);
+// So everything is unconditional: the last stage reads a spent buffer whose
+// values are never used, and the final refills re-read k-slice nk-1 (the
+// kernel waits for them before it ends).  nk is a multiple of kStages.
+template <int TN, int TM, int WN, int WM, int BK, int S, int STEP>
+__device__ __forceinline__ void lm_steps(const uint16_t* const* src,
+                                         f32x16 (&acc)[TN / WN / 32][TM / WM / 32],
+                                         u32x4 (&fa0)[TN / WN / 32], u32x4 (&fb0)[TM / WM / 32],
+                                         u32x4 (&fa1)[TN / WN / 32], u32x4 (&fb1)[TM / WM / 32],
+                                         int kt, int nk, int wave, int wn, int wm, int lane) {
+    using T = LmTile<TN, TM, WN, WM, BK>;
+    // Fragment sets alternate: even steps use set 0, odd steps set 1.
+    u32x4(&cur_a)[T::FN] = (STEP % 2 == 0) ? fa0 : fa1;
+    u32x4(&cur_b)[T::FM] = (STEP % 2 == 0) ? fb0 : fb1;
+    u32x4(&nxt_a)[T::FN] = (STEP % 2 == 0) ? fa1 : fa0;
+    u32x4(&nxt_b)[T::FM] = (STEP % 2 == 0) ? fb1 : fb0;
+    if constexpr (STEP + 1 < T::kSteps) {
+        lm_read_frags<TN, TM, WN, WM, BK, S>(nxt_a, nxt_b, STEP + 1, wn, wm, lane);
+        // sched_barrier(0) keeps the scheduler from moving the MFMA blocks
+        // across the waits and barriers (they do not depend on asm operands).
+        __builtin_amdgcn_sched_barrier(0);
+        lm_mfma<T::FN, T::FM>(acc, cur_a, cur_b);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_frags(nxt_a, nxt_b);
+        lm_steps<TN, TM, WN, WM, BK, S, STEP + 1>(src, acc, fa0, fb0, fa1, fb1, kt, nk, wave, wn,
+                                                  wm, lane);
+    } else {
+        // Stage kt+1 must have landed; with four stages the refills of kt+2
+        // and kt+3 may still be in flight.
+        if constexpr (T::kStages == 4) wait_vmcnt<2 * T::kDmaPerWave>();
+        else wait_vmcnt<0>();
+        block_barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        lm_read_frags<TN, TM, WN, WM, BK, (S + 1) % T::kStages>(nxt_a, nxt_b, 0, wn, wm, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        lm_mfma_dma<TN, TM, WN, WM, BK, S>(acc, cur_a, cur_b, src,
+                                           min(kt + T::kStages, nk - 1), wave);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_frags(nxt_a, nxt_b);
+    }
 }
 
-template <int TN, int TM, int WN, int WM>
+template <int TN, int TM, int WN, int WM, int BK>
 __global__ __launch_bounds__(256, 1) void lm_head_dma(const uint16_t* __restrict__ H,
                                                       const uint16_t* __restrict__ W,
                                                       uint16_t* __restrict__ C, int M, int N,
                                                       int K) {
-    using T = LmTile<TN, TM, WN, WM>;
+    using T = LmTile<TN, TM, WN, WM, BK>;
     const int tiles_m = (M + TM - 1) / TM;
     const int tiles_n = (N + TN - 1) / TN;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
@@ -304,25 +357,34 @@ __global__ __launch_bounds__(256, 1) void lm_head_dma(const uint16_t* __restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = K / kBKs;
-    lm_issue<TN, TM, WN, WM, 0>(W, H, n0, m0, M, N, K, 0, wave, lane);
-    lm_issue<TN, TM, WN, WM, 1>(W, H, n0, m0, M, N, K, 1, wave, lane);
-    lm_issue<TN, TM, WN, WM, 2>(W, H, n0, m0, M, N, K, 2, wave, lane);
-    lm_issue<TN, TM, WN, WM, 3>(W, H, n0, m0, M, N, K, 3, wave, lane);
-    wait_vmcnt<3 * T::kDmaPerWave>();
-    block_barrier_lds();
-    u32x4 fa0[T::FN], fb0[T::FM];
-    lm_read_frags<TN, TM, WN, WM, 0>(fa0, fb0, 0, wn, wm, lane);
-    wait_frags(fa0, fb0);
-    for (int kt = 0; kt < nk; kt += kStages) {  // nk is a multiple of kStages
-        lm_stage<TN, TM, WN, WM, 0>(W, H, acc, fa0, fb0, n0, m0, M, N, K, kt, nk, wave, wn, wm, lane);
-        lm_stage<TN, TM, WN, WM, 1>(W, H, acc, fa0, fb0, n0, m0, M, N, K, kt + 1, nk, wave, wn, wm,
-                                    lane);
-        lm_stage<TN, TM, WN, WM, 2>(W, H, acc, fa0, fb0, n0, m0, M, N, K, kt + 2, nk, wave, wn, wm,
-                                    lane);
-        lm_stage<TN, TM, WN, WM, 3>(W, H, acc, fa0, fb0, n0, m0, M, N, K, kt + 3, nk, wave, wn, wm,
-                                    lane);
+    const int nk = K / BK;
+    const uint16_t* src[T::kDmaPerWave];
+    lm_dma_bases<TN, TM, WN, WM, BK>(W, H, n0, m0, M, N, K, wave, lane, src);
+    lm_issue<TN, TM, WN, WM, BK, 0>(src, 0, wave);
+    lm_issue<TN, TM, WN, WM, BK, 1>(src, 1, wave);
+    if constexpr (T::kStages == 4) {
+        lm_issue<TN, TM, WN, WM, BK, 2>(src, 2, wave);
+        lm_issue<TN, TM, WN, WM, BK, 3>(src, 3, wave);
     }
+    wait_vmcnt<(T::kStages - 1) * T::kDmaPerWave>();
+    block_barrier_lds();
+    u32x4 fa0[T::FN], fb0[T::FM], fa1[T::FN], fb1[T::FM];
+    lm_read_frags<TN, TM, WN, WM, BK, 0>(fa0, fb0, 0, wn, wm, lane);
+    wait_frags(fa0, fb0);
+    for (int kt = 0; kt < nk; kt += T::kStages) {
+        lm_steps<TN, TM, WN, WM, BK, 0, 0>(src, acc, fa0, fb0, fa1, fb1, kt, nk, wave, wn, wm, lane);
+        lm_steps<TN, TM, WN, WM, BK, 1, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 1, nk, wave, wn, wm,
+                                           lane);
+        if constexpr (T::kStages == 4) {
+            lm_steps<TN, TM, WN, WM, BK, 2, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 2, nk, wave, wn,
+                                               wm, lane);
+            lm_steps<TN, TM, WN, WM, BK, 3, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 3, nk, wave, wn,
+                                               wm, lane);
+        }
+    }
+    // The last refills (re-reads of the final k-slice) must land before the
+    // workgroup's LDS is released.
+    wait_vmcnt<0>();
 
     // Lane (ln, lh) holds D[n][m] for m = column ln of each block and, per
     // group q of four registers, the four consecutive n = 8q + 4lh .. +3.
@@ -393,7 +455,7 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
             (const float*)H, (const float*)W, (float*)logits, M, vocab, hidden);
         return check_launch("lm_head_f32");
     }
-    if (hidden % (kBKs * kStages) == 0) {
+    if (hidden % 128 == 0) {
         // Tile rows to the batch: all rows in one tile where possible, so each
         // W tile is streamed from HBM once.
         int TM = M > 128 ? 256 : (M > 64 ? 128 : 64);
@@ -403,11 +465,14 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         const uint16_t* w = (const uint16_t*)W;
         uint16_t* c = (uint16_t*)logits;
         if (TM == 256)
-            lm_head_dma<256, 256, 2, 2><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab, hidden);
+            lm_head_dma<256, 256, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+                                                                               hidden);
         else if (TM == 128)
-            lm_head_dma<256, 128, 2, 2><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab, hidden);
+            lm_head_dma<256, 128, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+                                                                               hidden);
         else
-            lm_head_dma<256, 64, 4, 1><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab, hidden);
+            lm_head_dma<256, 64, 4, 1, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+                                                                              hidden);
         return check_launch("lm_head_dma");
     }
     const long tiles = (long)((M + kBM - 1) / kBM) * ((vocab + kBN - 1) / kBN);
