@@ -28,7 +28,7 @@ HIPCC_FLAGS = [
 # attention kernels' LDS DMA sets M0 in inline asm; they have no other M0 use,
 # so the reserved-register clobber warning is silenced for them.
 EXTRA_FLAGS = {
-    "attn_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"],
+    "attn_mla.hip": ["-Wno-inline-asm"],
     "attn_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"],
 }
 

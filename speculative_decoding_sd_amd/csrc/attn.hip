@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
 struct AttnPlan {
     int G = 0, R = 0, chunk = 0, max_splits = 0;
     int path = 0;  // 0 gqa bf16 (MFMA), 1 gqa f32, 2 mla bf16
-    size_t off_valid = 0, off_first = 0, off_po = 0, off_pml = 0, total = 0;
+    size_t off_valid = 0, off_first = 0, off_flags = 0, off_po = 0, off_pml = 0, total = 0;
 };
 
 int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
@@ -377,6 +377,11 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
     off = align_up(off + sizeof(int32_t) * d->batch, 256);
     p->off_first = off;
     off = align_up(off + sizeof(int32_t) * (d->batch + 1), 256);
+    p->off_flags = off;
+    if (p->path == 2)
+        off = align_up(off + sizeof(int32_t) *
+                                 mla_flag_count(d->batch, d->num_q, d->n_q_heads, p->max_splits),
+                       256);
     p->off_po = off;
     const size_t nparts = (size_t)d->batch * d->n_kv_heads *
                           (p->path == 2 && p->max_splits == 1 ? 0 : p->max_splits) * p->R;
@@ -452,7 +457,8 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     float2* pml = (float2*)(ws + p.off_pml);
     const float scale_log2 = scale * 1.4426950408889634f;
     if (p.path == 2) {
-        if ((rc = mla_launch(d, valid, po, pml, p.chunk, p.max_splits, scale_log2, s)) != SD_OK)
+        int32_t* flags = (int32_t*)(ws + p.off_flags);
+        if ((rc = mla_launch(d, valid, flags, po, pml, p.chunk, p.max_splits, scale, s)) != SD_OK)
             return rc;
         if (p.max_splits == 1) return SD_OK;
         attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),

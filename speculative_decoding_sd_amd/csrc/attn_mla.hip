@@ -9,8 +9,8 @@
 // not by HBM (about 970 flop per latent byte).  Layout of the work:
 //   workgroup = 128 query rows of one request x one chunk of keys, 4 waves;
 //   wave      = 32 rows (one position i, 32 heads) and all 512 output dims,
-//               O^T in 16 MFMA 32x32 accumulators (256 AGPRs), Q^T of its
-//               rows resident in 144 VGPRs for the whole chunk.
+//               O^T in 16 MFMA 32x32 accumulators, Q^T of its rows resident
+//               (registers and LDS) for the whole chunk.
 // Per 32-key tile:
 //   S^T = K Q^T   A = latent rows read from LDS with ds_read_b128, B = Q^T;
 //   online softmax lane-local (one query row per lane column).  The running
@@ -23,8 +23,12 @@
 //                 reading 4 dims of key row key0 + s/4 gives lane t the 4-key
 //                 column of dim d0 + t); P split into bf16 hi + lo halves (two
 //                 MFMAs per fragment) to hold the fp32 output accuracy.
-// Latent tiles arrive by LDS DMA (global_load_lds_dwordx4) three tiles deep,
-// so no registers stage them.  The 16-byte chunks of each 1152-byte latent row
+// Latent tiles arrive by LDS DMA (global_load_lds_dwordx4), double-buffered,
+// so no registers stage them.  Register budget (one wave per SIMD, 512
+// registers): O^T blocks 0..14 (240) and S^T (16) in AGPRs, the last O^T block
+// kept in LDS between tiles so that S^T can use its registers; half of Q^T in
+// VGPRs and half in LDS (read once per tile); the rest is fragment
+// prefetch, P and addressing.  LDS: 72 KiB latent + 72 KiB Q^T + 16 KiB O^T.  The 16-byte chunks of each 1152-byte latent row
 // are XOR-swizzled so that both LDS read patterns are free of bank conflicts.
 // With one chunk per request the kernel writes the normalised output itself;
 // otherwise it writes chunk partials for attn_combine.
@@ -44,18 +48,24 @@ constexpr int kTileKeys = 32;
 constexpr int kRowChunks = kDqk / 8;                       // 72 chunks of 16 bytes
 constexpr int kRowBytes = kDqk * 2;                        // 1152
 constexpr int kTileElems = kTileKeys * kDqk;               // 18432 bf16 = 36 KiB
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr int kDmaPerWave = kTileKeys * kRowChunks / 256;  // 9 x 1 KiB per wave
-constexpr float kRescaleSlack = 8.f;                       // log2 units
+constexpr float kRefSlack = 64.f;  // log2 units a later tile may exceed the reference max by
 constexpr int kRowsPerBlock = 128;
+constexpr int kQSteps = kDqk / 16;     // 36 MFMA k-steps over the latent
+constexpr int kQReg = 18;              // Q^T steps held in registers
+constexpr int kQLds = kQSteps - kQReg; // Q^T steps read from LDS each tile
 
 __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ valid, float* __restrict__ out, uint16_t* __restrict__ out_lowp,
-    float* __restrict__ part_o, float2* __restrict__ part_ml, int NQ, int Hq, int R,
-    int max_pages, int chunk, int max_splits, int rblks, int total, float scale_log2) {
+    float* __restrict__ part_o, float2* __restrict__ part_ml, int32_t* __restrict__ flags, int NQ,
+    int Hq, int R, int max_pages, int chunk, int max_splits, int rblks, int total,
+    float scale_log2) {
     __shared__ __attribute__((aligned(1024))) uint16_t s_lat[kStages][kTileElems];
+    __shared__ __attribute__((aligned(16))) float s_o15[4][16 * 64];
+    __shared__ __attribute__((aligned(16))) u32x4 s_qh[4][kQLds][64];
     const int tile_id = xcd_tile(blockIdx.x, total);
     const int rblk = tile_id % rblks;
     const int split = (tile_id / rblks) % max_splits;
@@ -75,28 +85,31 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const int lim = L + pos_i;  // causal: keys 0 .. L_b + i
 
     // Q^T fragments (B operand): lane (row ln, half lh), step s -> dims 16s+8lh..+8.
-    u32x4 qf[kDqk / 16];
-    if (rows_live) {
+    // Steps 0..kQReg-1 stay in registers; the rest go to this wave's LDS
+    // slot (lane order, so each step is one conflict-free 16-byte read).
+    u32x4 qf[kQReg];
+    {
         const int row = row0 + ln;
-        const int i = row / Hq, h = row - i * Hq;
+        const int i = rows_live ? row / Hq : 0, h = rows_live ? row - i * Hq : 0;
         const uint16_t* qp = q + (((size_t)b * NQ + i) * Hq + h) * kDqk + 8 * lh;
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s) qf[s] = *(const u32x4*)(qp + 16 * s);
-    } else {
+        for (int s = 0; s < kQReg; ++s)
+            qf[s] = rows_live ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s) qf[s] = u32x4{0, 0, 0, 0};
+        for (int s = kQReg; s < kQSteps; ++s) {
+            s_qh[wave][s - kQReg][lane] = rows_live ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
+            if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // DMA slots of this lane: instruction j of wave w fills LDS chunks
     // n = 64 (4j + w) + lane of the tile; chunk n holds latent row n / 72,
     // logical chunk (n % 72) ^ chunk_xor(row).
-    int goff[kDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
+    auto goff = [&](int j) {
         const int n = 64 * (4 * j + wave) + lane;
         const int key = n / kRowChunks;
-        goff[j] = key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
-    }
+        return key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
+    };
     const uint32_t lds0 = lds_byte_addr(&s_lat[0][0]);
     auto issue_tile = [&](int t) {
         const int ks = start + kTileKeys * t;
@@ -105,7 +118,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileElems * 2);
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j)
-            dma16(base + goff[j],
+            dma16(base + goff(j),
                   __builtin_amdgcn_readfirstlane(dst + (uint32_t)(1024 * (4 * j + wave))));
     };
 
@@ -122,25 +135,31 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const int vrow = (4 * (g >> 1) + (sl >> 2)) * kRowBytes + 8 * (sl & 1);
     const int voff_e = vrow + 16 * vx, voff_o = vrow + 16 * (4 ^ vx);
 
+    // O^T blocks 0..14 live in registers; block 15 lives in this wave's LDS
+    // slot between tiles (layout [q][lane][4] floats: conflict-free 16-byte
+    // accesses), so that S^T can use its registers while it is computed.
+    float* o15_lds = s_o15[wave];
     float m_r = -INFINITY, l_r = 0.f;
-    f32x16 o[kDv / 32];
+    bool over = false;
+    f32x16 o[kDv / 32 - 1];
 #pragma unroll
-    for (int db = 0; db < kDv / 32; ++db)
+    for (int db = 0; db < kDv / 32 - 1; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) *(f32x4*)(o15_lds + (qd * 64 + lane) * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Two stages: tile t+1 loads while tile t is computed.  At the top of
+    // iteration t, tile t (issued one iteration earlier) has landed and every
+    // wave has left iteration t-1, so stage (t+1)%2 is free to refill.
     issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
     for (int t = 0; t < ntiles; ++t) {
-        // Tile t has landed once at most the next tile's DMAs are in flight.
-        if (t + 1 < ntiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+        wait_vmcnt<0>();
         // This wave's reads of tile t-1 must have returned before another
         // wave refills that stage after the barrier.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         barrier_only();
-        // Stage (t+2)%3 was last read in iteration t-1, which every wave has
-        // left through the barrier above.
-        if (t + 2 < ntiles) issue_tile(t + 2);
+        if (t + 1 < ntiles) issue_tile(t + 1);
         const char* tile = (const char*)&s_lat[t % kStages][0];
         const int ks = start + kTileKeys * t;
         if (t == ntiles - 1 && end - ks < kTileKeys) {
@@ -153,16 +172,34 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             }
             __syncthreads();
         }
-        if (!rows_live) continue;
 
-        // S^T = K Q^T over 576 dims (one accumulator: with 256 output
-        // accumulators a second one does not fit the register file).
+        // S^T = K Q^T over 576 dims, K (and LDS-held Q^T) fragments read ahead.
         f32x16 sa;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+        constexpr int PF = 4;  // read-ahead distance in k-steps
+        u32x4 kf[PF], qx[PF];
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s)
-            sa = mfma_32x32x16(*(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2)), qf[s], sa);
+        for (int s = 0; s < PF; ++s) {
+            kf[s] = *(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2));
+            qx[s] = s_qh[wave][s][lane];
+        }
+#pragma unroll
+        for (int s = 0; s < kQSteps; ++s) {
+            const u32x4 cur = kf[s % PF];
+            u32x4 qcur;
+            if (s < kQReg) {
+                qcur = qf[s];
+            } else {
+                qcur = qx[(s - kQReg) % PF];
+                if (s - kQReg + PF < kQLds) qx[(s - kQReg) % PF] = s_qh[wave][s - kQReg + PF][lane];
+            }
+            if (s + PF < kQSteps)
+                kf[s % PF] = *(const u32x4*)(tile + koff[(s + PF) & 3] + 128 * ((s + PF) >> 2));
+            sa = mfma_32x32x16(cur, qcur, sa);
+            // Bounds how far the scheduler hoists reads.
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // Online softmax (lane holds 16 keys of query row ln).
         float tmax = -INFINITY;
 #pragma unroll
@@ -173,19 +210,12 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             tmax = fmaxf(tmax, sa[r]);
         }
         tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const bool raise = tmax > m_r + kRescaleSlack;
-        if (__any(raise)) {
-            const float mnew = raise ? tmax : m_r;
-            const float alpha = raise ? __builtin_amdgcn_exp2f(m_r - mnew) : 1.f;  // 0 if m_r = -inf
-            l_r *= alpha;
-            m_r = mnew;
-            // One accumulator at a time: bounds the VGPR copies of AGPRs.
-#pragma unroll
-            for (int db = 0; db < kDv / 32; ++db) {
-                o[db] *= alpha;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        // The chunk's first tile sets each row's reference max; later tiles
+        // are exponentiated against it (P up to 2^64 is exact enough in the
+        // hi/lo split and safe in fp32).  A row whose later scores exceed the
+        // reference by more than that is left to the exact path (flag).
+        if (t == 0) m_r = tmax;
+        else over |= tmax > m_r + kRefSlack;
         const float msafe = (m_r == -INFINITY) ? 0.f : m_r;
         float psum = 0.f;
         uint32_t pk[8], pl[8];
@@ -200,25 +230,63 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         }
         psum += shfl_xor(psum, 32);
         l_r += psum;
+        // Block 15 back from LDS (S^T is dead now; the barrier keeps the load
+        // from being hoisted into S^T's live range).
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 o15;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = *(const f32x4*)(o15_lds + (qd * 64 + lane) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o15[4 * qd + e] = v[e];
+        }
         const u32x4 pb[2] = {u32x4{pk[0], pk[1], pk[2], pk[3]}, u32x4{pk[4], pk[5], pk[6], pk[7]}};
         const u32x4 pbl[2] = {u32x4{pl[0], pl[1], pl[2], pl[3]},
                               u32x4{pl[4], pl[5], pl[6], pl[7]}};
         // O^T += V^T P^T.  Slot 8h + 4a + r of step tt is key 16tt + 8a + 4h + r.
+        // V^T fragments are read ahead.
+        auto vfrag = [&](int idx) {  // idx = tt * 16 + db
+            const int tt = idx >> 4, db = idx & 15;
+            const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1) + ((db & 1) ? voff_o : voff_e);
+            const u32x2 v0 = lds_read_tr16(vp);
+            const u32x2 v1 = lds_read_tr16(vp + 8 * kRowBytes);
+            return u32x4{v0.x, v0.y, v1.x, v1.y};
+        };
+        constexpr int PV = 3;  // V^T fragments read this many blocks ahead
+        u32x4 vf[PV];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int idx = 0; idx < PV; ++idx) vf[idx] = vfrag(idx);
 #pragma unroll
-            for (int db = 0; db < kDv / 32; ++db) {
-                const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1) +
-                                 ((db & 1) ? voff_o : voff_e);
-                const u32x2 v0 = lds_read_tr16(vp);
-                const u32x2 v1 = lds_read_tr16(vp + 8 * kRowBytes);
-                const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
-                o[db] = mfma_32x32x16(vf, pb[tt], o[db]);
-                o[db] = mfma_32x32x16(vf, pbl[tt], o[db]);
+        for (int idx = 0; idx < 32; ++idx) {
+            const u32x4 cur = vf[idx % PV];
+            if (idx + PV < 32) vf[idx % PV] = vfrag(idx + PV);
+            const int tt = idx >> 4, db = idx & 15;
+            if (db < 15) {
+                o[db] = mfma_32x32x16(cur, pb[tt], o[db]);
+                o[db] = mfma_32x32x16(cur, pbl[tt], o[db]);
+            } else {
+                o15 = mfma_32x32x16(cur, pb[tt], o15);
+                o15 = mfma_32x32x16(cur, pbl[tt], o15);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+            *(f32x4*)(o15_lds + (qd * 64 + lane) * 4) =
+                f32x4{o15[4 * qd], o15[4 * qd + 1], o15[4 * qd + 2], o15[4 * qd + 3]};
     }
+    // Flag of this wave's rows for this chunk: 1 sends them to the exact path.
+    const bool wave_over = __any(over);
+    if (lane == 0) flags[(((size_t)b * max_splits + split) * rblks + rblk) * 4 + wave] = wave_over ? 1 : 0;
     if (!rows_live) return;
+    f32x16 o15;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 v = *(const f32x4*)(o15_lds + (qd * 64 + lane) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o15[4 * qd + e] = v[e];
+    }
+    auto oblk = [&](int db, int r) -> float { return db < 15 ? o[db < 15 ? db : 0][r] : o15[r]; };
 
     const int nsplit = (Ltot + chunk - 1) / chunk;
     const int row = row0 + ln;
@@ -231,8 +299,8 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         for (int db = 0; db < kDv / 32; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
-                                 o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv};
+                const f32x4 v = {oblk(db, 4 * j) * inv, oblk(db, 4 * j + 1) * inv,
+                                 oblk(db, 4 * j + 2) * inv, oblk(db, 4 * j + 3) * inv};
                 *(f32x4*)(op + db * 32 + 8 * j) = v;
                 if (lp)
                     *(u32x2*)(lp + db * 32 + 8 * j) =
@@ -245,8 +313,105 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
 #pragma unroll
     for (int db = 0; db < kDv / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[db][r];
+        for (int r = 0; r < 16; ++r) po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = oblk(db, r);
     if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r, l_r);
+}
+
+// Exact path for the rows the fast kernel flagged (a later key scoring more
+// than 2^64 above the chunk's first-tile max): plain fp32 arithmetic, scores
+// by dot products, a max pass, then o = sum p v / sum p.  One workgroup per
+// (request, chunk, row block, wave) unit; units without a flag exit at once.
+// Writes the same output (single chunk) or partial (m, l, O) as the fast path.
+__global__ __launch_bounds__(256) void attn_mla_exact(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ valid, const int32_t* __restrict__ flags, float* __restrict__ out,
+    uint16_t* __restrict__ out_lowp, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int NQ, int Hq, int R, int max_pages, int chunk, int max_splits, int rblks, float scale) {
+    __shared__ float s_q[kDqk];
+    __shared__ float s_red[256];
+    __shared__ float s_p[256];
+    const int unit = blockIdx.x;
+    const int wave = unit % 4, rblk = (unit / 4) % rblks;
+    const int split = (unit / 4 / rblks) % max_splits, b = unit / 4 / rblks / max_splits;
+    if (!valid[b] || !flags[unit]) return;
+    const int L = seq_lens[b], Ltot = L + NQ;
+    const int start = split * chunk;
+    if (start >= Ltot) return;
+    const int end = min(start + chunk, Ltot);
+    const int nsplit = (Ltot + chunk - 1) / chunk;
+    const int tid = threadIdx.x;
+    auto latent = [&](int key) {
+        const int pg = page_table[(size_t)b * max_pages + key / kPage];
+        return lat + ((size_t)pg * kPage + key % kPage) * kDqk;
+    };
+    for (int rr = 0; rr < 32; ++rr) {
+        const int row = rblk * kRowsPerBlock + wave * 32 + rr;
+        if (row >= R) break;
+        const int i = row / Hq, h = row - i * Hq;
+        const int lim = min(end - 1, L + i);
+        const uint16_t* qp = q + (((size_t)b * NQ + i) * Hq + h) * kDqk;
+        for (int d = tid; d < kDqk; d += 256) s_q[d] = bf16_to_f32(qp[d]);
+        __syncthreads();
+        // Pass 1: row max over the chunk's visible keys.
+        float m = -INFINITY;
+        for (int key = start + tid; key <= lim; key += 256) {
+            const uint16_t* kp = latent(key);
+            float dot = 0.f;
+            for (int d = 0; d < kDqk; ++d) dot += s_q[d] * bf16_to_f32(kp[d]);
+            m = fmaxf(m, dot * scale);
+        }
+        s_red[tid] = m;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+            __syncthreads();
+        }
+        m = s_red[0];
+        __syncthreads();
+        // Pass 2: p = exp(s - m); thread d accumulates output dims d, d+256.
+        float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+        for (int k0 = start; k0 <= lim; k0 += 256) {
+            const int key = k0 + tid;
+            float p = 0.f;
+            if (key <= lim) {
+                const uint16_t* kp = latent(key);
+                float dot = 0.f;
+                for (int d = 0; d < kDqk; ++d) dot += s_q[d] * bf16_to_f32(kp[d]);
+                p = expf(dot * scale - m);
+            }
+            s_p[tid] = p;
+            __syncthreads();
+            const int cnt = min(256, lim - k0 + 1);
+            for (int k = 0; k < cnt; ++k) {
+                const uint16_t* vp = latent(k0 + k);
+                acc0 += s_p[k] * bf16_to_f32(vp[tid]);
+                acc1 += s_p[k] * bf16_to_f32(vp[tid + 256]);
+                lsum += s_p[k];
+            }
+            __syncthreads();
+        }
+        if (nsplit == 1) {
+            const float inv = 1.f / lsum;
+            float* op = out + ((size_t)b * R + row) * kDv;
+            op[tid] = acc0 * inv;
+            op[tid + 256] = acc1 * inv;
+            if (out_lowp) {
+                uint16_t* lp = out_lowp + ((size_t)b * R + row) * kDv;
+                lp[tid] = (uint16_t)f32_to_bf16_rne(acc0 * inv);
+                lp[tid + 256] = (uint16_t)f32_to_bf16_rne(acc1 * inv);
+            }
+        } else {
+            // Partial in the fast path's units: m in log2 units, O and l
+            // relative to 2^m.
+            const size_t pidx = (size_t)b * max_splits + split;
+            float* po = part_o + pidx * kDv * R;
+            po[(size_t)tid * R + row] = acc0;
+            po[(size_t)(tid + 256) * R + row] = acc1;
+            if (tid == 0) part_ml[pidx * R + row] = make_float2(m * 1.4426950408889634f, lsum);
+        }
+        __syncthreads();
+    }
 }
 
 }  // namespace
@@ -270,17 +435,29 @@ int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, i
     return SD_OK;
 }
 
-int mla_launch(const sd_attn_desc* d, const int32_t* valid, float* po, float2* pml, int chunk,
-               int max_splits, float scale_log2, hipStream_t s) {
+int mla_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* flags, float* po,
+               float2* pml, int chunk, int max_splits, float scale, hipStream_t s) {
     const int R = d->num_q * d->n_q_heads;
     const int rblks = (R + kRowsPerBlock - 1) / kRowsPerBlock;
     const long total = (long)d->batch * max_splits * rblks;
-    if (total > 0x7fffffff) return fail(SD_EUNSUPPORTED, "sd_verify_attn: MLA grid too large");
+    if (total * 4 > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_verify_attn: MLA grid too large");
     attn_mla_bf16<<<dim3((unsigned)total), 256, 0, s>>>(
         (const uint16_t*)d->q, (const uint16_t*)d->k_cache, d->page_table, d->seq_lens, valid,
-        d->out, (uint16_t*)d->out_lowp, po, pml, d->num_q, d->n_q_heads, R, d->max_pages, chunk,
-        max_splits, rblks, (int)total, scale_log2);
-    return check_launch("attn_mla_bf16");
+        d->out, (uint16_t*)d->out_lowp, po, pml, flags, d->num_q, d->n_q_heads, R, d->max_pages,
+        chunk, max_splits, rblks, (int)total, scale * 1.4426950408889634f);
+    int rc = check_launch("attn_mla_bf16");
+    if (rc != SD_OK) return rc;
+    attn_mla_exact<<<dim3((unsigned)(total * 4)), 256, 0, s>>>(
+        (const uint16_t*)d->q, (const uint16_t*)d->k_cache, d->page_table, d->seq_lens, valid,
+        flags, d->out, (uint16_t*)d->out_lowp, po, pml, d->num_q, d->n_q_heads, R, d->max_pages,
+        chunk, max_splits, rblks, scale);
+    return check_launch("attn_mla_exact");
+}
+
+// Workspace ints for the per-unit flags.
+size_t mla_flag_count(int batch, int num_q, int n_q_heads, int max_splits) {
+    const int R = num_q * n_q_heads;
+    return (size_t)batch * max_splits * ((R + kRowsPerBlock - 1) / kRowsPerBlock) * 4;
 }
 
 }  // namespace sdv

@@ -24,8 +24,9 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, floa
 
 // MLA verify attention (attn_mla.hip).
 int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits);
-int mla_launch(const sd_attn_desc* d, const int32_t* valid, float* po, float2* pml, int chunk,
-               int max_splits, float scale_log2, hipStream_t s);
+int mla_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* flags, float* po,
+               float2* pml, int chunk, int max_splits, float scale, hipStream_t s);
+size_t mla_flag_count(int batch, int num_q, int n_q_heads, int max_splits);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

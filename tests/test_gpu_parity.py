@@ -444,3 +444,32 @@ def test_attention_mla_full_config_sampled():
     o = out.cpu().numpy()
     got = np.stack([o[b, i, h] for b, i, h in sel])
     check_attention(got, ref, where="mla full config")
+
+
+@pytest.mark.parametrize("L,key_pos", [(300, 200), (3000, 1000)])
+def test_attention_mla_exact_path(L, key_pos):
+    """A latent row whose score for head 0 is ~67 (log2 units) above every
+    other key, placed past the first tile of its chunk: the fast kernel leaves
+    those rows to the exact path, which must still match the oracle (one chunk
+    and several chunks)."""
+    B, K, Hq = 1, 3, 32
+    wl = _mla_case(B, K, Hq, [L], seed=91)
+    t = wl.tensors
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal(576)
+    u /= np.linalg.norm(u)
+    q = t["q"].float()
+    q[0, :, 0, :] = torch.from_numpy(8.0 * u).float()
+    t["q"] = q.to(torch.bfloat16)
+    pg = int(wl.page_table[0, key_pos // 64])
+    lat = t["k_cache"].float()
+    lat[pg, key_pos % 64, :] = torch.from_numpy(140.0 * u).float()
+    t["k_cache"] = lat.to(torch.bfloat16)
+    out, lowp, lat_gpu, err = _run_gpu_mla(wl)
+    ref, lat_ref = _oracle_mla(wl)
+    assert err == 0
+    o = out.cpu().numpy()
+    # The dominant key carries the head-0 rows.
+    dom = oracle.bf16_to_f64(bits(t["k_cache"]))[pg, key_pos % 64, :512]
+    assert np.abs(ref[0, :, 0, :] - dom).max() < 1e-3 * np.abs(dom).max()
+    check_attention(o, ref, where=f"mla exact path L={L}")
