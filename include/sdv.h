@@ -211,6 +211,8 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *   out_offsets  int32 [B+1]       exclusive scan of emitted counts
  *   packed_tokens int32 [B*(K+1)]  emitted tokens back to back, then -1
  * Invalid requests (see SD_DERR_TOKEN/NONFINITE/PARAM) emit nothing.
+ * Returns SD_EINVAL for NULL required pointers, batch < 1, K < 0, vocab < 1
+ * or an unknown logits dtype, and SD_EUNSUPPORTED for vocab > 262144.
  * ---------------------------------------------------------------------- */
 typedef struct sd_accept_desc {
     int batch;

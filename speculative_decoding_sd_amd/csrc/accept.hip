@@ -12,9 +12,13 @@
 // emitted too.
 //
 // Kernels (one stream):
-//   accept_rowstats  one block per logits row: argmax (smallest id on ties),
-//                    finiteness, and for sampled rows the max m, the mass
-//                    Z = sum exp((l-m)/T) in fp64 and p_t of the row's draft
+//   accept_rowpart   one block per slice of a logits row (rows x slices
+//                    blocks): the slice's argmax (smallest id on ties),
+//                    finiteness and, for sampled rows, its max and fp64
+//                    mass sum exp((l - max)/T)
+//   accept_rowmerge  one thread per row: merges the slices in order into the
+//                    row max m, argmax, Z = sum exp((l-m)/T) and p_t of the
+//                    row's draft
 //   accept_topp_*    sampled rows with top_p < 1: the nucleus threshold
 //                    lambda (exact: all tokens tied with the last kept logit
 //                    are kept), the kept mass, p_t of the draft
@@ -24,6 +28,8 @@
 // Statistics and running sums that decide integers are fp64 and reduced in a
 // fixed order, so results do not depend on scheduling.
 #include <math.h>
+
+#include <algorithm>
 
 #include "sdv_device.h"
 #include "sdv_internal.h"
@@ -85,40 +91,194 @@ __device__ double block_sum(double x, double* s4) {
     return r;
 }
 
-// exp((x - m) / T) in fp64, with 1/T precomputed once per row.
-__device__ __forceinline__ double tempered(float x, float m, double invT) {
-    return exp(((double)x - (double)m) * invT);
+// exp(y) for y <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989): y = (64k + j) ln2/64 + r with
+// |r| <= ln2/128, exp(y) = 2^k 2^(j/64) e^r.  r comes from a two-part
+// (Cody-Waite) reduction with fused multiply-adds; e^r - 1 is its degree-5
+// Taylor polynomial (truncation below r^6/720 < 4e-17).  tab[j] = 2^(j/64)
+// from exp2 (see exp_table_init).  About 12 fp64 operations against ~40 for a
+// general exp; accuracy within about 2 ulp.
+constexpr double kExpInvL = 0x1.71547652b82fep+6;   // 64 / ln 2
+constexpr double kExpLHi = 0x1.62e42fefa39efp-7;    // ln 2 / 64, leading double
+constexpr double kExpLLo = 0x1.abc9e3b39803fp-62;   // ln 2 / 64 - kExpLHi
+// The two halves of exp_neg, for callers that batch the table reads.
+// y is clamped to -746 first (max ignores NaN), which maps y <= -746, -inf
+// and NaN to 2^-1077 * [1, 2) scaled by ldexp: 0 after rounding.  For
+// -746 < y <= -708 the result is the rounded subnormal.
+struct ExpRed {
+    double p;  // e^r - 1
+    int ni;    // n = 64k + j
+};
+__device__ __forceinline__ ExpRed exp_reduce(double y) {
+    ExpRed q;
+    const double yc = __builtin_fmax(y, -746.0);
+    const double n = __builtin_rint(yc * kExpInvL);
+    double r = __builtin_fma(-n, kExpLHi, yc);
+    r = __builtin_fma(-n, kExpLLo, r);
+    q.p = r * (1.0 + r * (0.5 + r * (1.0 / 6.0 + r * (1.0 / 24.0 + r * (1.0 / 120.0)))));
+    q.ni = (int)n;
+    return q;
+}
+__device__ __forceinline__ double exp_finish(const ExpRed& q, double tj) {
+    return __builtin_amdgcn_ldexp(__builtin_fma(tj, q.p, tj), q.ni >> 6);
+}
+__device__ __forceinline__ double exp_neg(double y, const double* tab) {
+    const ExpRed q = exp_reduce(y);
+    return exp_finish(q, tab[q.ni & 63]);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void accept_rowstats(
-    const T* __restrict__ logits, const int32_t* __restrict__ drafts,
-    const float* __restrict__ temperature, const float* __restrict__ top_p, int has_probs,
-    RowStat* __restrict__ stats, int K, int V, int vec_ok) {
-    __shared__ float s_best[4];
-    __shared__ int s_idx[4];
-    __shared__ double s_sum[4];
-    const int Q = K + 1;
-    const int row = blockIdx.x, b = row / Q, i = row - b * Q;
-    const T* lr = logits + (size_t)row * V;
-    const float Tb = temperature[b];
-    const float tp = top_p ? top_p[b] : 1.f;
-    const bool stoch = Tb > 0.f;
-    int flags = 0;
-    if (isnan(Tb) || Tb < 0.f) flags |= SD_DERR_PARAM;
-    if (stoch && (isnan(tp) || tp <= 0.f || (!has_probs && K > 0))) flags |= SD_DERR_PARAM;
+// LDS table 2^(j/64), j = 0..63, for exp_neg; a block's first 64 threads fill
+// it (the caller synchronises before use).
+__device__ __forceinline__ void exp_table_init(double* tab) {
+    if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
 
+// exp((x - m) / T) in fp64, with 1/T precomputed once per row.
+__device__ __forceinline__ double tempered(float x, float m, double invT, const double* tab) {
+    return exp_neg(((double)x - (double)m) * invT, tab);
+}
+
+// Per-thread accumulator over a slice of one row: the running max (its
+// smallest id), finiteness, and for sampled rows z = sum exp((x - best)/T)
+// over the thread's elements, rescaled whenever best rises.
+struct RowAcc {
     float best = -INFINITY;
     int bidx = 0x7fffffff;
-    int nonfinite = 0, anyfin = 0;
-    for_row(lr, V, vec_ok != 0, [&](float x, int v) {
-        if (x != x || x == INFINITY) nonfinite = 1;
-        if (x > -INFINITY) anyfin = 1;
-        if (x > best || (x == best && v < bidx)) {
-            best = x;
-            bidx = v;
+    bool nonfinite = false, anyfin = false;
+    double z = 0.0;
+};
+
+// Folds N elements into a, in the thread's visit order (ids rise along it).
+// The group max decides everything but the sum: finiteness (a NaN, or a
+// max of +inf), whether a value above -inf was seen, and whether best rises;
+// only then is the group searched for the first id of its max and z
+// rescaled.  Sampled rows then add the group's terms eight at a time (all
+// eight table reads issued before the first is used) as pairwise trees.
+template <bool STOCH, int N>
+__device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const int (&v)[N],
+                                         double invT, const double* tab) {
+    float gm = x[0];
+    bool nan = x[0] != x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) {
+        gm = fmaxf(gm, x[e]);
+        nan |= x[e] != x[e];
+    }
+    a.nonfinite |= nan | (gm == INFINITY);
+    a.anyfin |= gm > -INFINITY;
+    if (gm > a.best) {
+        int id = v[N - 1];
+#pragma unroll
+        for (int e = N - 1; e >= 0; --e) id = x[e] == gm ? v[e] : id;
+        if constexpr (STOCH) a.z *= exp_neg(((double)a.best - (double)gm) * invT, tab);
+        a.best = gm;
+        a.bidx = id;
+    }
+    if constexpr (STOCH) {
+        constexpr int G = N < 8 ? N : 8;
+        const double mtd = (double)a.best;
+        double acc = 0.0;
+#pragma unroll
+        for (int g = 0; g < N; g += G) {
+            ExpRed q[G];
+            double tj[G], w[G];
+#pragma unroll
+            for (int e = 0; e < G; ++e) q[e] = exp_reduce(((double)x[g + e] - mtd) * invT);
+#pragma unroll
+            for (int e = 0; e < G; ++e) tj[e] = tab[q[e].ni & 63];
+#pragma unroll
+            for (int e = 0; e < G; ++e) w[e] = exp_finish(q[e], tj[e]);
+#pragma unroll
+            for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+                for (int e = 0; e + h < G; e += 2 * h) w[e] += w[e + h];
+            acc += w[0];
         }
-    });
+        a.z += acc;
+    }
+}
+
+// One pass over ids [v_lo, v_hi) of a row (v_lo a multiple of the vector
+// width when vec_ok); U vectors in flight per thread.
+template <typename T, bool STOCH>
+__device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool vec_ok, RowAcc& a,
+                                         double invT, const double* tab) {
+    constexpr int E = Logit<T>::kPerVec;
+    constexpr int U = 4;
+    int v0 = v_lo;
+    if (vec_ok) {
+        const int c_lo = v_lo / E, c_hi = v_hi / E;
+        int c = c_lo + (int)threadIdx.x;
+        for (; c + (U - 1) * 256 < c_hi; c += U * 256) {
+            u32x4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = *(const u32x4*)(lr + (size_t)(c + u * 256) * E);
+            float x[U * E];
+            int v[U * E];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    x[u * E + e] = Logit<T>::lane(w[u], e);
+                    v[u * E + e] = (c + u * 256) * E + e;
+                }
+            row_fold<STOCH>(a, x, v, invT, tab);
+        }
+        for (; c < c_hi; c += 256) {
+            const u32x4 w = *(const u32x4*)(lr + (size_t)c * E);
+            float x[E];
+            int v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                x[e] = Logit<T>::lane(w, e);
+                v[e] = c * E + e;
+            }
+            row_fold<STOCH>(a, x, v, invT, tab);
+        }
+        v0 = c_hi * E;
+    }
+    for (int vv = v0 + (int)threadIdx.x; vv < v_hi; vv += 256) {
+        const float x[1] = {Logit<T>::at(lr, vv)};
+        const int v[1] = {vv};
+        row_fold<STOCH>(a, x, v, invT, tab);
+    }
+}
+
+// Statistics of one slice of a row, merged over slices by accept_rowmerge.
+struct RowPart {
+    float best;   // slice max (-inf if none finite)
+    int bidx;     // its smallest id
+    int bits;     // 1: a NaN or +inf seen; 2: a value above -inf seen
+    int pad;
+    double z;     // sum over the slice of exp((x - best)/T) (sampled rows)
+};
+
+// Grid: rows x splits blocks of 256 threads; block (row, s) covers ids
+// [s*span, min(V, (s+1)*span)) of its row.
+template <typename T>
+__global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logits,
+                                                      const float* __restrict__ temperature,
+                                                      RowPart* __restrict__ parts, int Q, int V,
+                                                      int splits, int span, int vec_ok) {
+    __shared__ double s_exptab[64];
+    __shared__ float s_best[4];
+    __shared__ int s_idx[4];
+    __shared__ double s_z[4];
+    exp_table_init(s_exptab);
+    __syncthreads();
+    const int row = blockIdx.x / splits, sp = blockIdx.x - row * splits;
+    const int b = row / Q;
+    const T* lr = logits + (size_t)row * V;
+    const int v_lo = sp * span, v_hi = min(V, v_lo + span);
+    const float Tb = temperature[b];
+    const bool stoch = Tb > 0.f;
+    const double invT = stoch ? 1.0 / (double)Tb : 0.0;
+    RowAcc a;
+    if (stoch) row_pass<T, true>(lr, v_lo, v_hi, vec_ok != 0, a, invT, s_exptab);
+    else row_pass<T, false>(lr, v_lo, v_hi, vec_ok != 0, a, invT, s_exptab);
+    float best = a.best;
+    int bidx = a.bidx;
 #pragma unroll
     for (int msk = 32; msk >= 1; msk >>= 1) {
         const float ob = shfl_xor(best, msk);
@@ -133,8 +293,8 @@ __global__ __launch_bounds__(256) void accept_rowstats(
         s_best[wave] = best;
         s_idx[wave] = bidx;
     }
-    nonfinite = __syncthreads_or(nonfinite);
-    anyfin = __syncthreads_or(anyfin);
+    const int nonfinite = __syncthreads_or(a.nonfinite);
+    const int anyfin = __syncthreads_or(a.anyfin);
     best = s_best[0];
     bidx = s_idx[0];
     for (int w = 1; w < 4; ++w)
@@ -142,28 +302,79 @@ __global__ __launch_bounds__(256) void accept_rowstats(
             best = s_best[w];
             bidx = s_idx[w];
         }
-    if (nonfinite || !anyfin) flags |= SD_DERR_NONFINITE;
-
-    double z = 0.0, pt_d = 0.0;
-    if (stoch && !flags) {
-        double part = 0.0;
-        const float m = best;
-        const double invT = 1.0 / (double)Tb;
-        for_row(lr, V, vec_ok != 0, [&](float x, int) { part += tempered(x, m, invT); });
-        z = block_sum(part, s_sum);
-        const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
-        if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), m, invT) / z;
+    double z = 0.0;
+    if (stoch && !nonfinite && best > -INFINITY) {
+        // The threads' (best, z) pairs rescaled to the slice max, summed by a
+        // fixed-order wave butterfly, then over the waves in order.
+        double zt = a.z * exp_neg(((double)a.best - (double)best) * invT, s_exptab);
+        zt = wave_sum(zt);
+        if (lane == 0) s_z[wave] = zt;
+        __syncthreads();
+        z = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
     }
     if (threadIdx.x == 0) {
-        RowStat st;
-        st.m = best;
-        st.lambda = -INFINITY;
-        st.argmax = bidx;
-        st.flags = flags;
-        st.zkeep = z;
-        st.pt_d = pt_d;
-        stats[row] = st;
+        RowPart p;
+        p.best = best;
+        p.bidx = bidx;
+        p.bits = (nonfinite ? 1 : 0) | (anyfin ? 2 : 0);
+        p.pad = 0;
+        p.z = z;
+        parts[blockIdx.x] = p;
     }
+}
+
+// One thread per row: merges the row's slices in order (max, smallest id on
+// ties, Z = sum_s z_s exp((best_s - m)/T)), checks the request's parameters
+// and, for sampled rows that judge a draft, p_t of that draft.
+template <typename T>
+__global__ __launch_bounds__(256) void accept_rowmerge(
+    const T* __restrict__ logits, const int32_t* __restrict__ drafts,
+    const float* __restrict__ temperature, const float* __restrict__ top_p, int has_probs,
+    const RowPart* __restrict__ parts, RowStat* __restrict__ stats, int rows, int K, int V,
+    int splits) {
+    __shared__ double s_exptab[64];
+    exp_table_init(s_exptab);
+    __syncthreads();
+    const int row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const int Q = K + 1, b = row / Q, i = row - b * Q;
+    const float Tb = temperature[b];
+    const float tp = top_p ? top_p[b] : 1.f;
+    const bool stoch = Tb > 0.f;
+    int flags = 0;
+    if (isnan(Tb) || Tb < 0.f) flags |= SD_DERR_PARAM;
+    if (stoch && (isnan(tp) || tp <= 0.f || (!has_probs && K > 0))) flags |= SD_DERR_PARAM;
+    const RowPart* pr = parts + (size_t)row * splits;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff, bits = 0;
+    for (int s = 0; s < splits; ++s) {
+        const RowPart p = pr[s];
+        bits |= p.bits;
+        if (p.best > best) {
+            best = p.best;
+            bidx = p.bidx;
+        }
+    }
+    if ((bits & 1) || !(bits & 2)) flags |= SD_DERR_NONFINITE;
+    double z = 0.0, pt_d = 0.0;
+    if (stoch && !flags) {
+        const double invT = 1.0 / (double)Tb;
+        for (int s = 0; s < splits; ++s) {
+            const RowPart p = pr[s];
+            z += p.z * exp_neg(((double)p.best - (double)best) * invT, s_exptab);
+        }
+        const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
+        const T* lr = logits + (size_t)row * V;
+        if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), best, invT, s_exptab) / z;
+    }
+    RowStat st;
+    st.m = best;
+    st.lambda = -INFINITY;
+    st.argmax = bidx;
+    st.flags = flags;
+    st.zkeep = z;
+    st.pt_d = pt_d;
+    stats[row] = st;
 }
 
 // ---------------------------------------------------------------------------
@@ -179,6 +390,9 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ top_p,
     RowStat* __restrict__ stats, int K, int V, int vec_ok) {
+    __shared__ double s_exptab[64];
+    exp_table_init(s_exptab);
+    __syncthreads();
     extern __shared__ __attribute__((aligned(16))) uint32_t s_hist[];  // kWin
     __shared__ double s_part[257];
     __shared__ int s_found, s_lkey;
@@ -213,7 +427,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
             const int idx = tid * nl + j;
             const uint32_t c = s_hist[idx];
             if (c && top - idx >= bottom)
-                part += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT);
+                part += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT, s_exptab);
         }
         s_part[tid] = part;
         __syncthreads();
@@ -237,7 +451,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
                 const int idx = tid * nl + j;
                 const uint32_t c = s_hist[idx];
                 if (!c || top - idx < bottom) continue;
-                run += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT);
+                run += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT, s_exptab);
                 last = top - idx;
                 at_last = run;
                 if (run >= target) break;
@@ -264,7 +478,7 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
         out.pt_d = 0.0;
         if (d >= 0 && d < V) {
             const float xd = bf16_to_f32(lr[d]);
-            if (xd >= out.lambda) out.pt_d = tempered(xd, m, invT) / out.zkeep;
+            if (xd >= out.lambda) out.pt_d = tempered(xd, m, invT, s_exptab) / out.zkeep;
         }
         stats[row] = out;
     }
@@ -277,6 +491,9 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
     const float* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ top_p,
     RowStat* __restrict__ stats, int K, int V, int vec_ok) {
+    __shared__ double s_exptab[64];
+    exp_table_init(s_exptab);
+    __syncthreads();
     __shared__ double s_sum[4];
     const int Q = K + 1;
     const int row = blockIdx.x, b = row / Q, i = row - b * Q;
@@ -295,7 +512,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
         const uint64_t mid = (lo + hi) / 2;
         double part = 0.0;
         for_row(lr, V, vec_ok != 0, [&](float x, int) {
-            if (f32_key(__float_as_uint(x)) >= mid) part += tempered(x, m, invT);
+            if (f32_key(__float_as_uint(x)) >= mid) part += tempered(x, m, invT, s_exptab);
         });
         const double mass = block_sum(part, s_sum);
         if (mass >= target) {
@@ -311,7 +528,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
         out.zkeep = mass_lo;
         const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
         out.pt_d = 0.0;
-        if (d >= 0 && d < V && lr[d] >= out.lambda) out.pt_d = tempered(lr[d], m, invT) / out.zkeep;
+        if (d >= 0 && d < V && lr[d] >= out.lambda) out.pt_d = tempered(lr[d], m, invT, s_exptab) / out.zkeep;
         stats[row] = out;
     }
 }
@@ -322,24 +539,64 @@ enum { kModeInvalid = 0, kModeDone = 1, kModeResidual = 2, kModeTarget = 3 };
 // Per-request decision and final-token draw.  One block of 1024 threads (16
 // waves) per request.  Thread 0 takes the sequential accept decision from the
 // row statistics.  A sampled final token is an inverse-CDF draw in token-id
-// order: wave w owns a contiguous run of ids, read 64 at a time (one id per
-// lane, coalesced); each 64-id chunk's fp64 weight sum is reduced in a fixed
-// lane order and kept in LDS.  A fixed-order scan over waves, then over the
-// crossing wave's chunks, finds the chunk whose running sum first exceeds
-// u * total; a lane-order prefix scan inside that chunk picks the token.
+// order: wave w owns a contiguous run of ids, read 512 at a time (8 per lane,
+// one 16-byte load of bf16 logits); each 512-id chunk's fp64 weight sum is
+// reduced in a fixed lane order and kept in LDS.  A fixed-order scan over
+// waves, then over the crossing wave's chunks, finds the chunk whose running
+// sum first exceeds u * total; a lane-order prefix scan inside that chunk
+// finds the lane, whose 8 ids are then walked in order.
 // ---------------------------------------------------------------------------
 constexpr int kDecThreads = 1024;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecMaxChunks = 160;  // per wave: V <= 16 * 160 * 64 = 163840
+constexpr int kDecChunk = 512;      // tokens per chunk: 8 per lane
+constexpr int kDecMaxChunks = 32;   // per wave: V <= 16 * 32 * 512 = 262144
 
+// Draw weights of the 8 consecutive tokens v0 .. v0+7 (0 past the row end),
+// with 16-byte loads when the rows are aligned.
 template <typename T>
-__device__ __forceinline__ double draw_weight(const T* lr, const float* pd, int v, bool resid,
-                                             float lambda, float m, double invT, double invZ) {
-    const float x = Logit<T>::at(lr, v);
-    const double p = (x >= lambda) ? tempered(x, m, invT) * invZ : 0.0;
-    if (!resid) return p;
-    const double r = p - (double)pd[v];
-    return r > 0.0 ? r : 0.0;
+__device__ __forceinline__ void weights8(const T* lr, const float* pd, int v0, int V, bool vec_ok,
+                                         bool resid, float lambda, float m, double invT,
+                                         double invZ, const double* tab, double (&w)[8]) {
+    float x[8], q[8];
+    if (vec_ok && v0 + 8 <= V) {
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 lw = *(const u32x4*)(lr + v0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = Logit<T>::lane(lw, e);
+        } else {
+            const u32x4 l0 = *(const u32x4*)(lr + v0), l1 = *(const u32x4*)(lr + v0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = Logit<T>::lane(l0, e);
+                x[e + 4] = Logit<T>::lane(l1, e);
+            }
+        }
+        if (resid) {
+            const f32x4 q0 = *(const f32x4*)(pd + v0), q1 = *(const f32x4*)(pd + v0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                q[e] = q0[e];
+                q[e + 4] = q1[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int v = v0 + e;
+            x[e] = v < V ? Logit<T>::at(lr, v) : -INFINITY;
+            q[e] = (resid && v < V) ? pd[v] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double p = (x[e] >= lambda) ? tempered(x[e], m, invT, tab) * invZ : 0.0;
+        if (!resid) {
+            w[e] = p;
+        } else {
+            const double r = p - (double)q[e];
+            w[e] = r > 0.0 ? r : 0.0;
+        }
+    }
 }
 
 template <typename T>
@@ -350,7 +607,10 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
     const RowStat* __restrict__ stats, int32_t* __restrict__ num_accepted,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_token, int32_t* err, int K,
     int V) {
-    __shared__ int s_mode, s_j, s_row, s_f, s_wave, s_chunk;
+    __shared__ double s_exptab[64];
+    exp_table_init(s_exptab);
+    __syncthreads();
+    __shared__ int s_mode, s_j, s_row, s_f, s_chunk;
     __shared__ double s_u, s_pre, s_total;
     __shared__ double s_wsum[kDecWaves];
     __shared__ double s_chunk_sum[kDecWaves * kDecMaxChunks];
@@ -413,18 +673,40 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         const float* pd = draft_probs ? draft_probs + ((size_t)b * K + row) * V : nullptr;
         const double invT = 1.0 / (double)temperature[b];
         const double invZ = 1.0 / st.zkeep;
-        const int nchunks = (V + 63) / 64;
+        const int nchunks = (V + kDecChunk - 1) / kDecChunk;
         const int cpw = (nchunks + kDecWaves - 1) / kDecWaves;  // chunks per wave
         const int c_begin = wave * cpw, c_end = min(nchunks, c_begin + cpw);
+        const bool vec_ok = (V % 8) == 0 && ((uintptr_t)lr & 15) == 0 &&
+                            (pd == nullptr || ((uintptr_t)pd & 15) == 0);
         bool resid = mode == kModeResidual;
+        auto lane_sum = [&](int c, double (&w)[8]) {
+            weights8(lr, pd, c * kDecChunk + 8 * lane, V, vec_ok, resid, st.lambda, st.m, invT,
+                     invZ, s_exptab, w);
+            double t = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t += w[e];
+            return t;
+        };
         for (int pass = 0; pass < 2; ++pass) {
             double wsum = 0.0;
-            for (int c = c_begin; c < c_end; ++c) {
-                const int v = c * 64 + lane;
-                double w = v < V ? draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) : 0.0;
-                w = wave_sum(w);
-                if (lane == 0) s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = w;
-                wsum += w;
+            int c = c_begin;
+            for (; c + 1 < c_end; c += 2) {  // two chunks in flight per wave
+                double w0[8], w1[8];
+                double t0 = lane_sum(c, w0), t1 = lane_sum(c + 1, w1);
+                t0 = wave_sum(t0);
+                t1 = wave_sum(t1);
+                if (lane == 0) {
+                    s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = t0;
+                    s_chunk_sum[wave * kDecMaxChunks + (c + 1 - c_begin)] = t1;
+                }
+                wsum += t0;
+                wsum += t1;
+            }
+            for (; c < c_end; ++c) {
+                double w0[8];
+                const double t0 = wave_sum(lane_sum(c, w0));
+                if (lane == 0) s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = t0;
+                wsum += t0;
             }
             if (lane == 0) s_wsum[wave] = wsum;
             __syncthreads();
@@ -442,42 +724,64 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
             // Locate the first chunk whose running sum exceeds u * total.
             const double target = s_u * s_total;
             double run = 0.0;
-            int fw = -1, fc = -1;
-            for (int w = 0; w < kDecWaves && fw < 0; ++w) {
+            int fc = -1;
+            for (int w = 0; w < kDecWaves && fc < 0; ++w) {
                 if (run + s_wsum[w] > target) {
                     const int cb = w * cpw, ce = min(nchunks, cb + cpw);
                     for (int c = cb; c < ce; ++c) {
                         const double cs = s_chunk_sum[w * kDecMaxChunks + (c - cb)];
                         if (run + cs > target) {
-                            fw = w;
                             fc = c;
                             break;
                         }
                         run += cs;
                     }
-                    if (fw < 0) fw = -2;  // rounding: fall back below
+                    if (fc < 0) break;  // rounding: fall back below
                 } else {
                     run += s_wsum[w];
                 }
             }
-            s_wave = fw;
             s_chunk = fc;
             s_pre = run;
         }
         __syncthreads();
         if (s_chunk >= 0 && wave == 0) {
-            const int v = s_chunk * 64 + lane;
-            const double w = v < V ? draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) : 0.0;
-            double incl = w;  // lane-order inclusive scan
+            // Inside the chunk: lane-order inclusive scan of the lanes' sums,
+            // then the crossing lane walks its 8 tokens in order.  If rounding
+            // leaves the target beyond the chunk, take its last positive token.
+            const int c = s_chunk;
+            double w[8];
+            const double t = lane_sum(c, w);
+            double incl = t;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const double y = __shfl_up(incl, o, 64);
                 if (lane >= o) incl += y;
             }
             const double target = s_u * s_total;
-            const bool hit = v < V && s_pre + incl > target;
-            const unsigned long long mask = __ballot(hit);
-            if (lane == 0) s_f = mask ? s_chunk * 64 + __ffsll((long long)mask) - 1 : -1;
+            const unsigned long long mask = __ballot(s_pre + incl > target);
+            if (mask) {
+                const int hl = __ffsll((long long)mask) - 1;
+                if (lane == hl) {
+                    double run = s_pre + incl - t;
+                    int pick = -1, lastpos = -1;
+                    for (int e = 0; e < 8; ++e) {
+                        if (w[e] > 0.0) lastpos = e;
+                        run += w[e];
+                        if (run > target && pick < 0) pick = e;
+                    }
+                    if (pick < 0) pick = lastpos;
+                    s_f = c * kDecChunk + 8 * lane + pick;
+                }
+            } else {
+                int lp = -1;
+                for (int e = 0; e < 8; ++e)
+                    if (w[e] > 0.0) lp = e;
+                const unsigned long long pm = __ballot(lp >= 0);
+                const int top = pm ? 63 - __clzll((long long)pm) : -1;
+                if (lane == 0) s_f = -1;
+                if (top >= 0 && lane == top) s_f = c * kDecChunk + 8 * lane + lp;
+            }
         }
         __syncthreads();
         if (s_chunk < 0 || s_f < 0) {
@@ -485,10 +789,17 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
             // positive weight.
             int cand = -1;
             for (int c = c_end - 1; c >= c_begin && cand < 0; --c) {
-                const int v = c * 64 + lane;
-                const bool pos = v < V && draw_weight(lr, pd, v, resid, st.lambda, st.m, invT, invZ) > 0.0;
-                const unsigned long long mask = __ballot(pos);
-                if (mask) cand = c * 64 + 63 - __clzll((long long)mask);
+                double w[8];
+                lane_sum(c, w);
+                int lp = -1;
+                for (int e = 0; e < 8; ++e)
+                    if (w[e] > 0.0) lp = e;
+                const unsigned long long pm = __ballot(lp >= 0);
+                if (pm) {
+                    const int top = 63 - __clzll((long long)pm);
+                    const int lpt = __shfl(lp, top, 64);
+                    cand = c * kDecChunk + 8 * top + lpt;
+                }
             }
             if (lane == 0) s_cand[wave] = cand;
             __syncthreads();
@@ -561,8 +872,25 @@ __global__ __launch_bounds__(1024) void accept_pack(const int32_t* __restrict__ 
     for (int k = total + tid; k < B * Q; k += blockDim.x) packed[k] = -1;
 }
 
+// Slices per row for the row statistics: enough blocks to fill the chip
+// (about 2048 of 256 threads), slices of at least 2048 ids, at most 32.
+// span is a multiple of 8 ids so every slice starts on a 16-byte vector.
+void row_split(int rows, int V, int* splits, int* span) {
+    int sp = (2048 + rows - 1) / rows;
+    sp = std::min(sp, std::max(1, V / 2048));
+    sp = std::max(1, std::min(sp, 32));
+    int sn = (V + sp - 1) / sp;
+    sn = (sn + 7) & ~7;
+    *span = sn;
+    *splits = (V + sn - 1) / sn;
+}
+
 size_t accept_ws_bytes(const sd_accept_desc* d) {
-    return align_up(sizeof(RowStat) * (size_t)d->batch * (d->K + 1), 256);
+    const int rows = d->batch * (d->K + 1);
+    int splits, span;
+    row_split(rows, d->vocab, &splits, &span);
+    return align_up(sizeof(RowStat) * (size_t)rows, 256) +
+           align_up(sizeof(RowPart) * (size_t)rows * splits, 256);
 }
 
 int check_accept(const sd_accept_desc* d) {
@@ -573,8 +901,9 @@ int check_accept(const sd_accept_desc* d) {
         return fail(SD_EINVAL, "sd_accept: unknown logits dtype %d", d->logits_dtype);
     if ((long)d->batch * (d->K + 1) > 0x7fffffffL)
         return fail(SD_EUNSUPPORTED, "sd_accept: too many rows");
-    if ((long)d->vocab > (long)kDecWaves * kDecMaxChunks * 64)
-        return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d", kDecWaves * kDecMaxChunks * 64);
+    if ((long)d->vocab > (long)kDecWaves * kDecMaxChunks * kDecChunk)
+        return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d",
+                    kDecWaves * kDecMaxChunks * kDecChunk);
     return SD_OK;
 }
 
@@ -605,17 +934,24 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
     const size_t need = accept_ws_bytes(d);
     if (ws_bytes < need) return fail(SD_EWORKSPACE, "sd_accept: workspace %zu < %zu", ws_bytes, need);
     hipStream_t s = (hipStream_t)stream;
-    RowStat* stats = (RowStat*)workspace;
     const int B = d->batch, K = d->K, V = d->vocab, Q = K + 1;
     const int rows = B * Q;
+    int splits, span;
+    row_split(rows, V, &splits, &span);
+    RowStat* stats = (RowStat*)workspace;
+    RowPart* parts = (RowPart*)((char*)workspace + align_up(sizeof(RowStat) * (size_t)rows, 256));
     const int es = d->logits_dtype == SD_BF16 ? 2 : 4;
     const int vec_ok = aligned16(d->logits) && ((size_t)V * es) % 16 == 0;
     const int has_probs = d->draft_probs != nullptr;
     if (d->logits_dtype == SD_BF16) {
         const uint16_t* lg = (const uint16_t*)d->logits;
-        accept_rowstats<uint16_t><<<rows, 256, 0, s>>>(lg, d->draft_tokens, d->temperature,
-                                                       d->top_p, has_probs, stats, K, V, vec_ok);
-        if ((rc = check_launch("accept_rowstats")) != SD_OK) return rc;
+        accept_rowpart<uint16_t><<<rows * splits, 256, 0, s>>>(lg, d->temperature, parts, Q, V,
+                                                               splits, span, vec_ok);
+        if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
+        accept_rowmerge<uint16_t><<<(rows + 255) / 256, 256, 0, s>>>(
+            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, parts, stats, rows, K, V,
+            splits);
+        if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;
         if (d->top_p) {
             accept_topp_bf16<<<rows, 256, kWin * sizeof(uint32_t), s>>>(
                 lg, d->draft_tokens, d->temperature, d->top_p, stats, K, V, vec_ok);
@@ -627,9 +963,13 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
                                                   d->dev_error, K, V);
     } else {
         const float* lg = (const float*)d->logits;
-        accept_rowstats<float><<<rows, 256, 0, s>>>(lg, d->draft_tokens, d->temperature,
-                                                    d->top_p, has_probs, stats, K, V, vec_ok);
-        if ((rc = check_launch("accept_rowstats")) != SD_OK) return rc;
+        accept_rowpart<float><<<rows * splits, 256, 0, s>>>(lg, d->temperature, parts, Q, V, splits,
+                                                            span, vec_ok);
+        if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
+        accept_rowmerge<float><<<(rows + 255) / 256, 256, 0, s>>>(
+            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, parts, stats, rows, K, V,
+            splits);
+        if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;
         if (d->top_p) {
             accept_topp_f32<<<rows, 256, 0, s>>>(lg, d->draft_tokens, d->temperature, d->top_p,
                                                  stats, K, V, vec_ok);

@@ -114,6 +114,12 @@ def test_accept_and_rollback_host_validation():
     with pytest.raises(sdv.SdvError) as e:
         sdv.sd_accept(d, 4096, n - 256, 0)
     assert e.value.code == sdv.SD_EWORKSPACE
+    d.vocab = 262145                            # one id above the largest supported vocab
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_accept_workspace_size(d)
+    assert e.value.code == sdv.SD_EUNSUPPORTED
+    d.vocab = 262144
+    assert sdv.sd_accept_workspace_size(d) % 256 == 0
     d.logits_dtype = 7
     with pytest.raises(sdv.SdvError) as e:
         sdv.sd_accept_workspace_size(d)

@@ -209,6 +209,7 @@ def test_accept_greedy(B, K, V, dtype):
     (48, 4, 2500, 0.8, 0.5, "bf16"),
     (24, 3, 777, 1.3, 0.9, "f32"),
     (16, 0, 1000, 0.9, 0.8, "bf16"),
+    (3, 2, 262144, 1.0, None, "bf16"),      # the largest supported vocab
 ])
 def test_accept_stochastic(B, K, V, T, top_p, dtype):
     seed = 100 + B + K
