@@ -117,9 +117,15 @@ __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restric
 // (BK = 32: four, refilled up to three stages ahead; BK = 64: two).  With
 // BK = 64 every DMA request covers whole 128-byte rows of W and H (full L2
 // lines); with BK = 32 each request is half a line.
+// WN x WM waves each own a (TN/WN) x (TM/WM) sub-tile.  The 256 x 256 tile
+// runs 8 waves of 128 x 64 (two per SIMD, accumulators in 128 registers):
+// a wave stalled on an LDS read or a barrier leaves the matrix unit to the
+// other wave of its SIMD, which outweighs the half more fragment reads.
 // LDS layout per stage: row r (W rows then H rows) holds BK/8 granules of 16
-// bytes; granule c sits at slot c ^ f(r) (f(r) = (r/4)%4 for BK = 32, r%8 for
-// BK = 64), so the rows of one ds_read_b128 phase hit distinct bank groups.
+// bytes; granule c sits at slot c ^ f(r) (f(r) = (r/4)%4 for BK = 32,
+// (r/2)%8 for BK = 64).  A ds_read_b128 is served 16 lanes (16 rows, one
+// logical granule) per pass over the 64 banks; with f those 16 rows land in 16
+// distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
 constexpr int kLmBK = 64;       // k per LDS stage of the DMA GEMM
 constexpr int kStageRows = 512;  // largest TN + TM
@@ -128,15 +134,17 @@ __shared__ __attribute__((aligned(1024))) uint16_t g_lds[kLdsElems];
 
 template <int TN, int TM, int WN, int WM, int BK>
 struct LmTile {
+    static constexpr int NW = WN * WM;                         // waves per workgroup
+    static constexpr int NT = 64 * NW;                         // threads per workgroup
     static constexpr int kRows = TN + TM;
     static constexpr int kGran = BK / 8;                       // 16-byte granules per row
     static constexpr int kStages = BK == 32 ? 4 : 2;
     static constexpr int kSteps = BK / 16;                     // MFMA k-steps per stage
     static constexpr int kStageElems = kStageRows * BK;
-    static constexpr int kDmaPerWave = kRows * kGran / 64 / 4; // 1 KiB DMA ops per wave
+    static constexpr int kDmaPerWave = kRows * kGran / NT;     // 1 KiB DMA ops per wave
     static constexpr int FN = TN / WN / 32;                    // 32-row MFMA blocks (vocab)
     static constexpr int FM = TM / WM / 32;                    // 32-col MFMA blocks (rows)
-    static_assert(kRows * kGran % 256 == 0, "stage must split into whole wave DMAs");
+    static_assert(kRows * kGran % NT == 0, "stage must split into whole wave DMAs");
     static_assert(kRows <= kStageRows, "stage buffer too small");
     static_assert(kStages * kStageElems <= kLdsElems, "stages exceed the LDS buffer");
     static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
@@ -145,7 +153,7 @@ struct LmTile {
 template <int BK>
 __device__ __forceinline__ int swz(int row, int c) {
     if constexpr (BK == 32) return row * 4 + (c ^ ((row >> 2) & 3));
-    else return row * 8 + (c ^ (row & 7));
+    else return row * 8 + (c ^ ((row >> 1) & 7));
 }
 
 // s_waitcnt vmcnt(n) (expcnt and lgkmcnt left free), gfx9 encoding.
@@ -161,7 +169,7 @@ __device__ __forceinline__ void block_barrier_lds() {
 }
 
 // Per-lane DMA sources for k = 0: op i of a stage covers LDS granules
-// g = 64 (4i + wave) + lane, i.e. row g / kGran (W rows, then H rows),
+// g = 64 (NW i + wave) + lane, i.e. row g / kGran (W rows, then H rows),
 // logical granule c with swz(row, c) = g.  Rows past the matrix ends re-read
 // the last row (their results are never stored).
 template <int TN, int TM, int WN, int WM, int BK>
@@ -172,10 +180,10 @@ __device__ __forceinline__ void lm_dma_bases(const uint16_t* __restrict__ W,
     using T = LmTile<TN, TM, WN, WM, BK>;
 #pragma unroll
     for (int i = 0; i < T::kDmaPerWave; ++i) {
-        const int g = (i * 4 + wave) * 64 + lane;
+        const int g = (i * T::NW + wave) * 64 + lane;
         const int row = g / T::kGran;
         const int slot = g % T::kGran;
-        const int c = BK == 32 ? (slot ^ ((row >> 2) & 3)) : (slot ^ (row & 7));
+        const int c = BK == 32 ? (slot ^ ((row >> 2) & 3)) : (slot ^ ((row >> 1) & 7));
         if (row < TN)
             src[i] = W + (size_t)min(n0 + row, N - 1) * K + 8 * c;
         else
@@ -188,7 +196,7 @@ template <int TN, int TM, int WN, int WM, int BK, int S>
 __device__ __forceinline__ void lm_dma(const uint16_t* const* src, int i, int kt, int wave) {
     using T = LmTile<TN, TM, WN, WM, BK>;
     uint16_t* buf = g_lds + S * T::kStageElems;
-    const int g0 = (i * 4 + wave) * 64;
+    const int g0 = (i * T::NW + wave) * 64;
     __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * BK,
                                      (__attribute__((address_space(3))) void*)(buf + g0 * 8), 16, 0,
                                      0);
@@ -335,7 +343,7 @@ __device__ __forceinline__ void lm_steps(const uint16_t* const* src,
 }
 
 template <int TN, int TM, int WN, int WM, int BK>
-__global__ __launch_bounds__(256, 1) void lm_head_dma(const uint16_t* __restrict__ H,
+__global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_dma(const uint16_t* __restrict__ H,
                                                       const uint16_t* __restrict__ W,
                                                       uint16_t* __restrict__ C, int M, int N,
                                                       int K) {
@@ -465,7 +473,7 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         const uint16_t* w = (const uint16_t*)W;
         uint16_t* c = (uint16_t*)logits;
         if (TM == 256)
-            lm_head_dma<256, 256, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+            lm_head_dma<256, 256, 2, 4, kLmBK><<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab,
                                                                                hidden);
         else if (TM == 128)
             lm_head_dma<256, 128, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
