@@ -105,19 +105,24 @@ constexpr int kCombineRows = 64;
 constexpr int kCombineDims = 32;
 constexpr int kCombineCache = 12288;  // split weights cached per block (48 KiB)
 
-// grid (kv head, request, row block x 32-dim block).  With `direct_single`,
-// requests whose keys fit one chunk were written by the attention kernel
-// already.  Each block weighs its rows' chunk partials once (weights cached in
-// LDS when ns * rows fits), then reads the partial planes [d][R] with
+// grid (kv head, request, row block x 32-dim block).  mode 1 (MLA): requests
+// whose keys fit one chunk were written by the attention kernel already.
+// mode 2 (GQA): the attention kernel marks in row 0 of each slot whether the
+// pair was written directly (slot 0) or a slot is empty (its chunk was merged
+// into an earlier slot of the same wave); only the written slots are merged,
+// in split order.  Each block weighs its rows' partials once (weights cached
+// in LDS when they fit), then reads the partial planes [d][R] with
 // consecutive threads on consecutive rows.
 __global__ __launch_bounds__(256) void attn_combine(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     float* __restrict__ out, uint16_t* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int G,
-    int R, int D, int chunk, int max_splits, int direct_single) {
+    int R, int D, int chunk, int max_splits, int mode) {
     __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
     __shared__ float s_red[4][kCombineRows];
     __shared__ __attribute__((aligned(16))) float s_w[kCombineCache];
+    __shared__ int s_list[kCombineMaxSplits];
+    __shared__ int s_cnt[4], s_np;
     const int kvh = blockIdx.x, b = blockIdx.y;
     const int ndb = D / kCombineDims;
     const int r0 = (blockIdx.z / ndb) * kCombineRows;
@@ -135,15 +140,36 @@ __global__ __launch_bounds__(256) void attn_combine(
         return;
     }
     const int ns = (seq_lens[b] + NQ + chunk - 1) / chunk;
-    if (direct_single && ns == 1) return;
+    if (mode == 1 && ns == 1) return;
     const size_t pbase = ((size_t)b * Hkv + kvh) * max_splits;
-    // Row statistics: four threads per row, each over every fourth split,
+    if (mode == 2 && part_ml[pbase * R].y == kPartDirect) return;
+    // The slots to merge, in split order (ordered compaction, 256 at a time).
+    if (threadIdx.x == 0) s_np = 0;
+    __syncthreads();
+    for (int base = 0; base < ns; base += 256) {
+        const int sp = base + threadIdx.x;
+        const bool pres = sp < ns && (mode != 2 || part_ml[(pbase + sp) * R].y != kPartEmpty);
+        const unsigned long long bal = __ballot(pres);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        if (lane == 0) s_cnt[w] = __popcll(bal);
+        __syncthreads();
+        int pos = s_np;
+        for (int k = 0; k < w; ++k) pos += s_cnt[k];
+        pos += __popcll(bal & ((1ull << lane) - 1ull));
+        if (pres) s_list[pos] = sp;
+        __syncthreads();
+        if (threadIdx.x == 0) s_np += (s_cnt[0] + s_cnt[1]) + (s_cnt[2] + s_cnt[3]);
+        __syncthreads();
+    }
+    const int np = s_np;
+    // Row statistics: four threads per row, each over every fourth slot,
     // merged in a fixed order.
     const int lr4 = threadIdx.x % kCombineRows, q4 = threadIdx.x / kCombineRows;
     {
         float M = -INFINITY;
         if (lr4 < nr)
-            for (int s = q4; s < ns; s += 4) M = fmaxf(M, part_ml[(pbase + s) * R + r0 + lr4].x);
+            for (int k = q4; k < np; k += 4)
+                M = fmaxf(M, part_ml[(pbase + s_list[k]) * R + r0 + lr4].x);
         s_red[q4][lr4] = M;
     }
     __syncthreads();
@@ -155,8 +181,8 @@ __global__ __launch_bounds__(256) void attn_combine(
         float den = 0.f;
         if (lr4 < nr) {
             const float M = s_m[lr4];
-            for (int s = q4; s < ns; s += 4) {
-                const float2 ml = part_ml[(pbase + s) * R + r0 + lr4];
+            for (int k = q4; k < np; k += 4) {
+                const float2 ml = part_ml[(pbase + s_list[k]) * R + r0 + lr4];
                 if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
             }
         }
@@ -167,11 +193,11 @@ __global__ __launch_bounds__(256) void attn_combine(
         s_inv[threadIdx.x] = 1.f / ((s_red[0][threadIdx.x] + s_red[1][threadIdx.x]) +
                                     (s_red[2][threadIdx.x] + s_red[3][threadIdx.x]));
     __syncthreads();
-    const bool cached = ns * nr <= kCombineCache;
+    const bool cached = np * nr <= kCombineCache;
     if (cached) {
-        for (int idx = threadIdx.x; idx < ns * nr; idx += blockDim.x) {
-            const int s = idx / nr, lr = idx - s * nr;
-            const float m = part_ml[(pbase + s) * R + r0 + lr].x;
+        for (int idx = threadIdx.x; idx < np * nr; idx += blockDim.x) {
+            const int k = idx / nr, lr = idx - k * nr;
+            const float m = part_ml[(pbase + s_list[k]) * R + r0 + lr].x;
             s_w[idx] = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
         }
         __syncthreads();
@@ -184,25 +210,25 @@ __global__ __launch_bounds__(256) void attn_combine(
         if (out_lowp) out_lowp[oi] = (uint16_t)f32_to_bf16_rne(acc);
     };
     if (cached && (R & 3) == 0 && (nr & 3) == 0) {
-        // Four consecutive rows per thread (16-byte loads), eight splits in
+        // Four consecutive rows per thread (16-byte loads), eight slots in
         // flight per step.
         const int nq = nr >> 2;
         for (int idx = threadIdx.x; idx < nq * kCombineDims; idx += blockDim.x) {
             const int dl = idx / nq, lq = 4 * (idx - dl * nq);
             const float* po = part_o + (pbase * D + d0 + dl) * R + r0 + lq;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            int s = 0;
-            for (; s + 8 <= ns; s += 8) {
+            int k = 0;
+            for (; k + 8 <= np; k += 8) {
                 f32x4 v[8], w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(po + (s + u) * sstride);
+                for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(po + s_list[k + u] * sstride);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(s_w + (s + u) * nr + lq);
+                for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(s_w + (k + u) * nr + lq);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) acc += w[u] * v[u];
             }
-            for (; s < ns; ++s)
-                acc += *(const f32x4*)(s_w + s * nr + lq) * *(const f32x4*)(po + s * sstride);
+            for (; k < np; ++k)
+                acc += *(const f32x4*)(s_w + k * nr + lq) * *(const f32x4*)(po + s_list[k] * sstride);
 #pragma unroll
             for (int j = 0; j < 4; ++j) emit(r0 + lq + j, d0 + dl, acc[j]);
         }
@@ -213,15 +239,15 @@ __global__ __launch_bounds__(256) void attn_combine(
         const int row = r0 + lr, d = d0 + dl;
         const float* po = part_o + (pbase * D + d) * R + row;
         float acc = 0.f;
-        for (int s = 0; s < ns; ++s) {
+        for (int k = 0; k < np; ++k) {
             float w;
             if (cached) {
-                w = s_w[s * nr + lr];
+                w = s_w[k * nr + lr];
             } else {
-                const float m = part_ml[(pbase + s) * R + row].x;
+                const float m = part_ml[(pbase + s_list[k]) * R + row].x;
                 w = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
             }
-            acc += w * po[s * sstride];
+            acc += w * po[s_list[k] * sstride];
         }
         emit(row, d, acc);
     }
@@ -347,6 +373,9 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         const int rc = mla_plan(d->batch, d->num_q, d->n_q_heads, d->max_seq_len, &p->chunk,
                                 &p->max_splits);
         if (rc != SD_OK) return rc;
+        if (p->max_splits > kCombineMaxSplits)
+            return fail(SD_EUNSUPPORTED, "sd_verify_attn: more than %d key chunks per request",
+                        kCombineMaxSplits);
     }
     if (d->kind == SD_ATTN_MLA) {
         // planned above
@@ -363,6 +392,7 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         const long pairs = (long)d->batch * d->n_kv_heads;
         int chunk = 1024;
         while (chunk > 128 && pairs * ((maxkeys + chunk - 1) / chunk) < 16L * 4 * 256) chunk >>= 1;
+        while ((maxkeys + chunk - 1) / chunk > kCombineMaxSplits) chunk <<= 1;
         p->chunk = chunk;
         p->max_splits = (int)((maxkeys + chunk - 1) / chunk);
     } else {
@@ -475,6 +505,6 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
                         (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),
                    256, 0, s>>>(
         po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
-        d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0);
+        d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 2);
     return check_launch("attn_combine");
 }

@@ -43,6 +43,25 @@ struct GqaTile {
     static constexpr int kRingBytes = (kKStages + kVStages) * kHalfBytes;
 };
 
+// XOR applied to the 16-byte chunk index of K/V tile row `row`.  The LDS has
+// 64 banks of 4 bytes: a ds_read_b128 is served 16 lanes per pass and a
+// ds_read_b64_tr_b16 32 lanes per pass, each pass covering 256 bytes.
+//  K reads: the 16 lanes of a pass read one logical chunk of 16 consecutive
+//    rows, so the 16 rows must land in 16 distinct 16-byte bank groups;
+//  V reads: a 32-lane pass reads 4 logical chunks 4c..4c+3 of 4 consecutive
+//    rows (4-aligned), two lanes per chunk.
+// D = 128 (256-byte rows, every row starts at bank 0): f(row) takes bits 3:2
+// from row%4 and bits 1:0 from (row/4)%4, a bijection on each 16-row group
+// whose bits 3:2 differ between the 4 rows of a V pass.  D = 64 (128-byte
+// rows, row parity picks the bank half): f(row) = 4((row/2)%2) + (row/4)%4, a
+// bijection on the 8 rows of one parity in a 16-row group, whose bit 2
+// differs between rows r and r+2.
+template <int D>
+__device__ __forceinline__ int gqa_xor(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // Work items are (kv head, request, key chunk) triples of non-empty chunks,
 // numbered kv-head-major: item i has kv head i / NRC and request-chunk index
 // rc = i % NRC, where request b owns rc in [first[b], first[b+1]) and
@@ -54,6 +73,7 @@ struct GqaTile {
 // address ranges.  All cursor fields are wave-uniform.
 struct ItemCursor {
     int item, hi, t, ntiles, b, kvh, split, rc, L, start, end;
+    int pg;  // physical page of the current tile (DMA cursors only)
 };
 
 __device__ __forceinline__ void cursor_fill(ItemCursor& c, int NQ, int chunk,
@@ -107,8 +127,9 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ first,
-    float* __restrict__ part_o, float2* __restrict__ part_ml, int B, int NQ, int Hq, int Hkv,
-    int G, int R, int max_pages, int chunk, int max_splits, float scale_log2) {
+    float* __restrict__ part_o, float2* __restrict__ part_ml, float* __restrict__ out,
+    uint16_t* __restrict__ out_lowp, int B, int NQ, int Hq, int Hkv, int G, int R, int max_pages,
+    int chunk, int max_splits, float scale_log2) {
     using T = GqaTile<D>;
     constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-dim blocks of O^T
@@ -122,22 +143,28 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
 
     // DMA op j of a half tile fills LDS bytes [1024 j, 1024 j + 1024): chunk
     // slot n = 64 j + lane, holding logical chunk (n % kRowChunks) ^
-    // chunk_xor(row) of row n / kRowChunks.
+    // gqa_xor(row) of row n / kRowChunks.
     int goff[T::kDmaHalf];
 #pragma unroll
     for (int j = 0; j < T::kDmaHalf; ++j) {
         const int n = 64 * j + lane;
         const int row = n / T::kRowChunks;
-        goff[j] = row * D + 8 * ((n % T::kRowChunks) ^ chunk_xor(row));
+        goff[j] = row * D + 8 * ((n % T::kRowChunks) ^ gqa_xor<D>(row));
     }
     const size_t head_elems = (size_t)kPage * D;
     char* const k_ring = ring;
     char* const v_ring = ring + T::kKStages * T::kHalfBytes;
+    // The page-table entry of a DMA cursor's tile is read when the cursor
+    // reaches the tile, one issue before it is needed, so the scalar load's
+    // latency is not on the DMA's critical path.
+    auto load_pg = [&](ItemCursor& c) {
+        if (c.item < c.hi)
+            c.pg = page_table[(size_t)c.b * max_pages + (c.start + kTile * c.t) / kPage];
+    };
     auto issue = [&](const uint16_t* __restrict__ cache, const ItemCursor& c, const char* dst_p) {
         const int ks = c.start + kTile * c.t;
-        const int pg = page_table[(size_t)c.b * max_pages + ks / kPage];
         const uint16_t* src =
-            cache + ((size_t)pg * Hkv + c.kvh) * head_elems + (size_t)(ks % kPage) * D;
+            cache + ((size_t)c.pg * Hkv + c.kvh) * head_elems + (size_t)(ks % kPage) * D;
         const uint32_t dst = lds_byte_addr(dst_p);
         // The stage's previous tile was read by this wave's ds_reads; make
         // sure they have returned before the DMA may overwrite it.
@@ -148,18 +175,23 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     };
 
     // Per-lane LDS byte offsets within a half tile.
-    //  K reads: row ln, logical chunk 2s + lh -> slot 8(s/4) + (2(s%4) ^ kx).
-    const int kx = lh ^ chunk_xor(ln);
-    int koff[4];
+    //  K reads of k-step s: row ln, logical chunk 2s + lh.
+    int koff[NS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) koff[r] = ln * T::kRowBytes + 16 * ((2 * r) ^ kx);
-    //  V reads (16-lane group g, lane sl): key 16tt + 4(g/2) + sl/4 (+8),
-    //  logical chunk 4db + 2(g&1) + (sl&3)/2, byte 8(sl&1) of the chunk.
+    for (int s = 0; s < NS; ++s) koff[s] = ln * T::kRowBytes + 16 * ((2 * s + lh) ^ gqa_xor<D>(ln));
+    //  V reads (16-lane group g, lane sl) of dim block db, half h: key
+    //  16tt + 4(g/2) + sl/4 + 8h, logical chunk 4db + 2(g&1) + (sl&3)/2, byte
+    //  8(sl&1) of the chunk (the swizzle depends on the key only modulo 16).
     const int g4 = lane >> 4, sl = lane & 15;
-    const int vx = (2 * (g4 & 1) + ((sl & 3) >> 1)) ^ (2 * (sl >> 2) + ((g4 >> 1) & 1));
-    const int vrow = (4 * (g4 >> 1) + (sl >> 2)) * T::kRowBytes + 8 * (sl & 1);
-    const int voff_e = vrow + 16 * vx;
-    const int voff_o = vrow + 16 * (4 ^ vx);
+    const int vch = 2 * (g4 & 1) + ((sl & 3) >> 1);
+    int voff[NDB][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int vr = 4 * (g4 >> 1) + (sl >> 2) + 8 * h;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db][h] = vr * T::kRowBytes + 16 * ((4 * db + vch) ^ gqa_xor<D>(vr)) + 8 * (sl & 1);
+    }
 
     // Three cursors over the wave's tile stream: K DMA (three tiles ahead of
     // the compute), V DMA (two ahead) and compute.  Issue order: K0 K1 V0 K2
@@ -172,6 +204,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     ItemCursor kc;
     cursor_begin(kc, (int)(n_items * gw / nw), (int)(n_items * (gw + 1) / nw), B, NRC, NQ, chunk,
                  first, seq_lens);
+    load_pg(kc);
     ItemCursor vc = kc, cc = kc;
     int nk = 0, nv = 0;
     auto issue_k = [&]() {
@@ -179,6 +212,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             issue(k_cache, kc, k_ring + (nk % T::kKStages) * T::kHalfBytes);
             ++nk;
             cursor_next(kc, NRC, NQ, chunk, first, seq_lens);
+            load_pg(kc);
         }
     };
     auto issue_v = [&]() {
@@ -186,6 +220,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             issue(v_cache, vc, v_ring + (nv % T::kVStages) * T::kHalfBytes);
             ++nv;
             cursor_next(vc, NRC, NQ, chunk, first, seq_lens);
+            load_pg(vc);
         }
     };
     auto wait_groups = [&](int g) {  // at most g half tiles still in flight
@@ -209,11 +244,18 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     int lim[RB];
     float m_r[RB], l_r[RB];
     f32x16 o[RB][NDB];
+    // Consecutive chunks of one (request, kv head) form a segment: the online
+    // softmax state and Q carry over from chunk to chunk, and the segment is
+    // written once, at its end.
+    int seg_b = -1, seg_kvh = -1, seg_split0 = 0;
     while (cc.item < cc.hi) {
         // K(cseq) has landed once at most the halves issued after it are in
         // flight: K(j > cseq) and V(j >= max(cseq - 1, 0)).
         wait_groups((nk - 1 - cseq) + (nv - max(cseq - 1, 0)));
-        if (cc.t == 0) {
+        if (cc.t == 0 && !(cc.b == seg_b && cc.kvh == seg_kvh)) {
+            seg_b = cc.b;
+            seg_kvh = cc.kvh;
+            seg_split0 = cc.split;
             // New item: Q fragments (B operand; column = query row, k = d).
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -249,7 +291,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const u32x4 kf = *(const u32x4*)(ktile + koff[s & 3] + 128 * (s >> 2));
+            const u32x4 kf = *(const u32x4*)(ktile + koff[s]);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma_32x32x16(kf, qf[rb][s], sacc[rb]);
         }
@@ -306,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             const int nv = cc.end - ks;
             for (int idx = lane; idx < (kTile - nv) * T::kRowChunks; idx += 64) {
                 const int row = nv + idx / T::kRowChunks, c = idx % T::kRowChunks;
-                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ chunk_xor(row))) =
+                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa_xor<D>(row))) =
                     u32x4{0, 0, 0, 0};
             }
         }
@@ -316,10 +358,9 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const char* vp = vtile + 16 * tt * T::kRowBytes + 128 * (db >> 1) +
-                                 ((db & 1) ? voff_o : voff_e);
-                const u32x2 v0 = lds_read_tr16(vp);
-                const u32x2 v1 = lds_read_tr16(vp + 8 * T::kRowBytes);
+                const char* vp = vtile + 16 * tt * T::kRowBytes;
+                const u32x2 v0 = lds_read_tr16(vp + voff[db][0]);
+                const u32x2 v1 = lds_read_tr16(vp + voff[db][1]);
                 const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
@@ -333,20 +374,56 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         // tiles ahead in the wave's stream.
         issue_k();
         issue_v();
-        if (cc.t == cc.ntiles - 1) {
-            const size_t pidx = ((size_t)cc.b * Hkv + cc.kvh) * max_splits + cc.split;
-            float* po = part_o + pidx * D * R;
+        const int ns_b = (cc.L + NQ + chunk - 1) / chunk;
+        const bool last_of_pair = cc.split == ns_b - 1;
+        if (cc.t == cc.ntiles - 1 && (last_of_pair || cc.item + 1 >= cc.hi)) {
+            const size_t pbase = ((size_t)cc.b * Hkv + cc.kvh) * max_splits;
+            if (seg_split0 == 0 && last_of_pair) {
+                // The segment covers the whole pair: normalised rows straight
+                // to the output.  Lane (ln, lh) holds dims 8(r/4) + 4lh + r%4.
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int row = rb * 32 + ln;
-                if (row >= R) continue;
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int row = rb * 32 + ln;
+                    if (row >= R) continue;
+                    const int i = row / G, gq = row - i * G;
+                    const size_t oi = (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D;
+                    const float inv = 1.f / l_r[rb];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[rb][db][r];
-                if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
+                        for (int qd = 0; qd < 4; ++qd) {
+                            const int d = db * 32 + 8 * qd + 4 * lh;
+                            const f32x4 v = {o[rb][db][4 * qd] * inv, o[rb][db][4 * qd + 1] * inv,
+                                             o[rb][db][4 * qd + 2] * inv,
+                                             o[rb][db][4 * qd + 3] * inv};
+                            *(f32x4*)(out + oi + d) = v;
+                            if (out_lowp) {
+                                u32x2 w;
+                                w.x = pack_bf16x2(v[0], v[1]);
+                                w.y = pack_bf16x2(v[2], v[3]);
+                                *(u32x2*)(out_lowp + oi + d) = w;
+                            }
+                        }
+                }
+                if (lane == 0) part_ml[pbase * R] = make_float2(-INFINITY, kPartDirect);
+            } else {
+                const size_t pidx = pbase + seg_split0;
+                float* po = part_o + pidx * D * R;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int row = rb * 32 + ln;
+                    if (row >= R) continue;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[rb][db][r];
+                    if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
+                }
+                for (int sp = seg_split0 + 1 + lane; sp <= cc.split; sp += 64)
+                    part_ml[(pbase + sp) * R] = make_float2(-INFINITY, kPartEmpty);
             }
+            seg_b = -1;  // the next item starts a new segment
         }
         cursor_next(cc, NRC, NQ, chunk, first, seq_lens);
         ++cseq;
@@ -405,8 +482,8 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, floa
 #define SDV_LAUNCH_GQA(DD, RBB)                                                                  \
     attn_gqa_stream<DD, RBB><<<g_num_cus, 256, 0, s>>>(                                          \
         (const uint16_t*)d->q, (const uint16_t*)d->k_cache, (const uint16_t*)d->v_cache,         \
-        d->page_table, d->seq_lens, first, po, pml, d->batch, d->num_q, d->n_q_heads,            \
-        d->n_kv_heads, G, R, d->max_pages, chunk, max_splits, scale_log2)
+        d->page_table, d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp, d->batch,   \
+        d->num_q, d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, chunk, max_splits, scale_log2)
     if (d->d_qk == 128) {
         if (R <= 32) SDV_LAUNCH_GQA(128, 1); else SDV_LAUNCH_GQA(128, 2);
     } else {
