@@ -50,7 +50,7 @@ def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_sd_amd", "csrc")
     for f in (os.path.join(csrc, KERNEL_SOURCES[kernel]), os.path.join(csrc, "sdv_device.h"),
-              os.path.join(csrc, "sdv_lds.h"),
+              os.path.join(csrc, "sdv_lds.h"), os.path.join(csrc, "sdv_internal.h"),
               os.path.join(ROOT, "speculative_decoding_sd_amd", "build.py")):
         with open(f, "rb") as fh:
             h.update(fh.read())
