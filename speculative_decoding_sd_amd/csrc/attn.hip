@@ -6,20 +6,18 @@
 // and each new key/value goes into the cache.
 //
 // Pipeline on one stream:
-//   attn_validate   per request: capacity and page-table entries (flags)
-//   attn_append     K+1 new keys/values -> cache positions L_b .. L_b+K
-//   attn_gqa_bf16   split-KV flash decoding; one workgroup per (request,
-//                   kv head, key chunk); every query row of the kv head's
-//                   group (G heads x K+1 positions) shares each K/V tile, so
+//   attn_validate_append  per request: capacity and page-table entries
+//                   (flags), then the K+1 new keys/values -> cache positions
+//                   L_b .. L_b+K
+//   GQA, bf16:      attn_items (prefix sum of the requests' key chunks) and
+//                   attn_gqa_stream (attn_gqa.hip): persistent waves stream
+//                   (kv head, request, chunk) items through LDS rings; every
+//                   query row of the kv head's group shares each K/V tile, so
 //                   a tile is read from HBM exactly once
+//   MLA, bf16:      attn_mla_bf16 and its exact fallback (attn_mla.hip)
 //   attn_combine    log-sum-exp merge of the chunk partials
 // plus attn_f32_rows, a plain fp32 path for small float32 problems.
-//
-// MFMA mapping (bf16, 32x32x16): S^T = K Q^T puts one query row per lane
-// column, so the online-softmax state and the rescale of O^T = V^T P^T stay
-// lane-local.  K tiles go straight from HBM into A-operand registers; V tiles
-// are written transposed into a per-wave LDS buffer (keys permuted so each
-// A-operand fragment is two 8-byte reads).
+
 #include <math.h>
 
 #include "sdv_device.h"
@@ -31,14 +29,23 @@ namespace {
 constexpr int kPage = 64;
 
 // ---------------------------------------------------------------------------
-// Per-request checks.  valid[b] = 1 when 0 <= L_b <= max_seq_len,
-// L_b + NQ <= max_pages * 64 and every page entry covering 0 .. L_b+NQ-1 is a
-// pool page.  Later kernels touch only valid requests.
+// Per-request checks and append, one block per (position i, request b).
+// Every block of a request takes the same decision; block i = 0 records it.
+// valid[b] = 1 when
+// 0 <= L_b <= max_seq_len, L_b + NQ <= max_pages * 64 and every page entry
+// covering 0 .. L_b+NQ-1 is a pool page.  Later kernels touch only valid
+// requests.  Then (k_new given) row i of k_new / v_new goes to position
+// L_b + i with 16-byte copies; MLA copies the latent row into k_cache only.
 // ---------------------------------------------------------------------------
-__global__ void attn_validate(const int32_t* __restrict__ seq_lens,
-                              const int32_t* __restrict__ page_table, int32_t* __restrict__ valid,
-                              int32_t* err, int NQ, int max_pages, int num_pages, int max_seq_len) {
-    const int b = blockIdx.x;
+__global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
+                                     const int32_t* __restrict__ page_table,
+                                     int32_t* __restrict__ valid, int32_t* err,
+                                     const uint8_t* __restrict__ k_new,
+                                     const uint8_t* __restrict__ v_new,
+                                     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                     int NQ, int Hkv, int row_bytes_k, int row_bytes_v,
+                                     int max_pages, int num_pages, int max_seq_len, int mla) {
+    const int i = blockIdx.x, b = blockIdx.y;
     const int L = seq_lens[b];
     const bool cap_ok =
         L >= 0 && L <= max_seq_len && (long)L + NQ <= (long)max_pages * kPage;
@@ -51,48 +58,40 @@ __global__ void attn_validate(const int32_t* __restrict__ seq_lens,
         }
     }
     bad_page = __syncthreads_or(bad_page);
-    if (threadIdx.x == 0) {
-        valid[b] = (cap_ok && !bad_page) ? 1 : 0;
+    const bool ok = cap_ok && !bad_page;
+    if (threadIdx.x == 0 && i == 0) {
+        valid[b] = ok ? 1 : 0;
         if (!cap_ok) set_error(err, SD_DERR_CAPACITY);
         if (bad_page) set_error(err, SD_DERR_PAGE);
     }
-}
-
-// ---------------------------------------------------------------------------
-// Append: row i of k_new / v_new -> position L_b + i.  One block per (i, b),
-// 16-byte copies.  MLA copies the latent row into k_cache only.
-// ---------------------------------------------------------------------------
-__global__ void attn_append(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
-                            uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                            const int32_t* __restrict__ page_table,
-                            const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
-                            int NQ, int Hkv, int row_bytes_k, int row_bytes_v, int max_pages,
-                            int mla) {
-    const int i = blockIdx.x, b = blockIdx.y;
-    if (!valid[b]) return;
-    const long pos = (long)seq_lens[b] + i;
-    const long pg = page_table[(size_t)b * max_pages + pos / kPage];
-    const long off = pos % kPage;
+    if (!ok || !k_new) return;
     const int nk = row_bytes_k / 16, nv = row_bytes_v / 16;
-    if (mla) {
-        const u32x4* src = (const u32x4*)(k_new + ((size_t)b * NQ + i) * row_bytes_k);
-        u32x4* dst = (u32x4*)(k_cache + ((size_t)pg * kPage + off) * row_bytes_k);
-        for (int c = threadIdx.x; c < nk; c += blockDim.x) dst[c] = src[c];
-        return;
-    }
-    for (int idx = threadIdx.x; idx < Hkv * nk; idx += blockDim.x) {
-        const int h = idx / nk, c = idx - h * nk;
-        const u32x4* src =
-            (const u32x4*)(k_new + (((size_t)b * NQ + i) * Hkv + h) * row_bytes_k) + c;
-        u32x4* dst = (u32x4*)(k_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_k) + c;
-        *dst = *src;
-    }
-    for (int idx = threadIdx.x; idx < Hkv * nv; idx += blockDim.x) {
-        const int h = idx / nv, c = idx - h * nv;
-        const u32x4* src =
-            (const u32x4*)(v_new + (((size_t)b * NQ + i) * Hkv + h) * row_bytes_v) + c;
-        u32x4* dst = (u32x4*)(v_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_v) + c;
-        *dst = *src;
+    {
+        const long pos = (long)L + i;
+        const long pg = page_table[(size_t)b * max_pages + pos / kPage];
+        const long off = pos % kPage;
+        if (mla) {
+            const u32x4* src = (const u32x4*)(k_new + ((size_t)b * NQ + i) * row_bytes_k);
+            u32x4* dst = (u32x4*)(k_cache + ((size_t)pg * kPage + off) * row_bytes_k);
+            for (int c = threadIdx.x; c < nk; c += blockDim.x) dst[c] = src[c];
+            return;
+        }
+        for (int idx = threadIdx.x; idx < Hkv * nk; idx += blockDim.x) {
+            const int h = idx / nk, c = idx - h * nk;
+            const u32x4* src =
+                (const u32x4*)(k_new + (((size_t)b * NQ + i) * Hkv + h) * row_bytes_k) + c;
+            u32x4* dst =
+                (u32x4*)(k_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_k) + c;
+            *dst = *src;
+        }
+        for (int idx = threadIdx.x; idx < Hkv * nv; idx += blockDim.x) {
+            const int h = idx / nv, c = idx - h * nv;
+            const u32x4* src =
+                (const u32x4*)(v_new + (((size_t)b * NQ + i) * Hkv + h) * row_bytes_v) + c;
+            u32x4* dst =
+                (u32x4*)(v_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_v) + c;
+            *dst = *src;
+        }
     }
 }
 
@@ -102,10 +101,9 @@ __global__ void attn_append(const uint8_t* __restrict__ k_new, const uint8_t* __
 // Invalid requests get NaN rows.
 // ---------------------------------------------------------------------------
 constexpr int kCombineRows = 64;
-constexpr int kCombineDims = 32;
 constexpr int kCombineCache = 12288;  // split weights cached per block (48 KiB)
 
-// grid (kv head, request, row block x 32-dim block).  mode 1 (MLA): requests
+// grid (kv head, request, 64-row block).  mode 1 (MLA): requests
 // whose keys fit one chunk were written by the attention kernel already.
 // mode 2 (GQA): the attention kernel marks in row 0 of each slot whether the
 // pair was written directly (slot 0) or a slot is empty (its chunk was merged
@@ -124,14 +122,12 @@ __global__ __launch_bounds__(256) void attn_combine(
     __shared__ int s_list[kCombineMaxSplits];
     __shared__ int s_cnt[4], s_np;
     const int kvh = blockIdx.x, b = blockIdx.y;
-    const int ndb = D / kCombineDims;
-    const int r0 = (blockIdx.z / ndb) * kCombineRows;
-    const int d0 = (blockIdx.z % ndb) * kCombineDims;
+    const int r0 = blockIdx.z * kCombineRows;
     const int nr = min(kCombineRows, R - r0);
     if (nr <= 0) return;
     if (!valid[b]) {
-        for (int idx = threadIdx.x; idx < nr * kCombineDims; idx += blockDim.x) {
-            const int row = r0 + idx % nr, d = d0 + idx / nr;
+        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
+            const int row = r0 + idx % nr, d = idx / nr;
             const int i = row / G, g = row - i * G;
             const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
             out[oi] = NAN;
@@ -213,9 +209,9 @@ __global__ __launch_bounds__(256) void attn_combine(
         // Four consecutive rows per thread (16-byte loads), eight slots in
         // flight per step.
         const int nq = nr >> 2;
-        for (int idx = threadIdx.x; idx < nq * kCombineDims; idx += blockDim.x) {
+        for (int idx = threadIdx.x; idx < nq * D; idx += blockDim.x) {
             const int dl = idx / nq, lq = 4 * (idx - dl * nq);
-            const float* po = part_o + (pbase * D + d0 + dl) * R + r0 + lq;
+            const float* po = part_o + (pbase * D + dl) * R + r0 + lq;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             int k = 0;
             for (; k + 8 <= np; k += 8) {
@@ -230,13 +226,13 @@ __global__ __launch_bounds__(256) void attn_combine(
             for (; k < np; ++k)
                 acc += *(const f32x4*)(s_w + k * nr + lq) * *(const f32x4*)(po + s_list[k] * sstride);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) emit(r0 + lq + j, d0 + dl, acc[j]);
+            for (int j = 0; j < 4; ++j) emit(r0 + lq + j, dl, acc[j]);
         }
         return;
     }
-    for (int idx = threadIdx.x; idx < nr * kCombineDims; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
         const int dl = idx / nr, lr = idx - dl * nr;
-        const int row = r0 + lr, d = d0 + dl;
+        const int row = r0 + lr, d = dl;
         const float* po = part_o + (pbase * D + d) * R + row;
         float acc = 0.f;
         for (int k = 0; k < np; ++k) {
@@ -465,16 +461,12 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     char* ws = (char*)workspace;
     int32_t* valid = (int32_t*)(ws + p.off_valid);
     const int B = d->batch, NQ = d->num_q;
-    attn_validate<<<B, 256, 0, s>>>(d->seq_lens, d->page_table, valid, d->dev_error, NQ,
-                                    d->max_pages, d->num_pages, d->max_seq_len);
-    if ((rc = check_launch("attn_validate")) != SD_OK) return rc;
-    if (d->k_new) {
-        attn_append<<<dim3(NQ, B), 256, 0, s>>>(
-            (const uint8_t*)d->k_new, (const uint8_t*)d->v_new, (uint8_t*)d->k_cache,
-            (uint8_t*)d->v_cache, d->page_table, d->seq_lens, valid, NQ, d->n_kv_heads,
-            d->d_qk * es, d->d_v * es, d->max_pages, d->kind == SD_ATTN_MLA);
-        if ((rc = check_launch("attn_append")) != SD_OK) return rc;
-    }
+    attn_validate_append<<<dim3(NQ, B), 256, 0, s>>>(
+        d->seq_lens, d->page_table, valid, d->dev_error, (const uint8_t*)d->k_new,
+        (const uint8_t*)d->v_new, (uint8_t*)d->k_cache, (uint8_t*)d->v_cache, NQ, d->n_kv_heads,
+        d->d_qk * es, d->d_v * es, d->max_pages, d->num_pages, d->max_seq_len,
+        d->kind == SD_ATTN_MLA);
+    if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {
         attn_f32_rows<<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
@@ -491,7 +483,7 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         if ((rc = mla_launch(d, valid, flags, po, pml, p.chunk, p.max_splits, scale, s)) != SD_OK)
             return rc;
         if (p.max_splits == 1) return SD_OK;
-        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),
+        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows),
                        256, 0, s>>>(
             po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads, 1,
             p.G, p.R, d->d_v, p.chunk, p.max_splits, 1);
@@ -502,7 +494,7 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         SD_OK)
         return rc;
     attn_combine<<<dim3(d->n_kv_heads, B,
-                        (p.R + kCombineRows - 1) / kCombineRows * (d->d_v / kCombineDims)),
+                        (p.R + kCombineRows - 1) / kCombineRows),
                    256, 0, s>>>(
         po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
         d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 2);
