@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time K replays of the step captured as one HIP graph (per-call "
+                         "times still come from the eager steps before it)")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
     return ap.parse_args()
@@ -261,7 +264,7 @@ def main():
     cfg = sdsynth.CONFIGS[args.config]
     seed = sdsynth.config_seed(args.config)
     dev = torch.device("cuda", 0)
-    extra = (args.warmup + args.steps + 2) * cfg.num_q
+    extra = (args.warmup + (2 if args.graph else 1) * args.steps + 4) * cfg.num_q
     wl = sdsynth.make_workload(cfg, seed, device=dev, extra_tokens=extra)
     sample = None
     n_cpu = args.cpu_sample_requests or cpu_sample_size(cfg, wl.seq_lens)
@@ -322,6 +325,21 @@ def main():
     acc_total = (L_end - L_start).sum()  # j_b + 1 per request per step
     n_err = int(step.dev_error.item())
     ms = wall_ms
+    eager_ms = wall_ms
+    if args.graph:
+        # The same step as one graph launch: capture, one untimed replay, then
+        # K timed replays.  Each replay continues from the previous state.
+        step.capture()
+        step.replay()
+        torch.cuda.synchronize()
+        Lg0 = seq_lens.cpu().numpy().copy()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        acc_total = (seq_lens.cpu().numpy() - Lg0).sum()
+        n_err = int(step.dev_error.item())
     B, Q = cfg.batch, cfg.num_q
     pos_per_s = B * Q / (ms * 1e-3)
     tok_per_s = acc_total / args.steps / (ms * 1e-3)
@@ -377,6 +395,8 @@ def main():
         "accepted_tokens_per_sec": tok_per_s,
         "mean_emitted_per_request": acc_total / args.steps / B,
         "event_ms_per_step": ev_step_ms,
+        "graph": bool(args.graph),
+        "eager_ms_per_step": eager_ms,
         "per_call_ms": per_call,
         "roofline": roof,
         "kernels": kernels,

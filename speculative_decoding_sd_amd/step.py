@@ -1,7 +1,8 @@
 """One verify step of a draft chain: the four library calls on one stream.
 
 VerifyStep owns the outputs and workspaces for one configuration and issues
-sd_verify_attn -> sd_lm_head -> sd_accept -> sd_kv_rollback.  The LM-head
+sd_verify_attn -> sd_lm_head -> sd_accept -> sd_kv_rollback, eagerly (run) or
+as one captured HIP graph (capture / replay).  The LM-head
 input is either a caller-supplied hidden matrix H [B*(K+1), hidden] or the
 attention output itself (rounded to the cache dtype) when H is None.
 """
@@ -97,3 +98,18 @@ class VerifyStep:
         self.lm_head(stream)
         self.accept(stream)
         self.rollback(stream)
+
+    def capture(self):
+        """Records the four calls of one step into a HIP graph (torch's
+        CUDAGraph on ROCm), so that replay() re-issues the whole step with one
+        launch.  The library allocates nothing and records no memsets, and the
+        step reads its state (seq_lens, page table, cache) from device memory,
+        so every replay is the next step.  Call run() once before capturing."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
