@@ -160,9 +160,12 @@ def lm_head(H, W, rows=None):
     return out
 
 
-def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample):
+def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample,
+           relaxed_topk=None, relaxed_delta=None):
     """Returns dict with num_accepted, out_tokens, next_token, out_offsets,
-    packed, diag, n_invalid.  logits: [B, K+1, V] float32/float64/bf16 bits."""
+    packed, diag, n_invalid.  logits: [B, K+1, V] float32/float64/bf16 bits.
+    relaxed_topk / relaxed_delta ([B] int / float, optional): relaxed
+    acceptance for greedy requests with top-N > 0 (orc_accept_ex)."""
     logits = _c(logits)
     B, Q, V = logits.shape
     K = Q - 1
@@ -176,9 +179,11 @@ def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample):
         num_accepted=np.empty(B, np.int32), out_tokens=np.empty((B, Q), np.int32),
         next_token=np.empty(B, np.int32), out_offsets=np.empty(B + 1, np.int32),
         packed=np.empty(B * Q, np.int32), diag=np.empty((B, 4), np.float64))
-    n_bad = lib().orc_accept(
+    rk = _c(relaxed_topk, np.int32) if relaxed_topk is not None else None
+    rd = _c(relaxed_delta, np.float32) if relaxed_delta is not None else None
+    n_bad = lib().orc_accept_ex(
         B, K, V, _dtype_code(logits), _ptr(logits), _ptr(drafts), _ptr(temperature),
-        _ptr(top_p), _ptr(draft_probs), _ptr(u_accept), _ptr(u_sample),
+        _ptr(top_p), _ptr(draft_probs), _ptr(u_accept), _ptr(u_sample), _ptr(rk), _ptr(rd),
         _ptr(out["num_accepted"]), _ptr(out["out_tokens"]), _ptr(out["next_token"]),
         _ptr(out["out_offsets"]), _ptr(out["packed"]), _ptr(out["diag"]))
     out["n_invalid"] = n_bad

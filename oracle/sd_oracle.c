@@ -470,11 +470,71 @@ static int inverse_cdf(const double* r, int V, double u, double* edge) {
  * top-p boundary gap over the rows used.  Returns the count of invalid
  * requests.
  */
+/*
+ * Relaxed acceptance of one draft ([TRT-MTP] "寬松接受", Fig. 6): take the
+ * top-N tokens of the row's logits (order: logit descending, id ascending),
+ * compute the token probabilities with a softmax of the logits, drop every
+ * candidate whose probability is below (top-1 probability - delta), and
+ * accept the draft if it is one of the remaining candidates.  margin: the
+ * draft's |p_d - (p_top1 - delta)| when it is among the top N (else
+ * +inf).  Probabilities in fp64.
+ */
+int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
+                  const int* drafts, const float* temperature, const float* top_p,
+                  const float* draft_probs, const float* u_accept, const float* u_sample,
+                  const int* relaxed_topk, const float* relaxed_delta, int* num_accepted,
+                  int* out_tokens, int* next_token, int* out_offsets, int* packed,
+                  double* diag);
+
+static int relaxed_accepts(const void* row, int dtype, int V, int N, double delta, int d,
+                           double* margin) {
+    int* idx = (int*)malloc(sizeof(int) * (size_t)V);
+    for (int v = 0; v < V; ++v) idx[v] = v;
+    g_sort_ctx.row = row;
+    g_sort_ctx.dtype = dtype;
+    qsort(idx, (size_t)V, sizeof(int), cmp_desc);
+    const int n_top = N < V ? N : V;
+    double m = load_elem(row, dtype, idx[0]);
+    double Z = 0.0;
+    for (int v = 0; v < V; ++v) Z += exp(load_elem(row, dtype, v) - m);
+    const double p_top1 = 1.0 / Z; /* exp(m - m) / Z */
+    int hit = 0;
+    *margin = INFINITY;
+    for (int k = 0; k < n_top; ++k) {
+        if (idx[k] != d) continue;
+        const double p_d = exp(load_elem(row, dtype, d) - m) / Z;
+        *margin = fabs(p_d - (p_top1 - delta));
+        hit = !(p_d < p_top1 - delta);
+    }
+    free(idx);
+    return hit;
+}
+
 int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
                const int* drafts, const float* temperature, const float* top_p,
                const float* draft_probs, const float* u_accept, const float* u_sample,
                int* num_accepted, int* out_tokens, int* next_token, int* out_offsets,
                int* packed, double* diag) {
+    return orc_accept_ex(B, K, V, logits_dtype, logits, drafts, temperature, top_p, draft_probs,
+                         u_accept, u_sample, NULL, NULL, num_accepted, out_tokens, next_token,
+                         out_offsets, packed, diag);
+}
+
+/*
+ * As orc_accept, plus relaxed acceptance for greedy requests:
+ * relaxed_topk[b] > 0 (with relaxed_delta[b], finite and >= 0) replaces the
+ * top-1 match of draft n by relaxed_accepts over row n-1 (the final token is
+ * still the argmax of row j); 0 keeps the strict rule; sampled requests
+ * ignore it.  A negative top-N, or a bad delta for a relaxed greedy request,
+ * makes the request invalid.  Either array may be NULL (strict).  For
+ * relaxed requests diag[1] holds the smallest margin of relaxed_accepts.
+ */
+int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
+                  const int* drafts, const float* temperature, const float* top_p,
+                  const float* draft_probs, const float* u_accept, const float* u_sample,
+                  const int* relaxed_topk, const float* relaxed_delta, int* num_accepted,
+                  int* out_tokens, int* next_token, int* out_offsets, int* packed,
+                  double* diag) {
     const int Q = K + 1;
     size_t es = elem_size(logits_dtype);
     int n_invalid = 0;
@@ -487,6 +547,10 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
         double dg[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
         int ok = !(isnan(T) || T < 0);
         if (ok && T > 0 && (isnan(tp) || tp <= 0)) ok = 0;
+        const int rN = relaxed_topk ? relaxed_topk[b] : 0;
+        const double rdelta = (relaxed_topk && relaxed_delta) ? relaxed_delta[b] : 0.0;
+        if (rN < 0) ok = 0;
+        if (ok && T == 0 && rN > 0 && (!relaxed_delta || !isfinite(rdelta) || rdelta < 0)) ok = 0;
         if (ok && T > 0 && K > 0 && !draft_probs) ok = 0;
         for (int n = 0; ok && n < K; ++n)
             if (drafts[(size_t)b * K + n] >= V) ok = 0;
@@ -501,7 +565,23 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
             continue;
         }
         int j = 0, f = -1;
-        if (T == 0.0) {
+        if (T == 0.0 && rN > 0) {
+            /* Relaxed: draft n is accepted while it is a surviving top-N
+             * candidate of row n-1; the final token is the argmax of row j. */
+            while (j < K) {
+                int d = drafts[(size_t)b * K + j];
+                if (d < 0) break;
+                double mr;
+                int hit = relaxed_accepts(base + (size_t)j * V * es, logits_dtype, V, rN, rdelta,
+                                          d, &mr);
+                if (mr < dg[1]) dg[1] = mr;
+                if (!hit) break;
+                ++j;
+            }
+            double mg;
+            f = row_argmax(base + (size_t)j * V * es, logits_dtype, V, &mg);
+            dg[0] = mg;
+        } else if (T == 0.0) {
             double mg;
             int t = row_argmax(base, logits_dtype, V, &mg);
             dg[0] = mg;
