@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 1
+#define SD_ABI_VERSION 2
 
 /* status codes */
 #define SD_OK 0
@@ -191,6 +191,14 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *   accepted it is drawn from p_t of row K.  Draws take the smallest v whose
  *   running sum over token ids exceeds u_sample[b][row] * (total); the
  *   statistics and sums are kept in float64.
+ * Relaxed greedy verification ([TRT-MTP] "寬松接受", Fig. 6): with
+ *   relaxed_topk[b] = N > 0 and temperature[b] == 0, draft n is accepted
+ *   while it is one of the N largest logits of row n-1 (order: logit desc,
+ *   id asc) and its softmax probability (T = 1, fp64) is not below the
+ *   top-1 probability minus relaxed_delta[b]; the final token is still the
+ *   argmax of row j.  N = 0 keeps the strict rule; sampled requests ignore
+ *   N.  N < 0, or (for a relaxed greedy request) a delta that is NaN,
+ *   infinite or negative, makes the request invalid (SD_DERR_PARAM).
  * A draft id < 0 ends the chain early (the final token is then drawn from,
  *   or is the argmax of, the row that draft would have been judged by).
  * Each request emits j_b + 1 tokens: accepted drafts, then the final token.
@@ -204,6 +212,9 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *                draft n was drawn from), or NULL when every request is greedy
  *                or K == 0
  *   u_accept, u_sample  float32 [B][K+1], uniforms in [0, 1)
+ *   relaxed_topk int32 [B], relaxed_delta float32 [B]: both NULL (strict
+ *                for every request) or relaxed_topk set; relaxed_delta is
+ *                read for greedy requests with relaxed_topk[b] > 0
  * Outputs (device):
  *   num_accepted int32 [B]         j_b, or -1 for an invalid request
  *   out_tokens   int32 [B][K+1]    j_b+1 emitted tokens, then -1
@@ -232,6 +243,8 @@ typedef struct sd_accept_desc {
     int32_t* out_offsets;
     int32_t* packed_tokens;
     int32_t* dev_error; /* optional */
+    const int32_t* relaxed_topk;  /* optional (ABI version 2) */
+    const float* relaxed_delta;   /* optional (ABI version 2) */
 } sd_accept_desc;
 
 int sd_accept_workspace_size(const sd_accept_desc* d, size_t* bytes);

@@ -50,6 +50,7 @@ class AcceptDesc(ctypes.Structure):
         ("draft_tokens", _P), ("temperature", _P), ("top_p", _P), ("draft_probs", _P),
         ("u_accept", _P), ("u_sample", _P), ("num_accepted", _P), ("out_tokens", _P),
         ("next_token", _P), ("out_offsets", _P), ("packed_tokens", _P), ("dev_error", _P),
+        ("relaxed_topk", _P), ("relaxed_delta", _P),
     ]
 
 
@@ -217,17 +218,19 @@ def lm_head(H, W, logits, stream=None):
 
 def accept_desc(*, logits, draft_tokens, temperature, u_accept, u_sample, num_accepted,
                 out_tokens, next_token, out_offsets, packed_tokens, top_p=None,
-                draft_probs=None, dev_error=None) -> AcceptDesc:
+                draft_probs=None, dev_error=None, relaxed_topk=None,
+                relaxed_delta=None) -> AcceptDesc:
     B, Q, V = logits.shape
     return _keeping((logits, draft_tokens, temperature, u_accept, u_sample, num_accepted,
                      out_tokens, next_token, out_offsets, packed_tokens, top_p, draft_probs,
-                     dev_error), AcceptDesc(
+                     dev_error, relaxed_topk, relaxed_delta), AcceptDesc(
         batch=B, K=Q - 1, vocab=V, logits_dtype=sd_dtype(logits), logits=_ptr(logits),
         draft_tokens=_ptr(draft_tokens), temperature=_ptr(temperature), top_p=_ptr(top_p),
         draft_probs=_ptr(draft_probs), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
         num_accepted=_ptr(num_accepted), out_tokens=_ptr(out_tokens),
         next_token=_ptr(next_token), out_offsets=_ptr(out_offsets),
-        packed_tokens=_ptr(packed_tokens), dev_error=_ptr(dev_error)))
+        packed_tokens=_ptr(packed_tokens), dev_error=_ptr(dev_error),
+        relaxed_topk=_ptr(relaxed_topk), relaxed_delta=_ptr(relaxed_delta)))
 
 
 def accept(desc: AcceptDesc, ws=None, stream=None):

@@ -44,6 +44,8 @@ struct RowStat {
     int flags;      // SD_DERR_* bits of this row
     double zkeep;   // sum over kept tokens of exp((l - m) / T)
     double pt_d;    // p_t of the draft this row judges (row i judges draft i+1)
+    int relaxed_ok; // relaxed rule: the draft this row judges survives
+    int pad;
 };
 
 template <typename T>
@@ -147,6 +149,7 @@ struct RowAcc {
     int bidx = 0x7fffffff;
     bool nonfinite = false, anyfin = false;
     double z = 0.0;
+    int beat = 0;  // relaxed rows: elements ranked before the draft
 };
 
 // Folds N elements into a, in the thread's visit order (ids rise along it).
@@ -155,9 +158,15 @@ struct RowAcc {
 // only then is the group searched for the first id of its max and z
 // rescaled.  Sampled rows then add the group's terms eight at a time (all
 // eight table reads issued before the first is used) as pairwise trees.
-template <bool STOCH, int N>
+// RELAX rows also count the elements ranked before the draft d (logit xd)
+// in the order (logit desc, id asc).
+template <bool STOCH, bool RELAX, int N>
 __device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const int (&v)[N],
-                                         double invT, const double* tab) {
+                                         double invT, const double* tab, float xd, int d) {
+    if constexpr (RELAX) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) a.beat += (x[e] > xd) | ((x[e] == xd) & (v[e] < d));
+    }
     float gm = x[0];
     bool nan = x[0] != x[0];
 #pragma unroll
@@ -201,11 +210,11 @@ __device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const i
 
 // One pass over ids [v_lo, v_hi) of a row (v_lo a multiple of the vector
 // width when vec_ok); U vectors in flight per thread.
-template <typename T, bool STOCH>
+template <typename T, bool STOCH, bool RELAX>
 __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool vec_ok, RowAcc& a,
-                                         double invT, const double* tab) {
+                                         double invT, const double* tab, float xd, int d) {
     constexpr int E = Logit<T>::kPerVec;
-    constexpr int U = 4;
+    constexpr int U = RELAX ? 2 : 4;  // vectors in flight (fewer with the rank count)
     int v0 = v_lo;
     if (vec_ok) {
         const int c_lo = v_lo / E, c_hi = v_hi / E;
@@ -223,7 +232,7 @@ __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool v
                     x[u * E + e] = Logit<T>::lane(w[u], e);
                     v[u * E + e] = (c + u * 256) * E + e;
                 }
-            row_fold<STOCH>(a, x, v, invT, tab);
+            row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
         }
         for (; c < c_hi; c += 256) {
             const u32x4 w = *(const u32x4*)(lr + (size_t)c * E);
@@ -234,14 +243,14 @@ __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool v
                 x[e] = Logit<T>::lane(w, e);
                 v[e] = c * E + e;
             }
-            row_fold<STOCH>(a, x, v, invT, tab);
+            row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
         }
         v0 = c_hi * E;
     }
     for (int vv = v0 + (int)threadIdx.x; vv < v_hi; vv += 256) {
         const float x[1] = {Logit<T>::at(lr, vv)};
         const int v[1] = {vv};
-        row_fold<STOCH>(a, x, v, invT, tab);
+        row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
     }
 }
 
@@ -250,20 +259,24 @@ struct RowPart {
     float best;   // slice max (-inf if none finite)
     int bidx;     // its smallest id
     int bits;     // 1: a NaN or +inf seen; 2: a value above -inf seen
-    int pad;
-    double z;     // sum over the slice of exp((x - best)/T) (sampled rows)
+    int beat;     // relaxed rows: elements of the slice ranked before the draft
+    double z;     // sum over the slice of exp((x - best)/T) (sampled and relaxed rows)
 };
 
 // Grid: rows x splits blocks of 256 threads; block (row, s) covers ids
-// [s*span, min(V, (s+1)*span)) of its row.
-template <typename T>
+// [s*span, min(V, (s+1)*span)) of its row.  Relaxed greedy rows (top-N > 0)
+// take the sum at T = 1 and count the elements ranked before their draft
+// (compiled in only for launches with relaxed parameters, RX).
+template <typename T, bool RX>
 __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logits,
+                                                      const int32_t* __restrict__ drafts,
                                                       const float* __restrict__ temperature,
+                                                      const int32_t* __restrict__ relaxed_topk,
                                                       RowPart* __restrict__ parts, int Q, int V,
                                                       int splits, int span, int vec_ok) {
     __shared__ double s_exptab[64];
     __shared__ float s_best[4];
-    __shared__ int s_idx[4];
+    __shared__ int s_idx[4], s_beat[4];
     __shared__ double s_z[4];
     exp_table_init(s_exptab);
     __syncthreads();
@@ -271,12 +284,19 @@ __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logi
     const int b = row / Q;
     const T* lr = logits + (size_t)row * V;
     const int v_lo = sp * span, v_hi = min(V, v_lo + span);
+    const int i = row - b * Q, K = Q - 1;
     const float Tb = temperature[b];
-    const bool stoch = Tb > 0.f;
-    const double invT = stoch ? 1.0 / (double)Tb : 0.0;
+    const bool relaxed = RX && Tb == 0.f && relaxed_topk[b] > 0;
+    const double invT = Tb > 0.f ? 1.0 / (double)Tb : 1.0;
+    const int d = (relaxed && i < K) ? drafts[(size_t)b * K + i] : -1;
+    const bool count = d >= 0 && d < V;
+    const bool stoch = Tb > 0.f || count;  // the slice's sum is needed
+    const float xd = count ? Logit<T>::at(lr, d) : 0.f;
+    const bool vk = vec_ok != 0;
     RowAcc a;
-    if (stoch) row_pass<T, true>(lr, v_lo, v_hi, vec_ok != 0, a, invT, s_exptab);
-    else row_pass<T, false>(lr, v_lo, v_hi, vec_ok != 0, a, invT, s_exptab);
+    if (count) row_pass<T, true, RX>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
+    else if (stoch) row_pass<T, true, false>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
+    else row_pass<T, false, false>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
     float best = a.best;
     int bidx = a.bidx;
 #pragma unroll
@@ -312,12 +332,21 @@ __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logi
         __syncthreads();
         z = ((s_z[0] + s_z[1]) + s_z[2]) + s_z[3];
     }
+    int beat = 0;
+    if (count) {
+        int bt = a.beat;
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) bt += shfl_xor(bt, msk);
+        if (lane == 0) s_beat[wave] = bt;
+        __syncthreads();
+        beat = (s_beat[0] + s_beat[1]) + (s_beat[2] + s_beat[3]);
+    }
     if (threadIdx.x == 0) {
         RowPart p;
         p.best = best;
         p.bidx = bidx;
         p.bits = (nonfinite ? 1 : 0) | (anyfin ? 2 : 0);
-        p.pad = 0;
+        p.beat = beat;
         p.z = z;
         parts[blockIdx.x] = p;
     }
@@ -325,11 +354,15 @@ __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logi
 
 // One thread per row: merges the row's slices in order (max, smallest id on
 // ties, Z = sum_s z_s exp((best_s - m)/T)), checks the request's parameters
-// and, for sampled rows that judge a draft, p_t of that draft.
+// and, for sampled rows that judge a draft, p_t of that draft.  Relaxed rows
+// ([TRT-MTP] "寬松接受"): the draft survives when fewer than N tokens rank
+// before it and its probability exp(l_d - m)/Z (T = 1) is not below the
+// top-1 probability 1/Z minus delta, i.e. exp(l_d - m) >= 1 - delta Z.
 template <typename T>
 __global__ __launch_bounds__(256) void accept_rowmerge(
     const T* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ top_p, int has_probs,
+    const int32_t* __restrict__ relaxed_topk, const float* __restrict__ relaxed_delta,
     const RowPart* __restrict__ parts, RowStat* __restrict__ stats, int rows, int K, int V,
     int splits) {
     __shared__ double s_exptab[64];
@@ -341,9 +374,14 @@ __global__ __launch_bounds__(256) void accept_rowmerge(
     const float Tb = temperature[b];
     const float tp = top_p ? top_p[b] : 1.f;
     const bool stoch = Tb > 0.f;
+    const int rN = relaxed_topk ? relaxed_topk[b] : 0;
+    const bool relaxed = Tb == 0.f && rN > 0;
+    const double delta = (relaxed && relaxed_delta) ? (double)relaxed_delta[b] : 0.0;
     int flags = 0;
     if (isnan(Tb) || Tb < 0.f) flags |= SD_DERR_PARAM;
     if (stoch && (isnan(tp) || tp <= 0.f || (!has_probs && K > 0))) flags |= SD_DERR_PARAM;
+    if (rN < 0) flags |= SD_DERR_PARAM;
+    if (relaxed && (!relaxed_delta || !(delta >= 0.0) || isinf(delta))) flags |= SD_DERR_PARAM;
     const RowPart* pr = parts + (size_t)row * splits;
     float best = -INFINITY;
     int bidx = 0x7fffffff, bits = 0;
@@ -367,6 +405,21 @@ __global__ __launch_bounds__(256) void accept_rowmerge(
         const T* lr = logits + (size_t)row * V;
         if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), best, invT, s_exptab) / z;
     }
+    int relaxed_ok = 0;
+    if (relaxed && !flags && i < K) {
+        const int d = drafts[(size_t)b * K + i];
+        if (d >= 0 && d < V) {
+            int rank = 0;
+            for (int s = 0; s < splits; ++s) {
+                const RowPart p = pr[s];
+                rank += p.beat;
+                z += p.z * exp_neg((double)p.best - (double)best, s_exptab);
+            }
+            const T* lr = logits + (size_t)row * V;
+            const double e_d = exp_neg((double)Logit<T>::at(lr, d) - (double)best, s_exptab);
+            relaxed_ok = rank < rN && e_d >= 1.0 - delta * z;
+        }
+    }
     RowStat st;
     st.m = best;
     st.lambda = -INFINITY;
@@ -374,6 +427,8 @@ __global__ __launch_bounds__(256) void accept_rowmerge(
     st.flags = flags;
     st.zkeep = z;
     st.pt_d = pt_d;
+    st.relaxed_ok = relaxed_ok;
+    st.pad = 0;
     stats[row] = st;
 }
 
@@ -604,9 +659,9 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
     const T* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ draft_probs,
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
-    const RowStat* __restrict__ stats, int32_t* __restrict__ num_accepted,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_token, int32_t* err, int K,
-    int V) {
+    const int32_t* __restrict__ relaxed_topk, const RowStat* __restrict__ stats,
+    int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ next_token, int32_t* err, int K, int V) {
     __shared__ double s_exptab[64];
     exp_table_init(s_exptab);
     __syncthreads();
@@ -627,10 +682,14 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         if (flags) {
             set_error(err, flags);
         } else if (temperature[b] == 0.f) {
+            // Strict: the draft must be the row's argmax.  Relaxed (top-N >
+            // 0): it must survive the row's top-N / delta filter.
+            const bool relaxed = relaxed_topk != nullptr && relaxed_topk[b] > 0;
             j = 0;
             while (j < K) {
                 const int d = drafts[(size_t)b * K + j];
-                if (d < 0 || d != stats[(size_t)b * Q + j].argmax) break;
+                const RowStat& st = stats[(size_t)b * Q + j];
+                if (d < 0 || !(relaxed ? st.relaxed_ok != 0 : d == st.argmax)) break;
                 ++j;
             }
             f = stats[(size_t)b * Q + j].argmax;
@@ -945,40 +1004,50 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
     const int has_probs = d->draft_probs != nullptr;
     if (d->logits_dtype == SD_BF16) {
         const uint16_t* lg = (const uint16_t*)d->logits;
-        accept_rowpart<uint16_t><<<rows * splits, 256, 0, s>>>(lg, d->temperature, parts, Q, V,
-                                                               splits, span, vec_ok);
+        if (d->relaxed_topk)
+            accept_rowpart<uint16_t, true><<<rows * splits, 256, 0, s>>>(
+                lg, d->draft_tokens, d->temperature, d->relaxed_topk, parts, Q, V, splits, span,
+                vec_ok);
+        else
+            accept_rowpart<uint16_t, false><<<rows * splits, 256, 0, s>>>(
+                lg, d->draft_tokens, d->temperature, nullptr, parts, Q, V, splits, span, vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
         accept_rowmerge<uint16_t><<<(rows + 255) / 256, 256, 0, s>>>(
-            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, parts, stats, rows, K, V,
-            splits);
+            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
+            d->relaxed_delta, parts, stats, rows, K, V, splits);
         if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;
         if (d->top_p) {
             accept_topp_bf16<<<rows, 256, kWin * sizeof(uint32_t), s>>>(
                 lg, d->draft_tokens, d->temperature, d->top_p, stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_bf16")) != SD_OK) return rc;
         }
-        accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(lg, d->draft_tokens, d->temperature,
-                                                  d->draft_probs, d->u_accept, d->u_sample, stats,
-                                                  d->num_accepted, d->out_tokens, d->next_token,
-                                                  d->dev_error, K, V);
+        accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(
+            lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
+            d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
+            K, V);
     } else {
         const float* lg = (const float*)d->logits;
-        accept_rowpart<float><<<rows * splits, 256, 0, s>>>(lg, d->temperature, parts, Q, V, splits,
-                                                            span, vec_ok);
+        if (d->relaxed_topk)
+            accept_rowpart<float, true><<<rows * splits, 256, 0, s>>>(
+                lg, d->draft_tokens, d->temperature, d->relaxed_topk, parts, Q, V, splits, span,
+                vec_ok);
+        else
+            accept_rowpart<float, false><<<rows * splits, 256, 0, s>>>(
+                lg, d->draft_tokens, d->temperature, nullptr, parts, Q, V, splits, span, vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
         accept_rowmerge<float><<<(rows + 255) / 256, 256, 0, s>>>(
-            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, parts, stats, rows, K, V,
-            splits);
+            lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
+            d->relaxed_delta, parts, stats, rows, K, V, splits);
         if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;
         if (d->top_p) {
             accept_topp_f32<<<rows, 256, 0, s>>>(lg, d->draft_tokens, d->temperature, d->top_p,
                                                  stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_f32")) != SD_OK) return rc;
         }
-        accept_decide<float><<<B, kDecThreads, 0, s>>>(lg, d->draft_tokens, d->temperature,
-                                               d->draft_probs, d->u_accept, d->u_sample, stats,
-                                               d->num_accepted, d->out_tokens, d->next_token,
-                                               d->dev_error, K, V);
+        accept_decide<float><<<B, kDecThreads, 0, s>>>(
+            lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
+            d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
+            K, V);
     }
     if ((rc = check_launch("accept_decide")) != SD_OK) return rc;
     accept_pack<<<1, 1024, 0, s>>>(d->num_accepted, d->out_tokens, d->out_offsets,

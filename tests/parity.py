@@ -72,7 +72,8 @@ def excluded_requests(diag: np.ndarray) -> np.ndarray:
     return (diag[:, 1] < 1e-3) | (diag[:, 2] < 1e-9) | (diag[:, 3] < 1e-9)
 
 
-def run_accept(logits_t, drafts_t, temp_t, top_p_t, pd_t, ua_t, us_t):
+def run_accept(logits_t, drafts_t, temp_t, top_p_t, pd_t, ua_t, us_t, relaxed_topk_t=None,
+               relaxed_delta_t=None):
     B, Q, V = logits_t.shape
     i32 = dict(dtype=torch.int32, device=DEV)
     out = dict(num_accepted=torch.full((B,), -7, **i32), out_tokens=torch.full((B, Q), -7, **i32),
@@ -81,7 +82,8 @@ def run_accept(logits_t, drafts_t, temp_t, top_p_t, pd_t, ua_t, us_t):
     err = torch.zeros(1, **i32)
     d = sdv.accept_desc(logits=logits_t, draft_tokens=drafts_t, temperature=temp_t,
                         u_accept=ua_t, u_sample=us_t, top_p=top_p_t, draft_probs=pd_t,
-                        dev_error=err, **out)
+                        dev_error=err, relaxed_topk=relaxed_topk_t,
+                        relaxed_delta=relaxed_delta_t, **out)
     sdv.accept(d)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in out.items()}

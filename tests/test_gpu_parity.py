@@ -232,6 +232,59 @@ def test_accept_stochastic(B, K, V, T, top_p, dtype):
     assert gpu["dev_error"] == 0
 
 
+@pytest.mark.parametrize("B,K,V,dtype", [(60, 4, 5000, "bf16"), (30, 3, 1031, "f32"),
+                                         (12, 5, 129280, "bf16")])
+def test_accept_relaxed(B, K, V, dtype):
+    """Relaxed greedy acceptance next to strict greedy and sampled requests,
+    plus a negative top-N and a NaN delta (both invalid).  Rows carry five
+    boosted tokens so that the top-N / delta filter keeps some of them and
+    drops others; drafts are mostly boosted tokens of the judging row."""
+    rng = np.random.default_rng(B + V)
+    Q = K + 1
+    lgf = rng.normal(0.0, 1.0, (B, Q, V))
+    boosted = np.stack([[rng.choice(V, 5, replace=False) for _ in range(Q)] for _ in range(B)])
+    for t, add in enumerate([8.0, 7.6, 7.2, 6.8, 6.0]):
+        np.put_along_axis(lgf, boosted[:, :, t:t + 1],
+                          np.take_along_axis(lgf, boosted[:, :, t:t + 1], -1) + add, -1)
+    lg = torch.tensor(lgf, dtype=torch.float32).to(sdsynth.torch_dtype(dtype))
+    lgh = host(lg)
+    drafts = np.where(rng.random((B, K)) < 0.75,
+                      boosted[:, :K, :][np.arange(B)[:, None], np.arange(K)[None, :],
+                                        rng.integers(0, 5, (B, K))],
+                      rng.integers(0, V, (B, K))).astype(np.int32)
+    modes = [(0, 0.0), (1, 0.3), (3, 0.1), (3, 0.3), (10, 0.6), (2, 0.05), (4, 0.2)]
+    rk = np.array([modes[b % len(modes)][0] for b in range(B)], np.int32)
+    rd = np.array([modes[b % len(modes)][1] for b in range(B)], np.float32)
+    temp = np.zeros(B, np.float32)
+    temp[5::8] = 0.8                      # sampled requests ignore the relaxed fields
+    rk[3] = -1                            # invalid: negative top-N
+    rd[4] = np.nan                        # invalid when that request is relaxed
+    rk[4] = 3
+    temp[3] = temp[4] = 0.0
+    if K > 1:
+        drafts[6, 1] = -1                 # a negative draft ends the chain
+    lf = oracle.bf16_to_f64(lgh) if dtype == "bf16" else lgh.astype(np.float64)
+    pd = sdsynth.draft_probs(lf[:, :K], B, 0.5, 0.8)
+    ua = sdsynth.philox_uniforms(B, B, Q, 0)
+    us = sdsynth.philox_uniforms(B, B, Q, 1)
+    ref = oracle.accept(lgh, drafts, temp, None, pd, ua, us, relaxed_topk=rk, relaxed_delta=rd)
+    gpu = run_accept(lg.to(DEV), torch.tensor(drafts, device=DEV), torch.tensor(temp, device=DEV),
+                     None, torch.tensor(pd, device=DEV), torch.tensor(ua, device=DEV),
+                     torch.tensor(us, device=DEV), torch.tensor(rk, device=DEV),
+                     torch.tensor(rd, device=DEV))
+    assert ref["n_invalid"] == 2
+    n_excl = compare_accept(gpu, ref, where=f"relaxed {dtype} V={V}")
+    assert n_excl <= B // 8
+    assert list(gpu["num_accepted"][[3, 4]]) == [-1, -1]
+    assert gpu["dev_error"] & sdv.SD_DERR_PARAM
+    relaxed = (rk > 0) & (temp == 0)
+    strict = oracle.accept(lgh, drafts, temp, None, pd, ua, us)
+    ok = ref["num_accepted"] >= 0
+    # The relaxed rule accepts at least as much as the strict one, and more here.
+    assert (ref["num_accepted"][relaxed & ok] >= strict["num_accepted"][relaxed & ok]).all()
+    assert ref["num_accepted"][relaxed & ok].sum() > strict["num_accepted"][relaxed & ok].sum()
+
+
 def test_accept_mixed_modes_and_invalid_requests():
     """Serving-style batch: even requests greedy, odd sampled at T=0.8, plus a
     NaN row, an out-of-range draft and a negative temperature."""
