@@ -31,6 +31,7 @@ constexpr int kPage = 64;
 // ---------------------------------------------------------------------------
 // Per-request checks and append, one block per (position i, request b).
 // Every block of a request takes the same decision; block i = 0 records it.
+// Blocks of an invalid request write its NaN output rows.
 // valid[b] = 1 when
 // 0 <= L_b <= max_seq_len, L_b + NQ <= max_pages * 64 and every page entry
 // covering 0 .. L_b+NQ-1 is a pool page.  Later kernels touch only valid
@@ -44,7 +45,9 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
                                      const uint8_t* __restrict__ v_new,
                                      uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                                      int NQ, int Hkv, int row_bytes_k, int row_bytes_v,
-                                     int max_pages, int num_pages, int max_seq_len, int mla) {
+                                     int max_pages, int num_pages, int max_seq_len, int mla,
+                                     float* __restrict__ out, void* __restrict__ out_lowp,
+                                     int lowp_f32, int Hq, int Dv) {
     const int i = blockIdx.x, b = blockIdx.y;
     const int L = seq_lens[b];
     const bool cap_ok =
@@ -64,7 +67,19 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
         if (!cap_ok) set_error(err, SD_DERR_CAPACITY);
         if (bad_page) set_error(err, SD_DERR_PAGE);
     }
-    if (!ok || !k_new) return;
+    if (!ok) {
+        // Invalid request: NaN output rows (the attention kernels skip it).
+        const size_t o0 = ((size_t)b * NQ + i) * Hq * Dv;
+        for (int e = threadIdx.x; e < Hq * Dv; e += blockDim.x) {
+            out[o0 + e] = NAN;
+            if (out_lowp) {
+                if (lowp_f32) ((float*)out_lowp)[o0 + e] = NAN;
+                else ((uint16_t*)out_lowp)[o0 + e] = 0x7fc0u;
+            }
+        }
+        return;
+    }
+    if (!k_new) return;
     const int nk = row_bytes_k / 16, nv = row_bytes_v / 16;
     {
         const long pos = (long)L + i;
@@ -465,7 +480,7 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         d->seq_lens, d->page_table, valid, d->dev_error, (const uint8_t*)d->k_new,
         (const uint8_t*)d->v_new, (uint8_t*)d->k_cache, (uint8_t*)d->v_cache, NQ, d->n_kv_heads,
         d->d_qk * es, d->d_v * es, d->max_pages, d->num_pages, d->max_seq_len,
-        d->kind == SD_ATTN_MLA);
+        d->kind == SD_ATTN_MLA, d->out, d->out_lowp, p.path == 1, d->n_q_heads, d->d_v);
     if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {

@@ -469,6 +469,21 @@ def test_attention_mla_bf16(B, K, Hq, lens):
     assert np.array_equal(bits(lowp), exp_lowp)
 
 
+def test_attention_mla_invalid_request_gets_nan():
+    """A request over capacity in the MLA path (one key chunk, so no combine
+    pass) is flagged and gets NaN rows; its neighbour is unaffected."""
+    wl = _mla_case(2, 3, 32, [40, 50], seed=77)
+    wl.seq_lens[1] = 10 ** 6
+    out, lowp, _, err = _run_gpu_mla(wl, max_seq_len=60)
+    o = out.cpu().numpy()
+    assert err & sdv.SD_DERR_CAPACITY
+    assert np.isnan(o[1]).all()
+    assert np.isnan(lowp.float().cpu().numpy().reshape(2, 4, -1)[1]).all()
+    wl.seq_lens[1] = 50
+    ref, _ = _oracle_mla(wl, sel=np.array([[0, i, h] for i in range(4) for h in range(32)]))
+    check_attention(o[0].reshape(-1, 512), ref, where="valid MLA request beside a faulty one")
+
+
 def test_attention_mla_full_config_sampled():
     """The MLA-shaped greedy configuration at full size (B=64, K=3, 128 heads,
     L=8192): every output of 8 requests' sampled rows against the oracle."""
