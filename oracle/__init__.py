@@ -3,8 +3,8 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
 package.  It wraps `liboracle.so` (built from `sd_oracle.c` by `build()`)
 with ctypes; it performs no arithmetic of its own beyond allocating outputs.
-Arrays are host numpy arrays: float32, float64, or uint16 holding bfloat16
-bit patterns.
+Arrays are host numpy arrays: float32, float64, uint16 holding bfloat16 bit
+patterns, or (FP8 KV caches) uint8 holding OCP E4M3 codes.
 """
 from __future__ import annotations
 
@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sd_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, E4M3 = 0, 1, 2, 3
 
 
 def build(verbose: bool = False) -> str:
@@ -59,6 +59,8 @@ def _dtype_code(a: np.ndarray) -> int:
         return F64
     if a.dtype == np.uint16:
         return BF16
+    if a.dtype == np.uint8:
+        return E4M3
     raise TypeError(f"unsupported oracle dtype {a.dtype}")
 
 
@@ -91,14 +93,46 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Exact value of OCP E4M3 (fn) codes (NaN for 0x7F / 0xFF)."""
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib().orc_e4m3_decode(_ptr(codes), _ptr(out), ctypes.c_size_t(codes.size))
+    return out
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """E4M3 code nearest to each fp64 value (ties to even, saturating at 448,
+    NaN -> 0x7F)."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_e4m3_encode(_ptr(x), _ptr(out), ctypes.c_size_t(x.size))
+    return out
+
+
 def kv_append(seq_lens, page_table, num_pages, k_new, v_new, k_cache, v_cache, *,
-              mla=False, page_size=64):
-    """In-place append of the step's K+1 keys/values into the cache copies."""
+              mla=False, page_size=64, k_scale=None, v_scale=None):
+    """In-place append of the step's K+1 keys/values into the cache copies.
+    uint8 caches hold E4M3 codes of value / scale[kv head] (k_scale, v_scale:
+    float32 [n_kv_heads])."""
     k_new = _c(k_new)
     v_new = _c(v_new)
     seq_lens = _c(seq_lens, np.int32)
     page_table = _c(page_table, np.int32)
     assert k_cache.flags["C_CONTIGUOUS"] and (v_cache is None or v_cache.flags["C_CONTIGUOUS"])
+    if k_cache.dtype == np.uint8:
+        assert not mla and v_cache.dtype == np.uint8
+        B, Q, Hkv, dk = k_new.shape
+        k_scale = _c(k_scale, np.float32)
+        v_scale = _c(v_scale, np.float32)
+        assert k_scale.shape == (Hkv,) and v_scale.shape == (Hkv,)
+        rc = lib().orc_kv_append_e4m3(
+            B, Q, Hkv, dk, v_new.shape[-1], page_size, page_table.shape[1], int(num_pages),
+            _dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(page_table), _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale))
+        if rc != 0:
+            raise ValueError(f"orc_kv_append_e4m3 failed ({rc})")
+        return
     if mla:
         B, Q, dk = k_new.shape
         Hkv, dv = 1, 0
@@ -114,9 +148,11 @@ def kv_append(seq_lens, page_table, num_pages, k_new, v_new, k_cache, v_cache, *
 
 
 def verify_attn(q, k_cache, v_cache, page_table, seq_lens, num_pages, *, n_kv_heads,
-                d_v, mla=False, page_size=64, scale=None, sel=None):
+                d_v, mla=False, page_size=64, scale=None, sel=None, k_scale=None,
+                v_scale=None):
     """fp64 attention outputs.  q: [B, Q, Hq, d_qk].  sel: optional int array
-    [n, 3] of (b, i, h).  Returns [B, Q, Hq, d_v] or [n, d_v] float64."""
+    [n, 3] of (b, i, h).  uint8 caches hold E4M3 codes scaled per kv head by
+    k_scale / v_scale.  Returns [B, Q, Hq, d_v] or [n, d_v] float64."""
     q = _c(q)
     B, Q, Hq, dqk = q.shape
     if scale is None:
@@ -131,11 +167,19 @@ def verify_attn(q, k_cache, v_cache, page_table, seq_lens, num_pages, *, n_kv_he
         out = np.empty((B, Q, Hq, d_v), dtype=np.float64)
         n_sel = 0
     dt = _dtype_code(q)
-    assert _dtype_code(k_cache) == dt
-    rc = lib().orc_verify_attn(
+    kdt = _dtype_code(k_cache)
+    if kdt == E4M3:
+        k_scale = _c(k_scale, np.float32)
+        v_scale = _c(v_scale, np.float32)
+        assert k_scale.shape == (n_kv_heads,) and v_scale.shape == (n_kv_heads,)
+    else:
+        assert kdt == dt
+        k_scale = v_scale = None
+    rc = lib().orc_verify_attn_ex(
         B, Q, Hq, n_kv_heads, dqk, d_v, int(mla), page_size, page_table.shape[1],
-        int(num_pages), ctypes.c_double(scale), dt, _ptr(q), _ptr(k_cache),
-        _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), n_sel, _ptr(sel), _ptr(out))
+        int(num_pages), ctypes.c_double(scale), dt, kdt, _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(seq_lens),
+        n_sel, _ptr(sel), _ptr(out))
     if rc != 0:
         raise ValueError(f"orc_verify_attn failed ({rc})")
     return out

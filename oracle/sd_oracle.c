@@ -36,7 +36,10 @@
  *     one-hot p_d this is p_t with the draft removed;
  *   - argmax ties go to the smallest token id;
  *   - top-p keeps the shortest prefix of (logit desc, id asc) whose tempered
- *     mass reaches top_p, extended to every token tied with its last logit.
+ *     mass reaches top_p, extended to every token tied with its last logit;
+ *   - an FP8 KV cache holds OCP E4M3 ("fn") codes with one key scale and one
+ *     value scale per kv head; appending stores the nearest code (ties to
+ *     even, saturating at 448, NaN kept) of value / scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -46,7 +49,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_E4M3 = 3 };
 enum { ORC_OK = 0, ORC_EARG = 1, ORC_EPAGE = 2 };
 
 int orc_num_threads(void) {
@@ -65,10 +68,61 @@ void orc_set_num_threads(int n) {
 #endif
 }
 
-/* Element i of an array stored as float32, bfloat16 bits, or float64. */
+/* ------------------------------------------------------------------------
+ * FP8 cache codes: the OCP 8-bit floating-point format E4M3 in its "fn"
+ * variant (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; 0x7F and 0xFF are NaN, so the largest finite value is
+ * 1.75 * 2^8 = 448; exponent field 0 holds the subnormals m/8 * 2^-6).
+ * The pages name FP8 attention only as prior art ([TRT-MTP] "支持 MTP 的注意力
+ * 機制": FP8 FlashMLA); the cache format is this reading of it.  A cached
+ * element stands for code_value * scale[kv head], with one scale for keys
+ * and one for values per kv head.
+ * ---------------------------------------------------------------------- */
+double orc_e4m3_value(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Code of x: NaN -> 0x7F; otherwise the sign bit of x and the code of the
+ * representable magnitude nearest to min(|x|, 448) (saturation), ties to the
+ * code with an even mantissa, found by trying every finite magnitude code
+ * 0x00 .. 0x7E (their values increase with the code). */
+uint8_t orc_e4m3_code(double x) {
+    if (isnan(x)) return 0x7F;
+    double a = fabs(x);
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double err = fabs(orc_e4m3_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)((signbit(x) ? 0x80 : 0) | best);
+}
+
+void orc_e4m3_decode(const uint8_t* codes, double* out, size_t n) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_e4m3_value(codes[i]);
+}
+
+void orc_e4m3_encode(const double* x, uint8_t* out, size_t n) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_e4m3_code(x[i]);
+}
+
+/* Element i of an array stored as float32, bfloat16 bits, float64, or E4M3
+ * codes (the code's value; a cache scale is applied by the caller). */
 static double load_elem(const void* p, int dtype, size_t i) {
     if (dtype == ORC_F32) return (double)((const float*)p)[i];
     if (dtype == ORC_F64) return ((const double*)p)[i];
+    if (dtype == ORC_E4M3) return orc_e4m3_value(((const uint8_t*)p)[i]);
     uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -76,7 +130,7 @@ static double load_elem(const void* p, int dtype, size_t i) {
 }
 
 static size_t elem_size(int dtype) {
-    return dtype == ORC_F32 ? 4 : dtype == ORC_F64 ? 8 : 2;
+    return dtype == ORC_F32 ? 4 : dtype == ORC_F64 ? 8 : dtype == ORC_E4M3 ? 1 : 2;
 }
 
 /* ------------------------------------------------------------------------
@@ -178,6 +232,40 @@ int orc_kv_append(int B, int Q, int n_kv_heads, int d_k, int d_v, int mla, int p
 }
 
 /*
+ * Append into an FP8 (E4M3) cache: as orc_kv_append, but element d of new
+ * row (b, i, h) is stored as the code of value / scale[h] (k_scale for keys,
+ * v_scale for values), so that code_value * scale is the nearest the cache
+ * can hold to the new value.  new_dtype is the type of k_new/v_new.
+ */
+int orc_kv_append_e4m3(int B, int Q, int n_kv_heads, int d_k, int d_v, int page_size,
+                       int max_pages, int num_pages, int new_dtype, const void* k_new,
+                       const void* v_new, uint8_t* k_cache, uint8_t* v_cache,
+                       const int* page_table, const int* seq_lens, const float* k_scale,
+                       const float* v_scale) {
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < Q; ++i) {
+            long pos = (long)seq_lens[b] + i;
+            long pg = phys_page(page_table, max_pages, num_pages, b, pos, page_size);
+            if (pg < 0) return ORC_EPAGE;
+            long off = pos % page_size;
+            for (int h = 0; h < n_kv_heads; ++h) {
+                for (int d = 0; d < d_k; ++d) {
+                    size_t src = (((size_t)b * Q + i) * n_kv_heads + h) * d_k + d;
+                    k_cache[gqa_index(pg, h, n_kv_heads, page_size, off, d_k, d)] =
+                        orc_e4m3_code(load_elem(k_new, new_dtype, src) / (double)k_scale[h]);
+                }
+                for (int d = 0; d < d_v; ++d) {
+                    size_t src = (((size_t)b * Q + i) * n_kv_heads + h) * d_v + d;
+                    v_cache[gqa_index(pg, h, n_kv_heads, page_size, off, d_v, d)] =
+                        orc_e4m3_code(load_elem(v_new, new_dtype, src) / (double)v_scale[h]);
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/*
  * Verify attention for the K+1 queries of each request, over a cache that
  * already holds the appended positions.  Query i of request b and head h
  * attends to keys 0 .. L_b+i (a causal mask over the K+1 new positions,
@@ -189,14 +277,18 @@ int orc_kv_append(int B, int Q, int n_kv_heads, int d_k, int d_v, int mla, int p
  * MLA: one latent vector per position; k_p = latent[0:d_qk] and
  * v_p = latent[0:d_v].
  *
+ * FP8 cache (kv_dtype ORC_E4M3, GQA): k_p = code_value * k_scale[kv head] and
+ * v_p = code_value * v_scale[kv head], elementwise; q stays in `dtype`.
+ *
  * sel: n_sel triples (b, i, h) to evaluate, or NULL for every (b, i, h) in
  * that order.  out: [n_sel][d_v] doubles.
  */
-int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
-                    int page_size, int max_pages, int num_pages, double scale, int dtype,
-                    const void* q, const void* k_cache, const void* v_cache,
-                    const int* page_table, const int* seq_lens, int n_sel, const int* sel,
-                    double* out) {
+int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
+                       int page_size, int max_pages, int num_pages, double scale, int dtype,
+                       int kv_dtype, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int* page_table,
+                       const int* seq_lens, int n_sel, const int* sel, double* out) {
+    if (kv_dtype == ORC_E4M3 && (mla || !k_scale || !v_scale)) return ORC_EARG;
     long total = sel ? n_sel : (long)B * Q * Hq;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
@@ -218,6 +310,8 @@ int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
         }
         long n = (long)seq_lens[b] + i + 1;  /* keys 0 .. L_b + i */
         int kvh = mla ? 0 : (int)((long)h * Hkv / Hq);
+        double ks = kv_dtype == ORC_E4M3 ? (double)k_scale[kvh] : 1.0;
+        double vs = kv_dtype == ORC_E4M3 ? (double)v_scale[kvh] : 1.0;
         double* sc = (double*)malloc(sizeof(double) * (size_t)n);
         size_t qoff = (((size_t)b * Q + i) * Hq + h) * d_qk;
         double m = -INFINITY;
@@ -233,7 +327,7 @@ int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
             for (int d = 0; d < d_qk; ++d) {
                 size_t ki = mla ? ((size_t)pg * page_size + off) * d_qk + d
                                 : gqa_index(pg, kvh, Hkv, page_size, off, d_qk, d);
-                acc += load_elem(q, dtype, qoff + d) * load_elem(k_cache, dtype, ki);
+                acc += load_elem(q, dtype, qoff + d) * (load_elem(k_cache, kv_dtype, ki) * ks);
             }
             sc[p] = scale * acc;
             if (sc[p] > m) m = sc[p];
@@ -251,13 +345,23 @@ int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
             for (int d = 0; d < d_v; ++d) {
                 size_t vi = mla ? ((size_t)pg * page_size + off) * d_qk + d
                                 : gqa_index(pg, kvh, Hkv, page_size, off, d_v, d);
-                o[d] += sc[p] * load_elem(mla ? k_cache : v_cache, dtype, vi);
+                o[d] += sc[p] * (load_elem(mla ? k_cache : v_cache, kv_dtype, vi) * vs);
             }
         }
         for (int d = 0; d < d_v; ++d) o[d] /= denom;
         free(sc);
     }
     return bad ? ORC_EPAGE : ORC_OK;
+}
+
+int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
+                    int page_size, int max_pages, int num_pages, double scale, int dtype,
+                    const void* q, const void* k_cache, const void* v_cache,
+                    const int* page_table, const int* seq_lens, int n_sel, const int* sel,
+                    double* out) {
+    return orc_verify_attn_ex(B, Q, Hq, Hkv, d_qk, d_v, mla, page_size, max_pages, num_pages,
+                              scale, dtype, dtype, q, k_cache, v_cache, NULL, NULL, page_table,
+                              seq_lens, n_sel, sel, out);
 }
 
 /*
