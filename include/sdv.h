@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 2
+#define SD_ABI_VERSION 3
 
 /* status codes */
 #define SD_OK 0
@@ -66,6 +66,11 @@ extern "C" {
 /* element types */
 #define SD_F32 0
 #define SD_BF16 1
+#define SD_E4M3 2   /* OCP 8-bit float E4M3, "fn" variant (KV caches only) */
+
+/* KV cache formats (sd_attn_desc.kv_format) */
+#define SD_KV_AS_DTYPE 0   /* k_cache / v_cache hold `dtype` elements */
+#define SD_KV_E4M3 1       /* k_cache / v_cache hold SD_E4M3 codes, scaled per kv head */
 
 /* attention layouts */
 #define SD_ATTN_GQA 0
@@ -120,9 +125,25 @@ const char* sd_last_error(void);
  *              [B*(K+1)][n_q_heads*d_v] (ready as LM-head input); may be NULL
  * A request with a capacity or page-table fault gets NaN outputs.
  *
- * Supported: page_size 64; GQA bf16 with d_qk = d_v in {64, 128} and
- * (n_q_heads/n_kv_heads)*(K+1) <= 64; GQA f32 with d_qk = d_v <= 256;
- * MLA bf16 with d_qk = 576, d_v = 512.  Others return SD_EUNSUPPORTED.
+ * FP8 KV cache (kv_format = SD_KV_E4M3; GQA with dtype SD_BF16 only).  The
+ * pages name FP8 attention kernels as prior art for this step ([TRT-MTP]
+ * "支持 MTP 的注意力機制"); the format here is OCP E4M3 ("fn": bias 7, no
+ * infinities, 0x7F/0xFF NaN, largest finite 448), one byte per element in
+ * the same [num_pages][n_kv_heads][page_size][d] layouts.  Element d of kv
+ * head h stands for value(code) * k_scale[h] (keys) or value(code) *
+ * v_scale[h] (values); k_scale, v_scale: device float32 [n_kv_heads],
+ * positive and finite (other values are the caller's error: outputs are
+ * then meaningless, but no access leaves the buffers).  The append stores
+ * the code nearest to bf16_value / scale[h] (float32 division, correctly
+ * rounded; ties to the even code; magnitudes above 448, infinities
+ * included, saturate to 448; NaN -> 0x7F).  q, k_new, v_new, out_lowp stay
+ * bf16.  The attention computes with the exact code values (every E4M3
+ * value is a bf16 value) and applies the scales in float32.
+ *
+ * Supported: page_size 64; GQA bf16 (bf16 or E4M3 cache) with d_qk = d_v in
+ * {64, 128} and (n_q_heads/n_kv_heads)*(K+1) <= 64; GQA f32 with d_qk = d_v
+ * <= 256; MLA bf16 with d_qk = 576, d_v = 512.  Others return
+ * SD_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct sd_attn_desc {
     int batch;
@@ -148,6 +169,9 @@ typedef struct sd_attn_desc {
     float* out;
     void* out_lowp;
     int32_t* dev_error; /* optional */
+    int kv_format;          /* SD_KV_AS_DTYPE (0) or SD_KV_E4M3 */
+    const float* k_scale;   /* SD_KV_E4M3: device [n_kv_heads]; else unread */
+    const float* v_scale;   /* SD_KV_E4M3: device [n_kv_heads]; else unread */
 } sd_attn_desc;
 
 /* Bytes of device workspace sd_verify_attn needs for this descriptor
@@ -279,7 +303,9 @@ int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* s
  *   poison_rejected: when non-zero, the rejected slots of k_cache/v_cache
  *                    (every kv head; the latent row for MLA) are zeroed;
  *                    kind, dtype, n_kv_heads, d_k, d_v describe the caches
- *                    exactly as in sd_attn_desc and are read only then.
+ *                    as in sd_attn_desc (dtype = the cache element type:
+ *                    SD_F32, SD_BF16, or SD_E4M3 for an FP8 cache, whose
+ *                    zero code is +0) and are read only then.
  * The page table itself is left unchanged: the caller returns freed pages
  * to its pool.
  * ---------------------------------------------------------------------- */

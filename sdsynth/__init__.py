@@ -101,7 +101,7 @@ def philox_uniforms(seed: int, rows: int, cols: int, stream: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 _TAGS = {
     "q": 1, "k_new": 2, "v_new": 3, "k_cache": 4, "v_cache": 5, "H": 6, "W": 7,
-    "pages": 8, "seq_lens": 9, "noise": 10, "modes": 11, "kv_new": 12,
+    "pages": 8, "seq_lens": 9, "noise": 10, "modes": 11, "kv_new": 12, "kv_scale": 13,
 }
 
 
@@ -177,6 +177,7 @@ class Config:
     page_size: int = 64
     draft_noise: float = 0.5
     geom_p: float = 0.4
+    kv_cache: str = "as_dtype"  # or "e4m3": FP8 cache codes with per-kv-head scales
 
     @property
     def num_q(self) -> int:
@@ -267,10 +268,26 @@ def make_workload(cfg: Config, seed: int, device="cpu", extra_tokens: int = 0,
         else:
             t["k_new"] = normal((B, Q, cfg.n_kv_heads, cfg.d_qk), 1.0, seed, "k_new", dt, device)
             t["v_new"] = normal((B, Q, cfg.n_kv_heads, cfg.d_v), 1.0, seed, "v_new", dt, device)
-            t["k_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_qk), 1.0,
-                                  seed, "k_cache", dt, device)
-            t["v_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_v), 1.0,
-                                  seed, "v_cache", dt, device)
+            if cfg.kv_cache == "e4m3":
+                # Codes: torch's float8_e4m3fn cast of N(0, 32^2) draws, stored as
+                # bytes; scales ~1/32 per kv head, so the cached values are
+                # roughly N(0, 1) like the bf16 cache.
+                f8 = torch.float8_e4m3fn
+                t["k_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_qk), 32.0,
+                                      seed, "k_cache", f8, device).view(torch.uint8)
+                t["v_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_v), 32.0,
+                                      seed, "v_cache", f8, device).view(torch.uint8)
+                rng = np.random.default_rng(seed * 7919 + _TAGS["kv_scale"])
+                sc = ((0.75 + 0.5 * rng.random((2, cfg.n_kv_heads))) / 32.0).astype(np.float32)
+                t["k_scale"] = torch.from_numpy(sc[0].copy()).to(device)
+                t["v_scale"] = torch.from_numpy(sc[1].copy()).to(device)
+            elif cfg.kv_cache == "as_dtype":
+                t["k_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_qk), 1.0,
+                                      seed, "k_cache", dt, device)
+                t["v_cache"] = normal((num_pages, cfg.n_kv_heads, cfg.page_size, cfg.d_v), 1.0,
+                                      seed, "v_cache", dt, device)
+            else:
+                raise ValueError(f"unknown kv_cache {cfg.kv_cache!r}")
     if with_lm_head:
         if not cfg.chain_attn_to_lm_head:
             # Stand-in for the normalised hidden state that feeds the output layer.

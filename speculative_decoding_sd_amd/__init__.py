@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdv.so")
 
 SD_OK, SD_EINVAL, SD_EUNSUPPORTED, SD_EWORKSPACE, SD_EDEVICE = 0, 1, 2, 3, 4
-SD_F32, SD_BF16 = 0, 1
+SD_F32, SD_BF16, SD_E4M3 = 0, 1, 2
+SD_KV_AS_DTYPE, SD_KV_E4M3 = 0, 1
 SD_ATTN_GQA, SD_ATTN_MLA = 0, 1
 SD_DERR_PAGE, SD_DERR_CAPACITY, SD_DERR_TOKEN = 1, 2, 4
 SD_DERR_NONFINITE, SD_DERR_PARAM, SD_DERR_ACCEPT_COUNT = 8, 16, 32
@@ -41,6 +42,7 @@ class AttnDesc(ctypes.Structure):
         ("num_pages", _I), ("max_seq_len", _I), ("softmax_scale", ctypes.c_float),
         ("q", _P), ("k_new", _P), ("v_new", _P), ("k_cache", _P), ("v_cache", _P),
         ("page_table", _P), ("seq_lens", _P), ("out", _P), ("out_lowp", _P), ("dev_error", _P),
+        ("kv_format", _I), ("k_scale", _P), ("v_scale", _P),
     ]
 
 
@@ -154,6 +156,8 @@ def sd_dtype(t) -> int:
         return SD_BF16
     if t.dtype == torch.float32:
         return SD_F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return SD_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -184,18 +188,23 @@ def _keeping(tensors, desc):
 
 def attn_desc(*, q, k_cache, v_cache, page_table, seq_lens, out, n_kv_heads, num_pages,
               max_seq_len, k_new=None, v_new=None, mla=False, out_lowp=None,
-              softmax_scale=0.0, dev_error=None, page_size=64) -> AttnDesc:
+              softmax_scale=0.0, dev_error=None, page_size=64, k_scale=None,
+              v_scale=None) -> AttnDesc:
+    """Caches of dtype uint8 or float8_e4m3fn hold E4M3 codes and take float32
+    per-kv-head k_scale / v_scale."""
     B, NQ, Hq, dqk = q.shape
     d_v = out.shape[-1]
+    fp8 = sd_dtype(k_cache) == SD_E4M3
     return _keeping((q, k_cache, v_cache, page_table, seq_lens, out, k_new, v_new, out_lowp,
-                     dev_error), AttnDesc(
+                     dev_error, k_scale, v_scale), AttnDesc(
         batch=B, num_q=NQ, n_q_heads=Hq, n_kv_heads=n_kv_heads, d_qk=dqk, d_v=d_v,
         kind=SD_ATTN_MLA if mla else SD_ATTN_GQA, dtype=sd_dtype(q), page_size=page_size,
         max_pages=page_table.shape[1], num_pages=num_pages, max_seq_len=max_seq_len,
         softmax_scale=softmax_scale, q=_ptr(q), k_new=_ptr(k_new), v_new=_ptr(v_new),
         k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), page_table=_ptr(page_table),
         seq_lens=_ptr(seq_lens), out=_ptr(out), out_lowp=_ptr(out_lowp),
-        dev_error=_ptr(dev_error)))
+        dev_error=_ptr(dev_error), kv_format=SD_KV_E4M3 if fp8 else SD_KV_AS_DTYPE,
+        k_scale=_ptr(k_scale) if fp8 else None, v_scale=_ptr(v_scale) if fp8 else None))
 
 
 def verify_attn(desc: AttnDesc, ws=None, stream=None):

@@ -9,7 +9,8 @@
 //   attn_validate_append  per request: capacity and page-table entries
 //                   (flags), then the K+1 new keys/values -> cache positions
 //                   L_b .. L_b+K
-//   GQA, bf16:      attn_items (prefix sum of the requests' key chunks) and
+//   GQA, bf16 q with a bf16 or E4M3 cache:
+//                   attn_items (prefix sum of the requests' key chunks) and
 //                   attn_gqa_stream (attn_gqa.hip): persistent waves stream
 //                   (kv head, request, chunk) items through LDS rings; every
 //                   query row of the kv head's group shares each K/V tile, so
@@ -37,7 +38,36 @@ constexpr int kPage = 64;
 // covering 0 .. L_b+NQ-1 is a pool page.  Later kernels touch only valid
 // requests.  Then (k_new given) row i of k_new / v_new goes to position
 // L_b + i with 16-byte copies; MLA copies the latent row into k_cache only.
+// With an E4M3 cache (k_scale given) each bf16 element is stored as the code
+// nearest to value / scale[kv head] instead, eight elements per thread.
 // ---------------------------------------------------------------------------
+
+// E4M3 ("fn") code of y: round to nearest, ties to even, magnitudes at or
+// above 448 (infinities included) saturate to 448, NaN -> 0x7F.  Normal
+// range: the float's exponent and top three mantissa bits, rounded on the
+// 20 bits dropped (a carry moves into the exponent); below 2^-6 the codes
+// are the multiples of 2^-9, code 8 being 2^-6 itself.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;
+    const float m = __uint_as_float(a);
+    if (m >= 448.f) return sign | 0x7eu;
+    if (m < 0.015625f) return sign | (uint32_t)__builtin_rintf(m * 512.f);
+    return sign | (((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3));
+}
+
+// Eight bf16 (one 16-byte load) -> eight codes of value / s (8 bytes).
+__device__ __forceinline__ u32x2 e4m3_pack8(u32x4 src, float s) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (src[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        w[e >> 2] |= e4m3_code(bf16_to_f32(h) / s) << (8 * (e & 3));
+    }
+    return u32x2{w[0], w[1]};
+}
+
 __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
                                      const int32_t* __restrict__ page_table,
                                      int32_t* __restrict__ valid, int32_t* err,
@@ -47,7 +77,9 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
                                      int NQ, int Hkv, int row_bytes_k, int row_bytes_v,
                                      int max_pages, int num_pages, int max_seq_len, int mla,
                                      float* __restrict__ out, void* __restrict__ out_lowp,
-                                     int lowp_f32, int Hq, int Dv) {
+                                     int lowp_f32, int Hq, int Dv,
+                                     const float* __restrict__ k_scale,
+                                     const float* __restrict__ v_scale) {
     const int i = blockIdx.x, b = blockIdx.y;
     const int L = seq_lens[b];
     const bool cap_ok =
@@ -85,6 +117,26 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
         const long pos = (long)L + i;
         const long pg = page_table[(size_t)b * max_pages + pos / kPage];
         const long off = pos % kPage;
+        if (k_scale) {
+            // E4M3 cache: row_bytes_* are the cache rows (one byte per
+            // element); the new rows are bf16, twice as long.
+            const int n8k = row_bytes_k / 8, n8v = row_bytes_v / 8;
+            for (int idx = threadIdx.x; idx < Hkv * n8k; idx += blockDim.x) {
+                const int h = idx / n8k, c = idx - h * n8k;
+                const u32x4 src = ((const u32x4*)(k_new + (((size_t)b * NQ + i) * Hkv + h) *
+                                                              2 * row_bytes_k))[c];
+                ((u32x2*)(k_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_k))[c] =
+                    e4m3_pack8(src, k_scale[h]);
+            }
+            for (int idx = threadIdx.x; idx < Hkv * n8v; idx += blockDim.x) {
+                const int h = idx / n8v, c = idx - h * n8v;
+                const u32x4 src = ((const u32x4*)(v_new + (((size_t)b * NQ + i) * Hkv + h) *
+                                                              2 * row_bytes_v))[c];
+                ((u32x2*)(v_cache + (((size_t)pg * Hkv + h) * kPage + off) * row_bytes_v))[c] =
+                    e4m3_pack8(src, v_scale[h]);
+            }
+            return;
+        }
         if (mla) {
             const u32x4* src = (const u32x4*)(k_new + ((size_t)b * NQ + i) * row_bytes_k);
             u32x4* dst = (u32x4*)(k_cache + ((size_t)pg * kPage + off) * row_bytes_k);
@@ -365,6 +417,11 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         return fail(SD_EINVAL, "sd_verify_attn: unknown dtype %d", d->dtype);
     if (d->kind != SD_ATTN_GQA && d->kind != SD_ATTN_MLA)
         return fail(SD_EINVAL, "sd_verify_attn: unknown kind %d", d->kind);
+    if (d->kv_format != SD_KV_AS_DTYPE && d->kv_format != SD_KV_E4M3)
+        return fail(SD_EINVAL, "sd_verify_attn: unknown kv_format %d", d->kv_format);
+    if (d->kv_format == SD_KV_E4M3 &&
+        (d->kind != SD_ATTN_GQA || d->dtype != SD_BF16))
+        return fail(SD_EUNSUPPORTED, "sd_verify_attn: an E4M3 cache needs GQA with bf16 q");
     if (d->n_q_heads % d->n_kv_heads != 0)
         return fail(SD_EINVAL, "sd_verify_attn: n_q_heads %% n_kv_heads != 0");
     if (d->page_size != kPage)
@@ -460,6 +517,9 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         return fail(SD_EINVAL, "sd_verify_attn: GQA needs v_cache (and v_new with k_new)");
     if (d->kind == SD_ATTN_MLA && (d->v_cache || d->v_new))
         return fail(SD_EINVAL, "sd_verify_attn: MLA takes the latent in k_cache/k_new only");
+    const bool fp8 = d->kv_format == SD_KV_E4M3;
+    if (fp8 && (!d->k_scale || !d->v_scale))
+        return fail(SD_EINVAL, "sd_verify_attn: an E4M3 cache needs k_scale and v_scale");
     if (!aligned16(d->q) || !aligned16(d->k_cache) || (d->v_cache && !aligned16(d->v_cache)) ||
         (d->k_new && !aligned16(d->k_new)) || (d->v_new && !aligned16(d->v_new)) ||
         (d->out_lowp && !aligned16(d->out_lowp)) || !aligned16(d->out))
@@ -468,7 +528,7 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         return fail(SD_EINVAL, "sd_verify_attn: workspace NULL or not 256-byte aligned");
     if (ws_bytes < p.total)
         return fail(SD_EWORKSPACE, "sd_verify_attn: workspace %zu < %zu bytes", ws_bytes, p.total);
-    const int es = d->dtype == SD_BF16 ? 2 : 4;
+    const int es = fp8 ? 1 : d->dtype == SD_BF16 ? 2 : 4;  // cache element bytes
     if ((d->d_qk * es) % 16 != 0 || (d->d_v * es) % 16 != 0)
         return fail(SD_EUNSUPPORTED, "sd_verify_attn: head rows must be multiples of 16 bytes");
 
@@ -480,7 +540,8 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         d->seq_lens, d->page_table, valid, d->dev_error, (const uint8_t*)d->k_new,
         (const uint8_t*)d->v_new, (uint8_t*)d->k_cache, (uint8_t*)d->v_cache, NQ, d->n_kv_heads,
         d->d_qk * es, d->d_v * es, d->max_pages, d->num_pages, d->max_seq_len,
-        d->kind == SD_ATTN_MLA, d->out, d->out_lowp, p.path == 1, d->n_q_heads, d->d_v);
+        d->kind == SD_ATTN_MLA, d->out, d->out_lowp, p.path == 1, d->n_q_heads, d->d_v,
+        fp8 ? d->k_scale : nullptr, fp8 ? d->v_scale : nullptr);
     if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {

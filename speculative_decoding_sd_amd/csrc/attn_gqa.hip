@@ -33,10 +33,10 @@ constexpr int kPage = 64;
 constexpr int kTile = 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
-template <int D>
+template <int D, bool F8>
 struct GqaTile {
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kRowChunks = D / 8;
+    static constexpr int kRowBytes = D * (F8 ? 1 : 2);
+    static constexpr int kRowChunks = kRowBytes / 16;
     static constexpr int kHalfBytes = kTile * kRowBytes;  // the K (or V) rows of a tile
     static constexpr int kDmaHalf = kHalfBytes / 1024;    // 1 KiB DMA ops per half tile
     static constexpr int kKStages = 3, kVStages = 2;      // K runs one tile further ahead
@@ -56,10 +56,39 @@ struct GqaTile {
 // rows, row parity picks the bank half): f(row) = 4((row/2)%2) + (row/4)%4, a
 // bijection on the 8 rows of one parity in a 16-row group, whose bit 2
 // differs between rows r and r+2.
-template <int D>
+// E4M3 tiles (one byte per element; V read by ds_read_b64_tr_b8, a pass
+// covering 8 rows x 2 chunks 2c, 2c+1: rows r0 + {0..3, 8..11}):
+// D = 128 (128-byte rows, row parity picks the bank half): with
+// x = (row/2)%8, f takes bit 2 from x's bit 2, bit 1 from x's bit 0 and bit 0
+// from x's bit 1 -- a bijection on x (K passes), and the four rows of one
+// parity in a V pass (x = x0 + {0, 1, 4, 5}) differ in bits 2:1 of f, which
+// the chunk pair's bit 0 does not touch.  D = 64 (64-byte rows, row%4 picks
+// the bank quarter): f = (row/4)%4, a bijection on the 4 rows of one class in
+// a 16-row group, differing in bit 1 between rows r and r+8.
+template <int D, bool F8>
 __device__ __forceinline__ int gqa_xor(int row) {
-    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    if constexpr (F8) {
+        if constexpr (D == 128) {
+            const int x = (row >> 1) & 7;
+            return (x & 4) | ((x & 1) << 1) | ((x >> 1) & 1);
+        } else {
+            return (row >> 2) & 3;
+        }
+    } else if constexpr (D == 128) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    }
+}
+
+// Eight E4M3 codes (bytes 0..7 of w, lowest first) -> eight bf16 in operand
+// order, exactly (every E4M3 value is a bf16 value; scale 1).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    return u32x4{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
 // Work items are (kv head, request, key chunk) triples of non-empty chunks,
@@ -122,15 +151,16 @@ __device__ __forceinline__ void cursor_next(ItemCursor& c, int NRC, int NQ, int 
     cursor_fill(c, NQ, chunk, seq_lens);
 }
 
-template <int D, int RB>
+template <int D, int RB, bool F8>
 __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ first,
     float* __restrict__ part_o, float2* __restrict__ part_ml, float* __restrict__ out,
     uint16_t* __restrict__ out_lowp, int B, int NQ, int Hq, int Hkv, int G, int R, int max_pages,
-    int chunk, int max_splits, float scale_log2) {
-    using T = GqaTile<D>;
+    int chunk, int max_splits, float scale_log2, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+    using T = GqaTile<D, F8>;
     constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-dim blocks of O^T
     __shared__ __attribute__((aligned(1024))) char s_ring[4][T::kRingBytes];
@@ -149,9 +179,9 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     for (int j = 0; j < T::kDmaHalf; ++j) {
         const int n = 64 * j + lane;
         const int row = n / T::kRowChunks;
-        goff[j] = row * D + 8 * ((n % T::kRowChunks) ^ gqa_xor<D>(row));
+        goff[j] = row * T::kRowBytes + 16 * ((n % T::kRowChunks) ^ gqa_xor<D, F8>(row));
     }
-    const size_t head_elems = (size_t)kPage * D;
+    const size_t head_bytes = (size_t)kPage * T::kRowBytes;
     char* const k_ring = ring;
     char* const v_ring = ring + T::kKStages * T::kHalfBytes;
     // The page-table entry of a DMA cursor's tile is read when the cursor
@@ -161,10 +191,10 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         if (c.item < c.hi)
             c.pg = page_table[(size_t)c.b * max_pages + (c.start + kTile * c.t) / kPage];
     };
-    auto issue = [&](const uint16_t* __restrict__ cache, const ItemCursor& c, const char* dst_p) {
+    auto issue = [&](const char* __restrict__ cache, const ItemCursor& c, const char* dst_p) {
         const int ks = c.start + kTile * c.t;
-        const uint16_t* src =
-            cache + ((size_t)c.pg * Hkv + c.kvh) * head_elems + (size_t)(ks % kPage) * D;
+        const char* src = cache + ((size_t)c.pg * Hkv + c.kvh) * head_bytes +
+                          (size_t)(ks % kPage) * T::kRowBytes;
         const uint32_t dst = lds_byte_addr(dst_p);
         // The stage's previous tile was read by this wave's ds_reads; make
         // sure they have returned before the DMA may overwrite it.
@@ -175,22 +205,42 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     };
 
     // Per-lane LDS byte offsets within a half tile.
-    //  K reads of k-step s: row ln, logical chunk 2s + lh.
-    int koff[NS];
+    //  K reads of k-step s: row ln, logical chunk 2s + lh (bf16); E4M3: one
+    //  read per k-step pair j = s/2, logical chunk 2j + lh (dims 32j + 16lh
+    //  .. +15), its bytes 0-7 for step 2j and 8-15 for step 2j+1 -- the
+    //  contraction runs over the dims in that order, and Q follows it.
+    constexpr int NKR = F8 ? NS / 2 : NS;
+    int koff[NKR];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) koff[s] = ln * T::kRowBytes + 16 * ((2 * s + lh) ^ gqa_xor<D>(ln));
+    for (int s = 0; s < NKR; ++s)
+        koff[s] = ln * T::kRowBytes + 16 * ((2 * s + lh) ^ gqa_xor<D, F8>(ln));
     //  V reads (16-lane group g, lane sl) of dim block db, half h: key
     //  16tt + 4(g/2) + sl/4 + 8h, logical chunk 4db + 2(g&1) + (sl&3)/2, byte
     //  8(sl&1) of the chunk (the swizzle depends on the key only modulo 16).
+    //  E4M3 (ds_read_b64_tr_b8: in each 16-lane group, lane t receives byte
+    //  t%8 of the 8-byte reads of lanes t/8 + 2e, e = 0..7): lane sl reads
+    //  key 16tt + 8(e/4) + 4(g/2) + e%4 with e = sl/2, bytes 16(g&1) + 8(sl&1)
+    //  .. +7 of dim block db, so lane t receives its dim's 8 keys in operand
+    //  slot order.
     const int g4 = lane >> 4, sl = lane & 15;
-    const int vch = 2 * (g4 & 1) + ((sl & 3) >> 1);
-    int voff[NDB][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int vr = 4 * (g4 >> 1) + (sl >> 2) + 8 * h;
+    int voff[NDB][F8 ? 1 : 2];
+    if constexpr (F8) {
+        const int e = sl >> 1;
+        const int vr = 8 * (e >> 2) + 4 * (g4 >> 1) + (e & 3);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-            voff[db][h] = vr * T::kRowBytes + 16 * ((4 * db + vch) ^ gqa_xor<D>(vr)) + 8 * (sl & 1);
+            voff[db][0] = vr * T::kRowBytes + 16 * ((2 * db + (g4 & 1)) ^ gqa_xor<D, F8>(vr)) +
+                          8 * (sl & 1);
+    } else {
+        const int vch = 2 * (g4 & 1) + ((sl & 3) >> 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int vr = 4 * (g4 >> 1) + (sl >> 2) + 8 * h;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                voff[db][h] = vr * T::kRowBytes + 16 * ((4 * db + vch) ^ gqa_xor<D, F8>(vr)) +
+                              8 * (sl & 1);
+        }
     }
 
     // Three cursors over the wave's tile stream: K DMA (three tiles ahead of
@@ -243,6 +293,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     u32x4 qf[RB][NS];
     int lim[RB];
     float m_r[RB], l_r[RB];
+    float sl2 = scale_log2, vsc = 1.f;  // per pair: key scale folded in; value scale
     f32x16 o[RB][NDB];
     // Consecutive chunks of one (request, kv head) form a segment: the online
     // softmax state and Q carry over from chunk to chunk, and the segment is
@@ -256,16 +307,22 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             seg_b = cc.b;
             seg_kvh = cc.kvh;
             seg_split0 = cc.split;
-            // New item: Q fragments (B operand; column = query row, k = d).
+            if constexpr (F8) {
+                sl2 = scale_log2 * k_scale[cc.kvh];
+                vsc = v_scale[cc.kvh];
+            }
+            // New item: Q fragments (B operand; column = query row, k = d;
+            // E4M3: the dims of k-step s are 32(s/2) + 16lh + 8(s%2) .. +7).
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int row = rb * 32 + ln;
                 if (row < R) {
                     const int i = row / G, gq = row - i * G;
-                    const uint16_t* qp =
-                        q + (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D + 8 * lh;
+                    const uint16_t* qp = q + (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D +
+                                         (F8 ? 16 : 8) * lh;
 #pragma unroll
-                    for (int s = 0; s < NS; ++s) qf[rb][s] = *(const u32x4*)(qp + 16 * s);
+                    for (int s = 0; s < NS; ++s)
+                        qf[rb][s] = *(const u32x4*)(qp + (F8 ? 32 * (s >> 1) + 8 * (s & 1) : 16 * s));
                     lim[rb] = cc.L + i;  // causal: keys 0 .. L_b + i
                 } else {
 #pragma unroll
@@ -289,11 +346,25 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+        if constexpr (F8) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const u32x4 kf = *(const u32x4*)(ktile + koff[s]);
+            for (int j = 0; j < NKR; ++j) {
+                const u32x4 raw = *(const u32x4*)(ktile + koff[j]);
+                const u32x4 k0 = e4m3x8_to_bf16(raw[0], raw[1]);
+                const u32x4 k1 = e4m3x8_to_bf16(raw[2], raw[3]);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma_32x32x16(kf, qf[rb][s], sacc[rb]);
+                for (int rb = 0; rb < RB; ++rb) {
+                    sacc[rb] = mfma_32x32x16(k0, qf[rb][2 * j], sacc[rb]);
+                    sacc[rb] = mfma_32x32x16(k1, qf[rb][2 * j + 1], sacc[rb]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kf = *(const u32x4*)(ktile + koff[s]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma_32x32x16(kf, qf[rb][s], sacc[rb]);
+            }
         }
 
         // Online softmax; lane (ln, lh) holds 16 keys of query row ln.
@@ -304,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = ks + mfma_row(r, lane);
-                const float v = sacc[rb][r] * scale_log2;
+                const float v = sacc[rb][r] * sl2;
                 sacc[rb][r] = (key >= cc.end || key > lim[rb]) ? -INFINITY : v;
                 tmax = fmaxf(tmax, sacc[rb][r]);
             }
@@ -348,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             const int nv = cc.end - ks;
             for (int idx = lane; idx < (kTile - nv) * T::kRowChunks; idx += 64) {
                 const int row = nv + idx / T::kRowChunks, c = idx % T::kRowChunks;
-                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa_xor<D>(row))) =
+                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa_xor<D, F8>(row))) =
                     u32x4{0, 0, 0, 0};
             }
         }
@@ -359,9 +430,15 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const char* vp = vtile + 16 * tt * T::kRowBytes;
-                const u32x2 v0 = lds_read_tr16(vp + voff[db][0]);
-                const u32x2 v1 = lds_read_tr16(vp + voff[db][1]);
-                const u32x4 vf = u32x4{v0.x, v0.y, v1.x, v1.y};
+                u32x4 vf;
+                if constexpr (F8) {
+                    const u32x2 raw = lds_read_tr8(vp + voff[db][0]);
+                    vf = e4m3x8_to_bf16(raw.x, raw.y);
+                } else {
+                    const u32x2 v0 = lds_read_tr16(vp + voff[db][0]);
+                    const u32x2 v1 = lds_read_tr16(vp + voff[db][1]);
+                    vf = u32x4{v0.x, v0.y, v1.x, v1.y};
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     o[rb][db] = mfma_32x32x16(vf, pb[rb][tt], o[rb][db]);
@@ -387,7 +464,7 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
                     if (row >= R) continue;
                     const int i = row / G, gq = row - i * G;
                     const size_t oi = (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D;
-                    const float inv = 1.f / l_r[rb];
+                    const float inv = vsc / l_r[rb];
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -417,7 +494,8 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
                     for (int db = 0; db < NDB; ++db)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] = o[rb][db][r];
+                            po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] =
+                                F8 ? o[rb][db][r] * vsc : o[rb][db][r];
                     if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
                 }
                 for (int sp = seg_split0 + 1 + lane; sp <= cc.split; sp += 64)
@@ -479,15 +557,25 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, floa
     int rc = check_launch("attn_items");
     if (rc != SD_OK) return rc;
     const int G = d->n_q_heads / d->n_kv_heads;
-#define SDV_LAUNCH_GQA(DD, RBB)                                                                  \
-    attn_gqa_stream<DD, RBB><<<g_num_cus, 256, 0, s>>>(                                          \
-        (const uint16_t*)d->q, (const uint16_t*)d->k_cache, (const uint16_t*)d->v_cache,         \
-        d->page_table, d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp, d->batch,   \
-        d->num_q, d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, chunk, max_splits, scale_log2)
+#define SDV_LAUNCH_GQA(DD, RBB, F8)                                                              \
+    attn_gqa_stream<DD, RBB, F8><<<g_num_cus, 256, 0, s>>>(                                      \
+        (const uint16_t*)d->q, (const char*)d->k_cache, (const char*)d->v_cache, d->page_table,  \
+        d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp, d->batch, d->num_q,         \
+        d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, chunk, max_splits, scale_log2,          \
+        d->k_scale, d->v_scale)
+    const bool f8 = d->kv_format == SD_KV_E4M3;
     if (d->d_qk == 128) {
-        if (R <= 32) SDV_LAUNCH_GQA(128, 1); else SDV_LAUNCH_GQA(128, 2);
+        if (f8) {
+            if (R <= 32) SDV_LAUNCH_GQA(128, 1, true); else SDV_LAUNCH_GQA(128, 2, true);
+        } else {
+            if (R <= 32) SDV_LAUNCH_GQA(128, 1, false); else SDV_LAUNCH_GQA(128, 2, false);
+        }
     } else {
-        if (R <= 32) SDV_LAUNCH_GQA(64, 1); else SDV_LAUNCH_GQA(64, 2);
+        if (f8) {
+            if (R <= 32) SDV_LAUNCH_GQA(64, 1, true); else SDV_LAUNCH_GQA(64, 2, true);
+        } else {
+            if (R <= 32) SDV_LAUNCH_GQA(64, 1, false); else SDV_LAUNCH_GQA(64, 2, false);
+        }
     }
 #undef SDV_LAUNCH_GQA
     return check_launch("attn_gqa_stream");

@@ -137,11 +137,11 @@ extern "C" int sd_kv_rollback(const sd_rollback_desc* d, void* stream) {
         return fail(SD_EUNSUPPORTED, "sd_kv_rollback: batch too large");
     int es = 0;
     if (d->poison_rejected) {
-        if (d->dtype != SD_F32 && d->dtype != SD_BF16)
+        if (d->dtype != SD_F32 && d->dtype != SD_BF16 && d->dtype != SD_E4M3)
             return fail(SD_EINVAL, "sd_kv_rollback: unknown dtype %d", d->dtype);
         if (d->kind != SD_ATTN_GQA && d->kind != SD_ATTN_MLA)
             return fail(SD_EINVAL, "sd_kv_rollback: unknown kind %d", d->kind);
-        es = d->dtype == SD_BF16 ? 2 : 4;
+        es = d->dtype == SD_BF16 ? 2 : d->dtype == SD_E4M3 ? 1 : 4;
         if (!d->k_cache || (d->kind == SD_ATTN_GQA && !d->v_cache) || d->num_pages <= 0 ||
             d->n_kv_heads <= 0 || d->d_k <= 0 || (d->kind == SD_ATTN_GQA && d->d_v <= 0))
             return fail(SD_EINVAL, "sd_kv_rollback: poisoning needs the cache description");

@@ -52,6 +52,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// ds_read_b64_tr_b8: in each group of 16 lanes, lane t receives byte t%8 of
+// the 8-byte reads of lanes t/8 + 2e (e = 0..7), as byte e of its result.
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
 // XOR applied to the 16-byte chunk index of tile row `row` (values 0..7, so
 // each aligned group of 8 chunks maps onto itself).  With it, the eight rows a
 // ds_read_b128 phase touches (same chunk, rows r..r+7) and the 4 rows x 2

@@ -67,6 +67,10 @@ def _attn_desc(**kw):
     (dict(d_qk=96, d_v=96), sdv.SD_EUNSUPPORTED),
     (dict(max_seq_len=1000), sdv.SD_EINVAL),            # exceeds max_pages * 64
     (dict(n_q_heads=64, n_kv_heads=2), sdv.SD_EUNSUPPORTED),  # 32 heads x 4 rows > 64
+    (dict(kv_format=7), sdv.SD_EINVAL),
+    (dict(kv_format=1, dtype=0), sdv.SD_EUNSUPPORTED),  # E4M3 cache with f32 q
+    (dict(kv_format=1, kind=1, n_kv_heads=1, d_qk=576, d_v=512), sdv.SD_EUNSUPPORTED),  # MLA
+    (dict(kv_format=1, d_qk=96, d_v=96), sdv.SD_EUNSUPPORTED),
 ])
 def test_attention_host_validation(kw, code):
     with pytest.raises(sdv.SdvError) as e:
@@ -90,6 +94,11 @@ def test_attention_workspace_and_pointer_checks():
     assert e.value.code == sdv.SD_EINVAL
     with pytest.raises(sdv.SdvError) as e:      # NULL output
         sdv.sd_verify_attn(_attn_desc(out=0), 4096, n, 0)
+    assert e.value.code == sdv.SD_EINVAL
+    d8 = _attn_desc(kv_format=1, k_scale=2048, v_scale=0)
+    assert sdv.sd_verify_attn_workspace_size(d8) == n  # the workspace does not depend on it
+    with pytest.raises(sdv.SdvError) as e:      # E4M3 cache without v_scale
+        sdv.sd_verify_attn(d8, 4096, n, 0)
     assert e.value.code == sdv.SD_EINVAL
 
 
