@@ -23,6 +23,7 @@ softmax((logits + N(0, 0.5^2)) / T)).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -88,6 +89,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time K replays of the step captured as one HIP graph (per-call "
                          "times still come from the eager steps before it)")
+    ap.add_argument("--kv-cache", choices=("as_dtype", "e4m3"), default="as_dtype",
+                    help="KV cache format: the workload's dtype (default) or FP8 E4M3 codes "
+                         "with per-kv-head scales (GQA bf16 workloads)")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
     return ap.parse_args()
@@ -95,16 +99,18 @@ def parse():
 
 def attention_bytes(cfg, seq_lens_before):
     """Algorithmic HBM bytes of one sd_verify_attn call: every cached and new
-    key/value read once, the new rows written once, q read, fp32 out written."""
+    key/value read once, the new rows read (q's dtype) and written once (the
+    cache's element size), q read, fp32 out written."""
     es = 2 if cfg.dtype == "bf16" else 4
+    es_kv = 1 if cfg.kv_cache == "e4m3" else es
     B, NQ = cfg.batch, cfg.num_q
     keys = float(np.sum(seq_lens_before.astype(np.float64) + NQ))
     if cfg.mla:
         kv = keys * cfg.d_qk * es
         new = B * NQ * cfg.d_qk * es * 2
     else:
-        kv = keys * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * es
-        new = B * NQ * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * es * 2
+        kv = keys * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * es_kv
+        new = B * NQ * cfg.n_kv_heads * (cfg.d_qk + cfg.d_v) * (es + es_kv)
     q = B * NQ * cfg.n_q_heads * cfg.d_qk * es
     out = B * NQ * cfg.n_q_heads * cfg.d_v * 4
     return kv + new + q + out
@@ -164,10 +170,11 @@ def cpu_baseline(cfg, seed, wl, host_inputs, n_req):
     kc, vc = sel["k_cache"], sel["v_cache"]
     s = time.perf_counter()
     oracle.kv_append(sel["seq_lens"], sel["page_table"], sel["num_pages"], sel["k_new"],
-                     sel["v_new"], kc, vc, mla=cfg.mla)
+                     sel["v_new"], kc, vc, mla=cfg.mla, k_scale=sel["k_scale"],
+                     v_scale=sel["v_scale"])
     ref_o = oracle.verify_attn(sel["q"], kc, vc, sel["page_table"], sel["seq_lens"],
                                sel["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
-                               mla=cfg.mla)
+                               mla=cfg.mla, k_scale=sel["k_scale"], v_scale=sel["v_scale"])
     timings["attention"] = time.perf_counter() - s
     H = sel["H"] if sel["H"] is not None else ref_o.reshape(B * Q, -1)
     W = sel["W"]
@@ -225,6 +232,8 @@ def gather_sample(cfg, wl, n_req):
            "k_cache": to_host(t["k_cache"].index_select(0, idx)),
            "v_cache": to_host(t["v_cache"].index_select(0, idx)) if t["v_cache"] is not None else None,
            "H": to_host(t["H"][: n_req * Q]) if "H" in t else None,
+           "k_scale": to_host(t["k_scale"]) if "k_scale" in t else None,
+           "v_scale": to_host(t["v_scale"]) if "v_scale" in t else None,
            "W": to_host(t["W"])}
     return out
 
@@ -262,7 +271,14 @@ def main():
 
     sdv.lib()  # fail loudly if the HIP library is missing
     cfg = sdsynth.CONFIGS[args.config]
+    if args.kv_cache != "as_dtype":
+        if cfg.mla or cfg.dtype != "bf16":
+            print(json.dumps({"error": "an E4M3 KV cache needs a GQA bf16 workload",
+                              "config": args.config}))
+            sys.exit(2)
+        cfg = dataclasses.replace(cfg, kv_cache=args.kv_cache)
     seed = sdsynth.config_seed(args.config)
+    workload = WORKLOAD_NAMES[args.config] + ("_e4m3" if cfg.kv_cache == "e4m3" else "")
     dev = torch.device("cuda", 0)
     extra = (args.warmup + (2 if args.graph else 1) * args.steps + 4) * cfg.num_q
     wl = sdsynth.make_workload(cfg, seed, device=dev, extra_tokens=extra)
@@ -286,7 +302,8 @@ def main():
                           n_kv_heads=cfg.n_kv_heads, W=t["W"], drafts=drafts, temperature=temp,
                           u_accept=ua, u_sample=us, k_new=t["k_new"], v_new=t["v_new"],
                           mla=cfg.mla, d_v=cfg.d_v, H=t.get("H"), top_p=top_p,
-                          draft_probs=pd if (wl.temperature > 0).any() else None)
+                          draft_probs=pd if (wl.temperature > 0).any() else None,
+                          k_scale=t.get("k_scale"), v_scale=t.get("v_scale"))
     # Target logits of the first step -> synthetic drafts (outside the timed region).
     step.attention()
     step.lm_head()
@@ -377,7 +394,7 @@ def main():
         dom_kernel = "lm_head_dma" if (cfg.dtype == "bf16" and cfg.hidden % 128 == 0) else None
     else:
         dom_kernel = "attn_mla_bf16" if cfg.mla else ("attn_gqa_stream" if cfg.dtype == "bf16" else None)
-    traffic = profiled_traffic(dom_kernel, WORKLOAD_NAMES[args.config]) if dom_kernel else None
+    traffic = profiled_traffic(dom_kernel, workload) if dom_kernel else None
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],
             "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": traffic}
     line = {
@@ -385,13 +402,16 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": f"C{args.config} {cfg.name}", "batch": B, "K": cfg.K,
+        "config": {"workload": f"C{args.config} {cfg.name}" + (
+                       ", E4M3 KV cache" if cfg.kv_cache == "e4m3" else ""),
+                   "batch": B, "K": cfg.K,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.d_qk, "kv_len": (int(cfg.seq_len) if cfg.seq_len
                                                     else list(cfg.seq_len_range)),
                    "mean_kv_len": float(L_mid.mean()), "hidden": cfg.hidden,
                    "vocab": cfg.vocab, "temperature": cfg.temperature or cfg.mixed_modes,
-                   "top_p": cfg.top_p, "page_size": cfg.page_size},
+                   "top_p": cfg.top_p, "page_size": cfg.page_size,
+                   "kv_cache": "e4m3" if cfg.kv_cache == "e4m3" else cfg.dtype},
         "accepted_tokens_per_sec": tok_per_s,
         "mean_emitted_per_request": acc_total / args.steps / B,
         "event_ms_per_step": ev_step_ms,

@@ -10,16 +10,19 @@
 //                   (flags), then the K+1 new keys/values -> cache positions
 //                   L_b .. L_b+K
 //   GQA, bf16 q with a bf16 or E4M3 cache:
-//                   attn_items (prefix sum of the requests' key chunks) and
+//                   attn_items (prefix sum of the requests' key tiles) and
 //                   attn_gqa_stream (attn_gqa.hip): persistent waves stream
-//                   (kv head, request, chunk) items through LDS rings; every
-//                   query row of the kv head's group shares each K/V tile, so
-//                   a tile is read from HBM exactly once
+//                   equal ranges of the 32-key tiles of all (kv head,
+//                   request) pairs through LDS rings; every query row of the
+//                   kv head's group shares each K/V tile, so a tile is read
+//                   from HBM exactly once
 //   MLA, bf16:      attn_mla_bf16 and its exact fallback (attn_mla.hip)
 //   attn_combine    log-sum-exp merge of the chunk partials
 // plus attn_f32_rows, a plain fp32 path for small float32 problems.
 
 #include <math.h>
+
+#include <algorithm>
 
 #include "sdv_device.h"
 #include "sdv_internal.h"
@@ -170,24 +173,27 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
 constexpr int kCombineRows = 64;
 constexpr int kCombineCache = 12288;  // split weights cached per block (48 KiB)
 
-// grid (kv head, request, 64-row block).  mode 1 (MLA): requests
-// whose keys fit one chunk were written by the attention kernel already.
-// mode 2 (GQA): the attention kernel marks in row 0 of each slot whether the
-// pair was written directly (slot 0) or a slot is empty (its chunk was merged
-// into an earlier slot of the same wave); only the written slots are merged,
-// in split order.  Each block weighs its rows' partials once (weights cached
-// in LDS when they fit), then reads the partial planes [d][R] with
-// consecutive threads on consecutive rows.
+// grid (kv head, request, 64-row block).
+// mode 1 (MLA): slot k of request b is its key chunk k; requests whose keys
+//   fit one chunk were written by the attention kernel already.
+// mode 2 (GQA): n = min(nw, T) of the streaming kernel's nw waves split the
+//   T = first[B] * Hkv tiles evenly, wave w < n taking [floor(w T / n),
+//   floor((w+1) T / n)); a
+//   pair whose tiles lie in one wave was written by that wave, otherwise its
+//   waves w_lo .. w_hi each left one partial: wave w_lo in slot 2 w_lo + 1
+//   (2 w_lo if its range starts at the pair's first tile), the others in
+//   slot 2w.  Slots are merged in key order.
+// Each block weighs its rows' partials once (weights cached in LDS when they
+// fit), then reads the partial planes [d][R] with consecutive threads on
+// consecutive rows.
 __global__ __launch_bounds__(256) void attn_combine(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
-    float* __restrict__ out, uint16_t* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int G,
-    int R, int D, int chunk, int max_splits, int mode) {
+    const int32_t* __restrict__ first, float* __restrict__ out, uint16_t* __restrict__ out_lowp,
+    int NQ, int Hq, int Hkv, int G, int R, int D, int chunk, int max_splits, int nw, int mode) {
     __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
     __shared__ float s_red[4][kCombineRows];
     __shared__ __attribute__((aligned(16))) float s_w[kCombineCache];
-    __shared__ int s_list[kCombineMaxSplits];
-    __shared__ int s_cnt[4], s_np;
     const int kvh = blockIdx.x, b = blockIdx.y;
     const int r0 = blockIdx.z * kCombineRows;
     const int nr = min(kCombineRows, R - r0);
@@ -202,29 +208,29 @@ __global__ __launch_bounds__(256) void attn_combine(
         }
         return;
     }
-    const int ns = (seq_lens[b] + NQ + chunk - 1) / chunk;
-    if (mode == 1 && ns == 1) return;
-    const size_t pbase = ((size_t)b * Hkv + kvh) * max_splits;
-    if (mode == 2 && part_ml[pbase * R].y == kPartDirect) return;
-    // The slots to merge, in split order (ordered compaction, 256 at a time).
-    if (threadIdx.x == 0) s_np = 0;
-    __syncthreads();
-    for (int base = 0; base < ns; base += 256) {
-        const int sp = base + threadIdx.x;
-        const bool pres = sp < ns && (mode != 2 || part_ml[(pbase + sp) * R].y != kPartEmpty);
-        const unsigned long long bal = __ballot(pres);
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        if (lane == 0) s_cnt[w] = __popcll(bal);
-        __syncthreads();
-        int pos = s_np;
-        for (int k = 0; k < w; ++k) pos += s_cnt[k];
-        pos += __popcll(bal & ((1ull << lane) - 1ull));
-        if (pres) s_list[pos] = sp;
-        __syncthreads();
-        if (threadIdx.x == 0) s_np += (s_cnt[0] + s_cnt[1]) + (s_cnt[2] + s_cnt[3]);
-        __syncthreads();
+    // Slot k (k < np) holds the k-th partial of this pair in key order.
+    long slot0, slot_step;
+    int np;
+    if (mode == 1) {
+        np = (seq_lens[b] + NQ + chunk - 1) / chunk;
+        if (np == 1) return;
+        slot0 = ((long)b * Hkv + kvh) * max_splits;
+        slot_step = 1;
+    } else {
+        const long Th = first[gridDim.y], T = Th * Hkv;
+        const long n = min((long)nw, T);  // waves in use
+        const long g0 = (long)kvh * Th + first[b], g1 = g0 + (first[b + 1] - first[b]) - 1;
+        // wave of tile x: the largest w with floor(w T / n) <= x
+        const int w_lo = (int)(((g0 + 1) * n + T - 1) / T) - 1;
+        const int w_hi = (int)(((g1 + 1) * n + T - 1) / T) - 1;
+        if (w_lo == w_hi) return;
+        np = w_hi - w_lo + 1;
+        slot0 = 2L * w_lo + ((long)w_lo * T / n < g0 ? 1 : 0);
+        slot_step = 2;
     }
-    const int np = s_np;
+    auto slot = [&](int k) -> long {
+        return k == 0 ? slot0 : (mode == 1 ? slot0 + k : slot0 - (slot0 & 1) + slot_step * k);
+    };
     // Row statistics: four threads per row, each over every fourth slot,
     // merged in a fixed order.
     const int lr4 = threadIdx.x % kCombineRows, q4 = threadIdx.x / kCombineRows;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256) void attn_combine(
         float M = -INFINITY;
         if (lr4 < nr)
             for (int k = q4; k < np; k += 4)
-                M = fmaxf(M, part_ml[(pbase + s_list[k]) * R + r0 + lr4].x);
+                M = fmaxf(M, part_ml[slot(k) * R + r0 + lr4].x);
         s_red[q4][lr4] = M;
     }
     __syncthreads();
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void attn_combine(
         if (lr4 < nr) {
             const float M = s_m[lr4];
             for (int k = q4; k < np; k += 4) {
-                const float2 ml = part_ml[(pbase + s_list[k]) * R + r0 + lr4];
+                const float2 ml = part_ml[slot(k) * R + r0 + lr4];
                 if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
             }
         }
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_combine(
     if (cached) {
         for (int idx = threadIdx.x; idx < np * nr; idx += blockDim.x) {
             const int k = idx / nr, lr = idx - k * nr;
-            const float m = part_ml[(pbase + s_list[k]) * R + r0 + lr].x;
+            const float m = part_ml[slot(k) * R + r0 + lr].x;
             s_w[idx] = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
         }
         __syncthreads();
@@ -278,20 +284,20 @@ __global__ __launch_bounds__(256) void attn_combine(
         const int nq = nr >> 2;
         for (int idx = threadIdx.x; idx < nq * D; idx += blockDim.x) {
             const int dl = idx / nq, lq = 4 * (idx - dl * nq);
-            const float* po = part_o + (pbase * D + dl) * R + r0 + lq;
+            const float* po = part_o + (size_t)dl * R + r0 + lq;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             int k = 0;
             for (; k + 8 <= np; k += 8) {
                 f32x4 v[8], w[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(po + s_list[k + u] * sstride);
+                for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(po + slot(k + u) * sstride);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(s_w + (k + u) * nr + lq);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) acc += w[u] * v[u];
             }
             for (; k < np; ++k)
-                acc += *(const f32x4*)(s_w + k * nr + lq) * *(const f32x4*)(po + s_list[k] * sstride);
+                acc += *(const f32x4*)(s_w + k * nr + lq) * *(const f32x4*)(po + slot(k) * sstride);
 #pragma unroll
             for (int j = 0; j < 4; ++j) emit(r0 + lq + j, dl, acc[j]);
         }
@@ -300,17 +306,17 @@ __global__ __launch_bounds__(256) void attn_combine(
     for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
         const int dl = idx / nr, lr = idx - dl * nr;
         const int row = r0 + lr, d = dl;
-        const float* po = part_o + (pbase * D + d) * R + row;
+        const float* po = part_o + (size_t)d * R + row;
         float acc = 0.f;
         for (int k = 0; k < np; ++k) {
             float w;
             if (cached) {
                 w = s_w[k * nr + lr];
             } else {
-                const float m = part_ml[(pbase + s_list[k]) * R + row].x;
+                const float m = part_ml[slot(k) * R + row].x;
                 w = (m == -INFINITY) ? 0.f : exp2f(m - s_m[lr]) * s_inv[lr];
             }
-            acc += w * po[s_list[k] * sstride];
+            acc += w * po[slot(k) * sstride];
         }
         emit(row, d, acc);
     }
@@ -403,6 +409,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
 // ---------------------------------------------------------------------------
 struct AttnPlan {
     int G = 0, R = 0, chunk = 0, max_splits = 0;
+    int max_waves = 0;  // GQA streaming kernel: waves sized for (two slots each)
     int path = 0;  // 0 gqa bf16 (MFMA), 1 gqa f32, 2 mla bf16
     size_t off_valid = 0, off_first = 0, off_flags = 0, off_po = 0, off_pml = 0, total = 0;
 };
@@ -455,14 +462,13 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
         if (p->R > 64)
             return fail(SD_EUNSUPPORTED, "sd_verify_attn: (Hq/Hkv)*(K+1) = %d > 64", p->R);
         p->path = 0;
-        // Chunks small enough that the persistent waves (4 per CU) get about
-        // sixteen items each at the longest length, within [128, 1024] keys.
-        const long pairs = (long)d->batch * d->n_kv_heads;
-        int chunk = 1024;
-        while (chunk > 128 && pairs * ((maxkeys + chunk - 1) / chunk) < 16L * 4 * 256) chunk >>= 1;
-        while ((maxkeys + chunk - 1) / chunk > kCombineMaxSplits) chunk <<= 1;
-        p->chunk = chunk;
-        p->max_splits = (int)((maxkeys + chunk - 1) / chunk);
+        // No more waves than 4-wave groups of tiles at the longest length.
+        const long max_tiles = (long)d->batch * d->n_kv_heads * ((maxkeys + 31) / 32);
+        if (max_tiles > 0x7fffffffL / 4)
+            return fail(SD_EUNSUPPORTED, "sd_verify_attn: too many key tiles");
+        p->max_waves = (int)std::min<long>(kGqaMaxWaves, 4 * ((max_tiles + 3) / 4));
+        if (p->max_waves + 1 > kCombineMaxSplits)
+            return fail(SD_EUNSUPPORTED, "sd_verify_attn: too many waves for the combine");
     } else {
         if (d->d_qk > 256 || 256 % d->d_qk != 0)
             return fail(SD_EUNSUPPORTED, "sd_verify_attn: f32 GQA needs head dim dividing 256");
@@ -481,8 +487,11 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
                                  mla_flag_count(d->batch, d->num_q, d->n_q_heads, p->max_splits),
                        256);
     p->off_po = off;
-    const size_t nparts = (size_t)d->batch * d->n_kv_heads *
-                          (p->path == 2 && p->max_splits == 1 ? 0 : p->max_splits) * p->R;
+    const size_t nparts =
+        (p->path == 0 ? 2 * (size_t)p->max_waves
+                      : (size_t)d->batch * d->n_kv_heads *
+                            (p->path == 2 && p->max_splits == 1 ? 0 : p->max_splits)) *
+        p->R;
     off = align_up(off + nparts * d->d_v * sizeof(float), 256);
     p->off_pml = off;
     off = align_up(off + nparts * sizeof(float2), 256);
@@ -561,18 +570,19 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         if (p.max_splits == 1) return SD_OK;
         attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows),
                        256, 0, s>>>(
-            po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads, 1,
-            p.G, p.R, d->d_v, p.chunk, p.max_splits, 1);
+            po, pml, d->seq_lens, valid, nullptr, d->out, (uint16_t*)d->out_lowp, NQ,
+            d->n_q_heads, 1, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0, 1);
         return check_launch("attn_combine");
     }
     int32_t* first = (int32_t*)(ws + p.off_first);
-    if ((rc = gqa_launch(d, valid, first, po, pml, p.R, p.chunk, p.max_splits, scale_log2, s)) !=
+    int nw = 0;
+    if ((rc = gqa_launch(d, valid, first, po, pml, p.R, p.max_waves, scale_log2, &nw, s)) !=
         SD_OK)
         return rc;
     attn_combine<<<dim3(d->n_kv_heads, B,
                         (p.R + kCombineRows - 1) / kCombineRows),
                    256, 0, s>>>(
-        po, pml, d->seq_lens, valid, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
-        d->n_kv_heads, p.G, p.R, d->d_v, p.chunk, p.max_splits, 2);
+        po, pml, d->seq_lens, valid, first, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
+        d->n_kv_heads, p.G, p.R, d->d_v, 0, 0, nw, 2);
     return check_launch("attn_combine");
 }

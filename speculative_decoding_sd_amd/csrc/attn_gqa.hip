@@ -1,4 +1,5 @@
-// GQA verify attention on gfx950, bf16 cache, fp32 accumulation.
+// GQA verify attention on gfx950, bf16 q with a bf16 or E4M3 (FP8) cache, fp32
+// accumulation.
 // [TRT-MTP] "支持 MTP 的注意力機制": the K+1 query positions of a request are
 // verified together against its cache under a causal mask; [CSDN-MTP]
 // "整体计算流程" step 2: softmax(QK^T/sqrt(d))V over the cached and new keys.
@@ -6,21 +7,27 @@
 // The query rows of one (request, kv head) are the G heads of the group at
 // each of the K+1 positions (row = i*G + g, at most 64), so every key/value
 // row fetched from HBM serves all of them: the kernel is bound by streaming
-// the cache.  Work items are (kv head, request, key chunk) triples; each wave
-// runs its own items start to finish (no workgroup barriers) and streams their
-// 32-key tiles through private LDS rings filled by LDS DMA (three K stages,
-// two V stages: 40 KiB per wave at head dim 128), so that about two tiles per
-// wave are in flight while one is computed, also across item boundaries.  The grid holds one workgroup of 4 waves per CU; each wave
-// takes an equal contiguous range of the non-empty items.
+// the cache.  The work is the sequence of 32-key tiles of all (kv head,
+// request) pairs; each persistent wave takes an equal contiguous range of it
+// (no workgroup barriers) and streams its tiles through private LDS rings
+// filled by LDS DMA (S K stages and S - 1 V stages, as many as the LDS holds
+// up to S = 5: 40 KiB per wave for bf16 at head dim 128), so that S - 1
+// tiles per wave are in flight while one is computed, also across pair
+// boundaries.  One 4-wave workgroup per CU (two for E4M3 with one row block).
 // Per tile and 32-row block:
-//   S^T = K Q^T    A = K rows from LDS (ds_read_b128), B = Q^T in registers;
+//   S^T = K Q^T    A = K rows from LDS (ds_read_b128; E4M3 bytes converted to
+//                  bf16 exactly), B = Q^T in registers;
 //   online softmax lane-local (one query row per lane column); the running
 //                  max is raised only when a tile exceeds it by more than 2^8;
-//   O^T += V^T P^T A = V^T fragments by ds_read_b64_tr_b16 from the row-major
-//                  V tile, P in bf16 hi + lo halves (two MFMAs).
-// Each item writes its unnormalised O^T and (m, l) per row; attn_combine
-// merges the chunks of a request.
+//   O^T += V^T P^T A = V^T fragments by ds_read_b64_tr_b16 (bf16) or
+//                  ds_read_b64_tr_b8 + conversion (E4M3) from the row-major V
+//                  tile, P in bf16 hi + lo halves (two MFMAs).
+// A wave's tiles of one pair form a segment, written once at its end: to the
+// output when it covers the whole pair, else as an unnormalised partial
+// (O^T, m, l) that attn_combine merges.
 #include <math.h>
+
+#include <algorithm>
 
 #include "sdv_device.h"
 #include "sdv_internal.h"
@@ -33,13 +40,13 @@ constexpr int kPage = 64;
 constexpr int kTile = 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
-template <int D, bool F8>
+template <int D, bool F8, int KS>
 struct GqaTile {
     static constexpr int kRowBytes = D * (F8 ? 1 : 2);
     static constexpr int kRowChunks = kRowBytes / 16;
     static constexpr int kHalfBytes = kTile * kRowBytes;  // the K (or V) rows of a tile
     static constexpr int kDmaHalf = kHalfBytes / 1024;    // 1 KiB DMA ops per half tile
-    static constexpr int kKStages = 3, kVStages = 2;      // K runs one tile further ahead
+    static constexpr int kKStages = KS, kVStages = KS - 1;  // K runs one tile further ahead
     static constexpr int kRingBytes = (kKStages + kVStages) * kHalfBytes;
 };
 
@@ -91,76 +98,117 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
-// Work items are (kv head, request, key chunk) triples of non-empty chunks,
-// numbered kv-head-major: item i has kv head i / NRC and request-chunk index
-// rc = i % NRC, where request b owns rc in [first[b], first[b+1]) and
-// NRC = first[B].  first[] is the exclusive prefix sum of the requests' chunk
-// counts (0 for invalid requests), written by attn_items.  Wave w of nw runs
-// the contiguous item range [w N / nw, (w+1) N / nw), N = NRC * Hkv, which
-// balances the waves to one item; kv-head-major numbering puts concurrent
-// waves on different heads, spreading their reads over the cache pages'
-// address ranges.  All cursor fields are wave-uniform.
-struct ItemCursor {
-    int item, hi, t, ntiles, b, kvh, split, rc, L, start, end;
-    int pg;  // physical page of the current tile (DMA cursors only)
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the
+// upper half of one copy with the lower half of the other: the pair then
+// holds both halves' values in every lane).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two floats -> packed bf16 (lo in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// The work is the sequence of 32-key tiles of every (kv head, request) pair,
+// kv-head-major: for each kv head, the requests in order, each request's
+// tiles 0 .. P_b - 1 (P_b = ceil((L_b + K + 1) / 32), 0 for an invalid
+// request).  first[b] is the exclusive prefix sum of P_b (first[B] = Th, the
+// tiles of one kv head), written by attn_items; global tile g is tile
+// g % Th of kv head g / Th.  With T = Th * Hkv tiles and n = min(nw, T) of
+// the nw waves in use, wave w < n runs tiles [tile_lo(w), tile_lo(w + 1)),
+// tile_lo(w) = floor(w T / n): every wave gets the same number of tiles to
+// one, and at least one.  All cursor fields are wave-uniform.
+struct TileCursor {
+    int g, hi;          // global tile, end of the wave's range
+    int kvh, b, t, P;   // kv head, request, tile within the pair, tiles of the pair
+    int L;              // seq_lens[b]
+    int pg;             // physical page of the tile (DMA cursors)
 };
 
-__device__ __forceinline__ void cursor_fill(ItemCursor& c, int NQ, int chunk,
-                                            const int32_t* __restrict__ seq_lens) {
-    c.L = seq_lens[c.b];
-    c.start = c.split * chunk;
-    c.end = min(c.start + chunk, c.L + NQ);
-    c.ntiles = (c.end - c.start + kTile - 1) / kTile;
-    c.t = 0;
-}
-
-__device__ __forceinline__ void cursor_begin(ItemCursor& c, int lo, int hi, int B, int NRC,
-                                             int NQ, int chunk, const int32_t* __restrict__ first,
+__device__ __forceinline__ void cursor_begin(TileCursor& c, int lo, int hi, int B, int Th,
+                                             const int32_t* __restrict__ first,
                                              const int32_t* __restrict__ seq_lens) {
-    c.item = lo;
+    c.g = lo;
     c.hi = hi;
     if (lo >= hi) return;
-    c.kvh = lo / NRC;
-    c.rc = lo - c.kvh * NRC;
-    int b0 = 0, b1 = B;  // largest b with first[b] <= rc (first[B] > rc)
+    c.kvh = lo / Th;
+    const int r = lo - c.kvh * Th;
+    int b0 = 0, b1 = B;  // largest b with first[b] <= r (first[B] = Th > r)
     while (b1 - b0 > 1) {
         const int mid = (b0 + b1) >> 1;
-        if (first[mid] <= c.rc) b0 = mid; else b1 = mid;
+        if (first[mid] <= r) b0 = mid; else b1 = mid;
     }
     c.b = b0;
-    c.split = c.rc - first[b0];
-    cursor_fill(c, NQ, chunk, seq_lens);
+    c.t = r - first[b0];
+    c.P = first[b0 + 1] - first[b0];
+    c.L = seq_lens[b0];
 }
 
-__device__ __forceinline__ void cursor_next(ItemCursor& c, int NRC, int NQ, int chunk,
+__device__ __forceinline__ void cursor_next(TileCursor& c, int B,
                                             const int32_t* __restrict__ first,
                                             const int32_t* __restrict__ seq_lens) {
-    if (++c.t < c.ntiles) return;
-    if (++c.item >= c.hi) return;
-    if (++c.rc == NRC) {
-        c.rc = 0;
-        ++c.kvh;
-        c.b = 0;
-        c.split = -1;
+    if (++c.g >= c.hi) return;
+    if (++c.t < c.P) return;
+    // Next pair with tiles; one exists because g < hi <= T.
+    c.t = 0;
+    do {
+        if (++c.b == B) {
+            c.b = 0;
+            ++c.kvh;
+        }
+        c.P = first[c.b + 1] - first[c.b];
+    } while (c.P == 0);
+    c.L = seq_lens[c.b];
+}
+
+// Workgroups per CU: two for E4M3 tiles with one row block (a 20 KiB ring per
+// wave at head dim 128, 256 registers), so that one wave's softmax overlaps
+// another's MFMAs and waits; one otherwise (the bf16 ring fills the LDS).
+template <int D, int RB, bool F8>
+constexpr int gqa_groups_per_cu() { return (F8 && RB == 1) ? 2 : 1; }
+
+// K ring stages (V has one fewer): as deep as the LDS allows for the
+// workgroups per CU, at most 5.
+template <int D, int RB, bool F8>
+constexpr int gqa_kstages() {
+    constexpr int half = 32 * D * (F8 ? 1 : 2);
+    constexpr int per_wave = 160 * 1024 / (4 * gqa_groups_per_cu<D, RB, F8>());
+    constexpr int ks = (per_wave / half + 1) / 2;  // KS + (KS - 1) halves
+    return ks > 5 ? 5 : ks;
+}
+
+// s_waitcnt for at most g half tiles of H vm ops each still in flight (a
+// larger g than the counter can express waits for fewer, which is safe).
+template <int H, int G = 0>
+__device__ __forceinline__ void wait_halves(int g) {
+    if constexpr ((G + 1) * H > 63) {
+        wait_vmcnt<G * H>();
+    } else {
+        if (g <= G) wait_vmcnt<G * H>();
+        else wait_halves<H, G + 1>(g);
     }
-    ++c.split;
-    while (c.split >= first[c.b + 1] - first[c.b]) {  // next request with chunks
-        ++c.b;
-        c.split = 0;
-    }
-    cursor_fill(c, NQ, chunk, seq_lens);
 }
 
 template <int D, int RB, bool F8>
-__global__ __launch_bounds__(256, 1) void attn_gqa_stream(
+__global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gqa_stream(
     const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ first,
     float* __restrict__ part_o, float2* __restrict__ part_ml, float* __restrict__ out,
     uint16_t* __restrict__ out_lowp, int B, int NQ, int Hq, int Hkv, int G, int R, int max_pages,
-    int chunk, int max_splits, float scale_log2, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale) {
-    using T = GqaTile<D, F8>;
+    float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+    using T = GqaTile<D, F8, gqa_kstages<D, RB, F8>()>;
     constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-dim blocks of O^T
     __shared__ __attribute__((aligned(1024))) char s_ring[4][T::kRingBytes];
@@ -187,12 +235,11 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     // The page-table entry of a DMA cursor's tile is read when the cursor
     // reaches the tile, one issue before it is needed, so the scalar load's
     // latency is not on the DMA's critical path.
-    auto load_pg = [&](ItemCursor& c) {
-        if (c.item < c.hi)
-            c.pg = page_table[(size_t)c.b * max_pages + (c.start + kTile * c.t) / kPage];
+    auto load_pg = [&](TileCursor& c) {
+        if (c.g < c.hi) c.pg = page_table[(size_t)c.b * max_pages + (kTile * c.t) / kPage];
     };
-    auto issue = [&](const char* __restrict__ cache, const ItemCursor& c, const char* dst_p) {
-        const int ks = c.start + kTile * c.t;
+    auto issue = [&](const char* __restrict__ cache, const TileCursor& c, const char* dst_p) {
+        const int ks = kTile * c.t;
         const char* src = cache + ((size_t)c.pg * Hkv + c.kvh) * head_bytes +
                           (size_t)(ks % kPage) * T::kRowBytes;
         const uint32_t dst = lds_byte_addr(dst_p);
@@ -243,51 +290,55 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         }
     }
 
-    // Three cursors over the wave's tile stream: K DMA (three tiles ahead of
-    // the compute), V DMA (two ahead) and compute.  Issue order: K0 K1 V0 K2
-    // V1, then after computing tile c: K(c+3) V(c+2).  nk / nv count the
-    // halves issued; vmcnt waits count the 1 KiB ops issued after the one
-    // needed (DMAs complete in issue order).
-    const int NRC = first[B];
-    const long n_items = (long)NRC * Hkv;
+    // Three cursors over the wave's tile stream: K DMA (S = kKStages tiles
+    // ahead of the compute), V DMA (S - 1 ahead) and compute.  Issue order:
+    // K0, then K(i) V(i-1) for i < S, then after computing tile c: K(c+S)
+    // V(c+S-1).  nk / nv count the halves issued; vmcnt waits count the 1 KiB
+    // ops issued after the one needed (DMAs complete in issue order).
+    // With fewer tiles than waves only the first T waves take one tile each,
+    // so that every wave in use has work (the combine relies on it).
+    const int Th = first[B];
+    const long n_tiles = (long)Th * Hkv;
     const int gw = blockIdx.x * 4 + wave;
-    ItemCursor kc;
-    cursor_begin(kc, (int)(n_items * gw / nw), (int)(n_items * (gw + 1) / nw), B, NRC, NQ, chunk,
-                 first, seq_lens);
+    const int nwe = (int)min((long)nw, n_tiles);
+    TileCursor kc;
+    if (gw < nwe)
+        cursor_begin(kc, (int)(n_tiles * gw / nwe), (int)(n_tiles * (gw + 1) / nwe), B, Th, first,
+                     seq_lens);
+    else
+        kc.g = kc.hi = 0;
     load_pg(kc);
-    ItemCursor vc = kc, cc = kc;
+    TileCursor vc = kc, cc = kc;
     int nk = 0, nv = 0;
+    // issue_k / issue_v advance their cursor without reading its next page
+    // entry: the main loop reads both entries right after the tile's K
+    // fragments have been read from LDS, so that the scalar loads complete
+    // under the softmax instead of stalling the next LDS wait (LDS reads and
+    // scalar loads share one counter).
     auto issue_k = [&]() {
-        if (kc.item < kc.hi) {
+        if (kc.g < kc.hi) {
             issue(k_cache, kc, k_ring + (nk % T::kKStages) * T::kHalfBytes);
             ++nk;
-            cursor_next(kc, NRC, NQ, chunk, first, seq_lens);
-            load_pg(kc);
+            cursor_next(kc, B, first, seq_lens);
         }
     };
     auto issue_v = [&]() {
-        if (vc.item < vc.hi) {
+        if (vc.g < vc.hi) {
             issue(v_cache, vc, v_ring + (nv % T::kVStages) * T::kHalfBytes);
             ++nv;
-            cursor_next(vc, NRC, NQ, chunk, first, seq_lens);
-            load_pg(vc);
+            cursor_next(vc, B, first, seq_lens);
         }
     };
-    auto wait_groups = [&](int g) {  // at most g half tiles still in flight
-        switch (g) {
-            case 0: wait_vmcnt<0>(); break;
-            case 1: wait_vmcnt<1 * T::kDmaHalf>(); break;
-            case 2: wait_vmcnt<2 * T::kDmaHalf>(); break;
-            case 3: wait_vmcnt<3 * T::kDmaHalf>(); break;
-            case 4: wait_vmcnt<4 * T::kDmaHalf>(); break;
-            default: wait_vmcnt<5 * T::kDmaHalf>(); break;
-        }
-    };
+    auto wait_groups = [&](int g) { wait_halves<T::kDmaHalf>(g); };
     issue_k();
-    issue_k();
-    issue_v();
-    issue_k();
-    issue_v();
+    load_pg(kc);
+#pragma unroll
+    for (int i = 1; i < T::kKStages; ++i) {
+        issue_k();
+        load_pg(kc);
+        issue_v();
+        load_pg(vc);
+    }
     int cseq = 0;
 
     u32x4 qf[RB][NS];
@@ -295,23 +346,24 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
     float m_r[RB], l_r[RB];
     float sl2 = scale_log2, vsc = 1.f;  // per pair: key scale folded in; value scale
     f32x16 o[RB][NDB];
-    // Consecutive chunks of one (request, kv head) form a segment: the online
-    // softmax state and Q carry over from chunk to chunk, and the segment is
-    // written once, at its end.
-    int seg_b = -1, seg_kvh = -1, seg_split0 = 0;
-    while (cc.item < cc.hi) {
+    // The wave's tiles of one (request, kv head) pair form a segment: Q and the
+    // online softmax state live in registers across it, and it is written
+    // once, at its end.  Only the wave's first and last segments can miss
+    // tiles of their pair (the others cover whole pairs).
+    int seg_t0 = 0;
+    bool first_seg = true;
+    while (cc.g < cc.hi) {
         // K(cseq) has landed once at most the halves issued after it are in
         // flight: K(j > cseq) and V(j >= max(cseq - 1, 0)).
         wait_groups((nk - 1 - cseq) + (nv - max(cseq - 1, 0)));
-        if (cc.t == 0 && !(cc.b == seg_b && cc.kvh == seg_kvh)) {
-            seg_b = cc.b;
-            seg_kvh = cc.kvh;
-            seg_split0 = cc.split;
+        const int cend = cc.L + NQ;  // keys of the pair
+        if (cc.t == 0 || cseq == 0) {
+            seg_t0 = cc.t;
             if constexpr (F8) {
                 sl2 = scale_log2 * k_scale[cc.kvh];
                 vsc = v_scale[cc.kvh];
             }
-            // New item: Q fragments (B operand; column = query row, k = d;
+            // New segment: Q fragments (B operand; column = query row, k = d;
             // E4M3: the dims of k-step s are 32(s/2) + 16lh + 8(s%2) .. +7).
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -336,50 +388,79 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
             }
+            // The Q loads share vmcnt with the LDS DMAs the compiler cannot
+            // see: wait for them here, once per segment, so that the compiler
+            // knows them complete on every path into the tile loop body and
+            // inserts no vmcnt wait there (which would also drain the tiles
+            // prefetched ahead).
+            wait_vmcnt<0>();
         }
         const char* ktile = k_ring + (cseq % T::kKStages) * T::kHalfBytes;
         char* vtile = v_ring + (cseq % T::kVStages) * T::kHalfBytes;
-        const int ks = cc.start + kTile * cc.t;
-        // S^T = K Q^T.
-        f32x16 sacc[RB];
+        const int ks = kTile * cc.t;
+        // S^T = K Q^T, the even and odd k-steps in two independent MFMA
+        // chains (half the dependent latency), every K fragment read from LDS
+        // before the first MFMA.
+        f32x16 sacc[RB], sacc2[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) sacc[rb][r] = sacc2[rb][r] = 0.f;
         if constexpr (F8) {
+            u32x4 raw[NKR];
+#pragma unroll
+            for (int j = 0; j < NKR; ++j) raw[j] = *(const u32x4*)(ktile + koff[j]);
 #pragma unroll
             for (int j = 0; j < NKR; ++j) {
-                const u32x4 raw = *(const u32x4*)(ktile + koff[j]);
-                const u32x4 k0 = e4m3x8_to_bf16(raw[0], raw[1]);
-                const u32x4 k1 = e4m3x8_to_bf16(raw[2], raw[3]);
+                const u32x4 k0 = e4m3x8_to_bf16(raw[j][0], raw[j][1]);
+                const u32x4 k1 = e4m3x8_to_bf16(raw[j][2], raw[j][3]);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     sacc[rb] = mfma_32x32x16(k0, qf[rb][2 * j], sacc[rb]);
-                    sacc[rb] = mfma_32x32x16(k1, qf[rb][2 * j + 1], sacc[rb]);
+                    sacc2[rb] = mfma_32x32x16(k1, qf[rb][2 * j + 1], sacc2[rb]);
                 }
             }
         } else {
+            u32x4 kf[NS];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const u32x4 kf = *(const u32x4*)(ktile + koff[s]);
+            for (int s = 0; s < NS; ++s) kf[s] = *(const u32x4*)(ktile + koff[s]);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma_32x32x16(kf, qf[rb][s], sacc[rb]);
-            }
+            for (int s = 0; s < NS; s += 2)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    sacc[rb] = mfma_32x32x16(kf[s], qf[rb][s], sacc[rb]);
+                    sacc2[rb] = mfma_32x32x16(kf[s + 1], qf[rb][s + 1], sacc2[rb]);
+                }
         }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[rb] += sacc2[rb];
+        load_pg(kc);
+        load_pg(vc);
 
-        // Online softmax; lane (ln, lh) holds 16 keys of query row ln.
+        // Online softmax; lane (ln, lh) holds 16 keys of query row ln.  A
+        // tile whose keys all lie before the chunk end and at or before L_b
+        // (the causal limit of the first query) needs no mask.
+        const bool unmasked = ks + kTile <= cend && ks + kTile - 1 <= cc.L;
         u32x4 pb[RB][2], pbl[RB][2];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             float tmax = -INFINITY;
+            if (unmasked) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = ks + mfma_row(r, lane);
-                const float v = sacc[rb][r] * sl2;
-                sacc[rb][r] = (key >= cc.end || key > lim[rb]) ? -INFINITY : v;
-                tmax = fmaxf(tmax, sacc[rb][r]);
+                for (int r = 0; r < 16; ++r) {
+                    sacc[rb][r] *= sl2;
+                    tmax = fmaxf(tmax, sacc[rb][r]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = ks + mfma_row(r, lane);
+                    const float v = sacc[rb][r] * sl2;
+                    sacc[rb][r] = (key >= cend || key > lim[rb]) ? -INFINITY : v;
+                    tmax = fmaxf(tmax, sacc[rb][r]);
+                }
             }
-            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+            tmax = halves_max(tmax);
             const bool raise = tmax > m_r[rb] + kRescaleSlack;
             if (__any(raise)) {
                 const float mnew = raise ? tmax : m_r[rb];
@@ -396,13 +477,13 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(sacc[rb][r] - msafe);
                 const float p1 = __builtin_amdgcn_exp2f(sacc[rb][r + 1] - msafe);
-                const uint32_t hi = pack_bf16_finite(p0, p1);
+                const uint32_t hi = cvt_pk_bf16(p0, p1);
                 psum += p0 + p1;
                 pk[r >> 1] = hi;
-                pl[r >> 1] =
-                    pack_bf16_finite(p0 - bf16_to_f32(hi & 0xffffu), p1 - bf16_to_f32(hi >> 16));
+                pl[r >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
+                                         p1 - __uint_as_float(hi & 0xffff0000u));
             }
-            psum += shfl_xor(psum, 32);
+            psum = halves_sum(psum);
             l_r[rb] += psum;
             pb[rb][0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
             pb[rb][1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
@@ -413,10 +494,10 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         // V(cseq) has landed once at most V(j > cseq) and K(j >= cseq + 2) are
         // in flight.
         wait_groups((nv - 1 - cseq) + max(0, nk - (cseq + 2)));
-        if (ks + kTile > cc.end) {
-            // Rows past the chunk end may hold anything (NaN included): zero
+        if (ks + kTile > cend) {
+            // Rows past the last key may hold anything (NaN included): zero
             // their values so that P = 0 contributes exactly nothing.
-            const int nv = cc.end - ks;
+            const int nv = cend - ks;
             for (int idx = lane; idx < (kTile - nv) * T::kRowChunks; idx += 64) {
                 const int row = nv + idx / T::kRowChunks, c = idx % T::kRowChunks;
                 *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa_xor<D, F8>(row))) =
@@ -425,37 +506,41 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
         }
 
         // O^T += V^T P^T.  Slot 8h + 4a + r of step tt is key 16tt + 8a + 4h + r.
+        // Every V fragment is read from LDS before the first MFMA.
+        u32x4 vf[2][NDB];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const char* vp = vtile + 16 * tt * T::kRowBytes;
-                u32x4 vf;
                 if constexpr (F8) {
                     const u32x2 raw = lds_read_tr8(vp + voff[db][0]);
-                    vf = e4m3x8_to_bf16(raw.x, raw.y);
+                    vf[tt][db] = u32x4{raw.x, raw.y, 0u, 0u};
                 } else {
                     const u32x2 v0 = lds_read_tr16(vp + voff[db][0]);
                     const u32x2 v1 = lds_read_tr16(vp + voff[db][1]);
-                    vf = u32x4{v0.x, v0.y, v1.x, v1.y};
-                }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    o[rb][db] = mfma_32x32x16(vf, pb[rb][tt], o[rb][db]);
-                    o[rb][db] = mfma_32x32x16(vf, pbl[rb][tt], o[rb][db]);
+                    vf[tt][db] = u32x4{v0.x, v0.y, v1.x, v1.y};
                 }
             }
-        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const u32x4 a = F8 ? e4m3x8_to_bf16(vf[tt][db][0], vf[tt][db][1]) : vf[tt][db];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    o[rb][db] = mfma_32x32x16(a, pb[rb][tt], o[rb][db]);
+                    o[rb][db] = mfma_32x32x16(a, pbl[rb][tt], o[rb][db]);
+                }
+            }
 
-        // This tile's stages are read: refill them three (K) and two (V)
-        // tiles ahead in the wave's stream.
+        // This tile's stages are read: refill them kKStages (K) and
+        // kVStages (V) tiles ahead in the wave's stream.
         issue_k();
         issue_v();
-        const int ns_b = (cc.L + NQ + chunk - 1) / chunk;
-        const bool last_of_pair = cc.split == ns_b - 1;
-        if (cc.t == cc.ntiles - 1 && (last_of_pair || cc.item + 1 >= cc.hi)) {
-            const size_t pbase = ((size_t)cc.b * Hkv + cc.kvh) * max_splits;
-            if (seg_split0 == 0 && last_of_pair) {
+        const bool last_of_pair = cc.t == cc.P - 1;
+        if (last_of_pair || cc.g + 1 >= cc.hi) {
+            if (seg_t0 == 0 && last_of_pair) {
                 // The segment covers the whole pair: normalised rows straight
                 // to the output.  Lane (ln, lh) holds dims 8(r/4) + 4lh + r%4.
 #pragma unroll
@@ -482,9 +567,10 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
                             }
                         }
                 }
-                if (lane == 0) part_ml[pbase * R] = make_float2(-INFINITY, kPartDirect);
             } else {
-                const size_t pidx = pbase + seg_split0;
+                // Partial rows in the wave's slot: 2w for its first segment,
+                // 2w + 1 for its last.
+                const size_t pidx = 2 * (size_t)gw + (first_seg ? 0 : 1);
                 float* po = part_o + pidx * D * R;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
@@ -498,28 +584,25 @@ __global__ __launch_bounds__(256, 1) void attn_gqa_stream(
                                 F8 ? o[rb][db][r] * vsc : o[rb][db][r];
                     if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
                 }
-                for (int sp = seg_split0 + 1 + lane; sp <= cc.split; sp += 64)
-                    part_ml[(pbase + sp) * R] = make_float2(-INFINITY, kPartEmpty);
             }
-            seg_b = -1;  // the next item starts a new segment
+            first_seg = false;
         }
-        cursor_next(cc, NRC, NQ, chunk, first, seq_lens);
+        cursor_next(cc, B, first, seq_lens);
         ++cseq;
     }
 }
 
-// first[b] = number of non-empty key chunks of the valid requests before b
-// (exclusive prefix sum), first[B] = their total.  One block.
+// first[b] = number of 32-key tiles of the valid requests before b (exclusive
+// prefix sum), first[B] = their total.  One block.
 __global__ __launch_bounds__(1024) void attn_items(const int32_t* __restrict__ seq_lens,
                                                    const int32_t* __restrict__ valid,
-                                                   int32_t* __restrict__ first, int B, int NQ,
-                                                   int chunk) {
+                                                   int32_t* __restrict__ first, int B, int NQ) {
     __shared__ int32_t s_sum[1024];
     __shared__ int32_t s_carry;
     if (threadIdx.x == 0) s_carry = 0;
     for (int b0 = 0; b0 < B; b0 += 1024) {
         const int b = b0 + threadIdx.x;
-        const int n = (b < B && valid[b]) ? (seq_lens[b] + NQ + chunk - 1) / chunk : 0;
+        const int n = (b < B && valid[b]) ? (seq_lens[b] + NQ + kTile - 1) / kTile : 0;
         s_sum[threadIdx.x] = n;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
@@ -540,9 +623,11 @@ int g_num_cus = 0;
 
 }  // namespace
 
-// Item plan, then the persistent kernel: one 4-wave workgroup per CU.
+// Tile prefix, then the persistent kernel: gqa_groups_per_cu 4-wave
+// workgroups per CU, at most max_waves waves in all.  *nw receives the number
+// of waves launched (the combine needs it to find each pair's slots).
 int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, float* po,
-               float2* pml, int R, int chunk, int max_splits, float scale_log2, hipStream_t s) {
+               float2* pml, int R, int max_waves, float scale_log2, int* nw, hipStream_t s) {
     if (g_num_cus == 0) {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -551,19 +636,21 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, floa
             return fail(SD_EDEVICE, "sd_verify_attn: cannot query the CU count");
         g_num_cus = n;
     }
-    const long n_items = (long)max_splits * d->batch * d->n_kv_heads;
-    if (n_items > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_verify_attn: too many chunks");
-    attn_items<<<1, 1024, 0, s>>>(d->seq_lens, valid, first, d->batch, d->num_q, chunk);
+    attn_items<<<1, 1024, 0, s>>>(d->seq_lens, valid, first, d->batch, d->num_q);
     int rc = check_launch("attn_items");
     if (rc != SD_OK) return rc;
     const int G = d->n_q_heads / d->n_kv_heads;
+    const bool f8 = d->kv_format == SD_KV_E4M3;
+    // gqa_groups_per_cu of the variant launched (it does not depend on D)
+    const int groups = (f8 && R <= 32) ? gqa_groups_per_cu<128, 1, true>()
+                                       : gqa_groups_per_cu<128, 2, false>();
+    const int grid = std::min(g_num_cus * groups, max_waves / 4);
+    *nw = 4 * grid;
 #define SDV_LAUNCH_GQA(DD, RBB, F8)                                                              \
-    attn_gqa_stream<DD, RBB, F8><<<g_num_cus, 256, 0, s>>>(                                      \
+    attn_gqa_stream<DD, RBB, F8><<<grid, 256, 0, s>>>(                                           \
         (const uint16_t*)d->q, (const char*)d->k_cache, (const char*)d->v_cache, d->page_table,  \
         d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp, d->batch, d->num_q,         \
-        d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, chunk, max_splits, scale_log2,          \
-        d->k_scale, d->v_scale)
-    const bool f8 = d->kv_format == SD_KV_E4M3;
+        d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, scale_log2, d->k_scale, d->v_scale)
     if (d->d_qk == 128) {
         if (f8) {
             if (R <= 32) SDV_LAUNCH_GQA(128, 1, true); else SDV_LAUNCH_GQA(128, 2, true);

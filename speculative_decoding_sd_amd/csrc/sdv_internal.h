@@ -18,19 +18,17 @@ void clear_error();
 // SD_EDEVICE with the HIP error text if the last launch failed, else SD_OK.
 int check_launch(const char* what);
 
-// Markers in the l field of row 0 of a GQA chunk-partial slot (a real l is
-// >= 0).  A wave that runs several consecutive chunks of one (request, kv head)
-// keeps them in registers and writes one partial at its first chunk's slot,
-// marking the slots of its other chunks empty; when it ran every chunk of the
-// pair it writes the output rows itself and marks slot 0 direct.
-constexpr float kPartEmpty = -1.f;
-constexpr float kPartDirect = -2.f;
-// Upper bound on the splits of one (request, kv head) the combine accepts.
+// Upper bound on the chunk partials of one (request, kv head) the combine
+// merges.
 constexpr int kCombineMaxSplits = 4096;
+// Upper bound on the waves of the GQA streaming kernel (two partial slots
+// each): 256 CUs x 2 workgroups x 4 waves.
+constexpr int kGqaMaxWaves = 2048;
 
-// GQA verify attention (attn_gqa.hip): persistent streaming kernel.
+// GQA verify attention (attn_gqa.hip): persistent streaming kernel over at
+// most max_waves waves; *nw receives the number launched.
 int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, float* po,
-               float2* pml, int R, int chunk, int max_splits, float scale_log2, hipStream_t s);
+               float2* pml, int R, int max_waves, float scale_log2, int* nw, hipStream_t s);
 
 // MLA verify attention (attn_mla.hip).
 int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits);

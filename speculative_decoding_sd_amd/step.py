@@ -4,7 +4,8 @@ VerifyStep owns the outputs and workspaces for one configuration and issues
 sd_verify_attn -> sd_lm_head -> sd_accept -> sd_kv_rollback, eagerly (run) or
 as one captured HIP graph (capture / replay).  The LM-head
 input is either a caller-supplied hidden matrix H [B*(K+1), hidden] or the
-attention output itself (rounded to the cache dtype) when H is None.
+attention output itself (rounded to q's dtype) when H is None.  An E4M3
+(uint8) cache takes its per-kv-head k_scale / v_scale.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ class VerifyStep:
     def __init__(self, *, q, k_cache, v_cache, page_table, seq_lens, num_pages, max_seq_len,
                  n_kv_heads, W, drafts, temperature, u_accept, u_sample, k_new=None,
                  v_new=None, mla=False, d_v=None, H=None, top_p=None, draft_probs=None,
-                 poison=False):
+                 poison=False, k_scale=None, v_scale=None):
         dev = q.device
         B, Q, Hq, dqk = q.shape
         self.B, self.Q, self.K = B, Q, Q - 1
@@ -34,7 +35,7 @@ class VerifyStep:
                               seq_lens=seq_lens, out=self.out, n_kv_heads=n_kv_heads,
                               num_pages=num_pages, max_seq_len=max_seq_len, k_new=k_new,
                               v_new=v_new, mla=mla, out_lowp=self.out_lowp,
-                              dev_error=self.dev_error)
+                              dev_error=self.dev_error, k_scale=k_scale, v_scale=v_scale)
         self.attn_ws = workspace(sd_verify_attn_workspace_size(self.attn), dev)
         hin = H if H is not None else self.out_lowp
         self.W = W
@@ -68,7 +69,7 @@ class VerifyStep:
                                 n_kv_heads=n_kv_heads, d_k=dqk, d_v=d_v, num_pages=num_pages,
                                 dev_error=self.dev_error)
         self._keep = (q, k_cache, v_cache, page_table, seq_lens, W, drafts, temperature,
-                      u_accept, u_sample, k_new, v_new, H, top_p, draft_probs)
+                      u_accept, u_sample, k_new, v_new, H, top_p, draft_probs, k_scale, v_scale)
 
     def _ws(self, t):
         return _aligned(t), t.numel() - (_aligned(t) - t.data_ptr())

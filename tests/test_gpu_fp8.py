@@ -167,3 +167,60 @@ def test_rollback_poison_e4m3_cache():
     assert np.array_equal(sl.cpu().numpy(), ref["seq_lens"])
     assert np.array_equal(slots.cpu().numpy(), ref["rb_slots"])
     assert np.array_equal(kc.cpu().numpy(), kch) and np.array_equal(vc.cpu().numpy(), vch)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_attention_ragged_batch_with_invalid_requests(kv):
+    """Many requests of mixed lengths (zero included), one with a bad page
+    entry: the waves' equal tile ranges cut pairs at arbitrary tiles, and the
+    combine must find every pair's partials (and skip the invalid request)."""
+    rng = np.random.default_rng(31)
+    B, K, Hq, Hkv, D = 37, 3, 16, 4, 128
+    lens = rng.integers(0, 3000, B)
+    lens[[0, 5, 9]] = [0, 1, 2999]
+    if kv == "e4m3":
+        wl = _case(B, K, Hq, Hkv, D, lens, seed=32)
+    else:
+        cfg = sdsynth.Config(name="case", batch=B, K=K, n_q_heads=Hq, n_kv_heads=Hkv, d_qk=D,
+                             d_v=D, mla=False, hidden=Hq * D, vocab=8, dtype="bf16",
+                             seq_len=None)
+        wl = sdsynth.make_workload(cfg, 32, device="cpu", seq_lens=lens, with_lm_head=False)
+    ref, _, _ = (_oracle(wl) if kv == "e4m3" else _oracle_bf16(wl))
+    bad = 11
+    wl.page_table[bad, 0] = wl.num_pages + 3
+    if kv == "e4m3":
+        out, _, _, _, err = _run_gpu(wl)
+    else:
+        out, err = _run_gpu_bf16(wl)
+    o = out.cpu().numpy()
+    assert err & sdv.SD_DERR_PAGE
+    assert np.isnan(o[bad]).all()
+    keep = np.arange(B) != bad
+    check_attention(o[keep], ref[keep], where=f"ragged batch {kv}")
+
+
+def _oracle_bf16(wl):
+    t = wl.tensors
+    kc, vc = host(t["k_cache"]).copy(), host(t["v_cache"]).copy()
+    oracle.kv_append(wl.seq_lens, wl.page_table, wl.num_pages, host(t["k_new"]),
+                     host(t["v_new"]), kc, vc)
+    ref = oracle.verify_attn(host(t["q"]), kc, vc, wl.page_table, wl.seq_lens, wl.num_pages,
+                             n_kv_heads=wl.cfg.n_kv_heads, d_v=wl.cfg.d_v)
+    return ref, kc, vc
+
+
+def _run_gpu_bf16(wl):
+    t = wl.tensors
+    q, kc, vc = t["q"].to(DEV), t["k_cache"].to(DEV), t["v_cache"].to(DEV)
+    pt = torch.tensor(wl.page_table, device=DEV)
+    sl = torch.tensor(wl.seq_lens, device=DEV)
+    B, Q, Hq, D = q.shape
+    out = torch.full((B, Q, Hq, D), -5.0, dtype=torch.float32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    d = sdv.attn_desc(q=q, k_cache=kc, v_cache=vc, page_table=pt, seq_lens=sl, out=out,
+                      n_kv_heads=wl.cfg.n_kv_heads, num_pages=wl.num_pages,
+                      max_seq_len=int(wl.seq_lens.max()), k_new=t["k_new"].to(DEV),
+                      v_new=t["v_new"].to(DEV), dev_error=err)
+    sdv.verify_attn(d)
+    torch.cuda.synchronize()
+    return out, int(err.item())
