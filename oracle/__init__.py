@@ -149,10 +149,11 @@ def kv_append(seq_lens, page_table, num_pages, k_new, v_new, k_cache, v_cache, *
 
 def verify_attn(q, k_cache, v_cache, page_table, seq_lens, num_pages, *, n_kv_heads,
                 d_v, mla=False, page_size=64, scale=None, sel=None, k_scale=None,
-                v_scale=None):
+                v_scale=None, tree_parent=None):
     """fp64 attention outputs.  q: [B, Q, Hq, d_qk].  sel: optional int array
     [n, 3] of (b, i, h).  uint8 caches hold E4M3 codes scaled per kv head by
-    k_scale / v_scale.  Returns [B, Q, Hq, d_v] or [n, d_v] float64."""
+    k_scale / v_scale.  tree_parent: optional int [B, Q] parent of each new
+    position (tree attention mask).  Returns [B, Q, Hq, d_v] or [n, d_v]."""
     q = _c(q)
     B, Q, Hq, dqk = q.shape
     if scale is None:
@@ -179,7 +180,7 @@ def verify_attn(q, k_cache, v_cache, page_table, seq_lens, num_pages, *, n_kv_he
         B, Q, Hq, n_kv_heads, dqk, d_v, int(mla), page_size, page_table.shape[1],
         int(num_pages), ctypes.c_double(scale), dt, kdt, _ptr(q), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(seq_lens),
-        n_sel, _ptr(sel), _ptr(out))
+        n_sel, _ptr(sel), _ptr(out), _ptr(_c(tree_parent, np.int32)))
     if rc != 0:
         raise ValueError(f"orc_verify_attn failed ({rc})")
     return out
@@ -205,11 +206,12 @@ def lm_head(H, W, rows=None):
 
 
 def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample,
-           relaxed_topk=None, relaxed_delta=None):
+           relaxed_topk=None, relaxed_delta=None, tree_parent=None):
     """Returns dict with num_accepted, out_tokens, next_token, out_offsets,
-    packed, diag, n_invalid.  logits: [B, K+1, V] float32/float64/bf16 bits.
-    relaxed_topk / relaxed_delta ([B] int / float, optional): relaxed
-    acceptance for greedy requests with top-N > 0 (orc_accept_ex)."""
+    packed, accepted_nodes, diag, n_invalid.  logits: [B, K+1, V]
+    float32/float64/bf16 bits.  relaxed_topk / relaxed_delta ([B] int /
+    float, optional): relaxed acceptance for greedy requests with top-N > 0.
+    tree_parent ([B, K+1] int, optional): greedy tree verification."""
     logits = _c(logits)
     B, Q, V = logits.shape
     K = Q - 1
@@ -222,14 +224,17 @@ def accept(logits, drafts, temperature, top_p, draft_probs, u_accept, u_sample,
     out = dict(
         num_accepted=np.empty(B, np.int32), out_tokens=np.empty((B, Q), np.int32),
         next_token=np.empty(B, np.int32), out_offsets=np.empty(B + 1, np.int32),
-        packed=np.empty(B * Q, np.int32), diag=np.empty((B, 4), np.float64))
+        packed=np.empty(B * Q, np.int32), diag=np.empty((B, 4), np.float64),
+        accepted_nodes=np.empty((B, Q), np.int32))
+    tp_arr = _c(tree_parent, np.int32) if tree_parent is not None else None
     rk = _c(relaxed_topk, np.int32) if relaxed_topk is not None else None
     rd = _c(relaxed_delta, np.float32) if relaxed_delta is not None else None
     n_bad = lib().orc_accept_ex(
         B, K, V, _dtype_code(logits), _ptr(logits), _ptr(drafts), _ptr(temperature),
         _ptr(top_p), _ptr(draft_probs), _ptr(u_accept), _ptr(u_sample), _ptr(rk), _ptr(rd),
         _ptr(out["num_accepted"]), _ptr(out["out_tokens"]), _ptr(out["next_token"]),
-        _ptr(out["out_offsets"]), _ptr(out["packed"]), _ptr(out["diag"]))
+        _ptr(out["out_offsets"]), _ptr(out["packed"]), _ptr(out["diag"]), _ptr(tp_arr),
+        _ptr(out["accepted_nodes"]))
     out["n_invalid"] = n_bad
     return out
 
@@ -247,9 +252,12 @@ def argmax(logits):
 
 
 def kv_rollback(page_table, num_accepted, seq_lens, K, *, page_size=64, poison=False,
-                k_cache=None, v_cache=None, n_kv_heads=1, d_k=0, d_v=0, mla=False):
+                k_cache=None, v_cache=None, n_kv_heads=1, d_k=0, d_v=0, mla=False,
+                accepted_nodes=None):
     """Returns dict with new seq_lens, rb_slots, rb_offsets, freed, freed_offsets,
-    n_bad.  Poison zeroes rejected slots of the given cache copies in place."""
+    n_bad.  Poison zeroes rejected slots of the given cache copies in place.
+    accepted_nodes ([B, K+1], tree of drafts): the accepted path's rows are
+    gathered to contiguous slots first (in place in the cache copies)."""
     page_table = _c(page_table, np.int32)
     num_accepted = _c(num_accepted, np.int32)
     sl = np.array(seq_lens, dtype=np.int32, copy=True)
@@ -262,7 +270,7 @@ def kv_rollback(page_table, num_accepted, seq_lens, K, *, page_size=64, poison=F
         B, K, page_size, page_table.shape[1], _ptr(page_table), _ptr(num_accepted),
         _ptr(sl), _ptr(out["rb_slots"]), _ptr(out["rb_offsets"]), _ptr(out["freed"]),
         _ptr(out["freed_offsets"]), int(poison), n_kv_heads, d_k, d_v, int(mla), dt,
-        _ptr(k_cache), _ptr(v_cache))
+        _ptr(k_cache), _ptr(v_cache), _ptr(_c(accepted_nodes, np.int32)))
     out["seq_lens"] = sl
     out["n_bad"] = n_bad
     return out

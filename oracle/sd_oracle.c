@@ -39,7 +39,11 @@
  *     mass reaches top_p, extended to every token tied with its last logit;
  *   - an FP8 KV cache holds OCP E4M3 ("fn") codes with one key scale and one
  *     value scale per kv head; appending stores the nearest code (ties to
- *     even, saturating at 448, NaN kept) of value / scale.
+ *     even, saturating at 448, NaN kept) of value / scale;
+ *   - a tree of drafts lists its nodes in topological order (root 0,
+ *     parent[i] < i); a node attends to its ancestors and itself; greedy
+ *     verification descends through the first child (by index) that matches
+ *     the argmax; the accepted path's rows are gathered to contiguous slots.
  */
 #include <math.h>
 #include <stdint.h>
@@ -266,6 +270,22 @@ int orc_kv_append_e4m3(int B, int Q, int n_kv_heads, int d_k, int d_v, int page_
 }
 
 /*
+ * A tree of Q nodes per request in topological order: parent[0] = -1 and
+ * 0 <= parent[i] < i for i >= 1.  Returns 1 if every request's tree is
+ * well formed.
+ */
+int orc_tree_valid(int B, int Q, const int* parent) {
+    for (int b = 0; b < B; ++b) {
+        if (Q > 0 && parent[(size_t)b * Q] != -1) return 0;
+        for (int i = 1; i < Q; ++i) {
+            int p = parent[(size_t)b * Q + i];
+            if (p < 0 || p >= i) return 0;
+        }
+    }
+    return 1;
+}
+
+/*
  * Verify attention for the K+1 queries of each request, over a cache that
  * already holds the appended positions.  Query i of request b and head h
  * attends to keys 0 .. L_b+i (a causal mask over the K+1 new positions,
@@ -280,6 +300,15 @@ int orc_kv_append_e4m3(int B, int Q, int n_kv_heads, int d_k, int d_v, int page_
  * FP8 cache (kv_dtype ORC_E4M3, GQA): k_p = code_value * k_scale[kv head] and
  * v_p = code_value * v_scale[kv head], elementwise; q stays in `dtype`.
  *
+ * Tree of drafts (tree_parent, [B][Q], optional): the Q new positions are the
+ * nodes of a tree in topological order, node 0 the root (parent -1) and
+ * parent[i] < i for the others.  Node i attends to the cached keys 0 .. L_b-1
+ * and to the new keys L_b + a for a = i and every ancestor of i -- the tree
+ * attention mask that replaces the causal one when the drafts form a tree
+ * ([TRT-MTP] "工作展望", Fig. 9: tree instead of chain drafting).  A chain
+ * (parent[i] = i - 1) is the causal case.  An ill-formed tree is an
+ * argument error.
+ *
  * sel: n_sel triples (b, i, h) to evaluate, or NULL for every (b, i, h) in
  * that order.  out: [n_sel][d_v] doubles.
  */
@@ -287,8 +316,10 @@ int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla
                        int page_size, int max_pages, int num_pages, double scale, int dtype,
                        int kv_dtype, const void* q, const void* k_cache, const void* v_cache,
                        const float* k_scale, const float* v_scale, const int* page_table,
-                       const int* seq_lens, int n_sel, const int* sel, double* out) {
+                       const int* seq_lens, int n_sel, const int* sel, double* out,
+                       const int* tree_parent) {
     if (kv_dtype == ORC_E4M3 && (mla || !k_scale || !v_scale)) return ORC_EARG;
+    if (tree_parent && !orc_tree_valid(B, Q, tree_parent)) return ORC_EARG;
     long total = sel ? n_sel : (long)B * Q * Hq;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
@@ -309,6 +340,12 @@ int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla
             continue;
         }
         long n = (long)seq_lens[b] + i + 1;  /* keys 0 .. L_b + i */
+        long Lb = seq_lens[b];
+        /* vis[a]: new key L_b + a is visible (chain: every a <= i) */
+        unsigned char* vis = (unsigned char*)malloc((size_t)Q);
+        for (int a = 0; a < Q; ++a) vis[a] = tree_parent ? 0 : (a <= i);
+        if (tree_parent)
+            for (int a = i; a >= 0; a = tree_parent[(size_t)b * Q + a]) vis[a] = 1;
         int kvh = mla ? 0 : (int)((long)h * Hkv / Hq);
         double ks = kv_dtype == ORC_E4M3 ? (double)k_scale[kvh] : 1.0;
         double vs = kv_dtype == ORC_E4M3 ? (double)v_scale[kvh] : 1.0;
@@ -316,6 +353,10 @@ int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla
         size_t qoff = (((size_t)b * Q + i) * Hq + h) * d_qk;
         double m = -INFINITY;
         for (long p = 0; p < n; ++p) {
+            if (p >= Lb && !vis[p - Lb]) {
+                sc[p] = -INFINITY;
+                continue;
+            }
             long pg = phys_page(page_table, max_pages, num_pages, b, p, page_size);
             if (pg < 0) {
                 bad |= 2;
@@ -339,6 +380,7 @@ int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla
         }
         for (int d = 0; d < d_v; ++d) o[d] = 0.0;
         for (long p = 0; p < n; ++p) {
+            if (p >= Lb && !vis[p - Lb]) continue;
             long pg = phys_page(page_table, max_pages, num_pages, b, p, page_size);
             if (pg < 0) continue;
             long off = p % page_size;
@@ -350,6 +392,7 @@ int orc_verify_attn_ex(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla
         }
         for (int d = 0; d < d_v; ++d) o[d] /= denom;
         free(sc);
+        free(vis);
     }
     return bad ? ORC_EPAGE : ORC_OK;
 }
@@ -361,7 +404,7 @@ int orc_verify_attn(int B, int Q, int Hq, int Hkv, int d_qk, int d_v, int mla,
                     double* out) {
     return orc_verify_attn_ex(B, Q, Hq, Hkv, d_qk, d_v, mla, page_size, max_pages, num_pages,
                               scale, dtype, dtype, q, k_cache, v_cache, NULL, NULL, page_table,
-                              seq_lens, n_sel, sel, out);
+                              seq_lens, n_sel, sel, out, NULL);
 }
 
 /*
@@ -588,7 +631,7 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
                   const float* draft_probs, const float* u_accept, const float* u_sample,
                   const int* relaxed_topk, const float* relaxed_delta, int* num_accepted,
                   int* out_tokens, int* next_token, int* out_offsets, int* packed,
-                  double* diag);
+                  double* diag, const int* tree_parent, int* accepted_nodes);
 
 static int relaxed_accepts(const void* row, int dtype, int V, int N, double delta, int d,
                            double* margin) {
@@ -621,7 +664,7 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
                int* packed, double* diag) {
     return orc_accept_ex(B, K, V, logits_dtype, logits, drafts, temperature, top_p, draft_probs,
                          u_accept, u_sample, NULL, NULL, num_accepted, out_tokens, next_token,
-                         out_offsets, packed, diag);
+                         out_offsets, packed, diag, NULL, NULL);
 }
 
 /*
@@ -632,13 +675,24 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
  * ignore it.  A negative top-N, or a bad delta for a relaxed greedy request,
  * makes the request invalid.  Either array may be NULL (strict).  For
  * relaxed requests diag[1] holds the smallest margin of relaxed_accepts.
+ *
+ * Tree of drafts (tree_parent [B][K+1], optional; node 0 is the root, node
+ * n >= 1 carries draft n, parent[n] < n): greedy verification walks down
+ * from the root, at node c accepting its first child (smallest node index)
+ * whose draft equals the argmax of row c, until no child matches; the final
+ * token is the argmax of the last accepted node's row, and the accepted
+ * drafts are those along the path ([TRT-MTP] "工作展望", Fig. 9; a chain is
+ * the case parent[n] = n - 1).  A negative draft id marks an unused node.
+ * A malformed tree, a sampled request or a relaxed request with a tree is
+ * invalid.  accepted_nodes [B][K+1] (optional, also without a tree) receives
+ * the node path: 0, the accepted nodes, then -1.
  */
 int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
                   const int* drafts, const float* temperature, const float* top_p,
                   const float* draft_probs, const float* u_accept, const float* u_sample,
                   const int* relaxed_topk, const float* relaxed_delta, int* num_accepted,
                   int* out_tokens, int* next_token, int* out_offsets, int* packed,
-                  double* diag) {
+                  double* diag, const int* tree_parent, int* accepted_nodes) {
     const int Q = K + 1;
     size_t es = elem_size(logits_dtype);
     int n_invalid = 0;
@@ -656,12 +710,20 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
         if (rN < 0) ok = 0;
         if (ok && T == 0 && rN > 0 && (!relaxed_delta || !isfinite(rdelta) || rdelta < 0)) ok = 0;
         if (ok && T > 0 && K > 0 && !draft_probs) ok = 0;
+        if (ok && tree_parent) {
+            const int* par = tree_parent + (size_t)b * Q;
+            if (!orc_tree_valid(1, Q, par) || T != 0.0 || rN > 0) ok = 0;
+        }
         for (int n = 0; ok && n < K; ++n)
             if (drafts[(size_t)b * K + n] >= V) ok = 0;
         for (int i = 0; ok && i < Q; ++i)
             if (!row_valid(base + (size_t)i * V * es, logits_dtype, V)) ok = 0;
         for (int i = 0; i < Q; ++i) out_tokens[(size_t)b * Q + i] = -1;
+        int* path = accepted_nodes ? accepted_nodes + (size_t)b * Q : NULL;
+        if (path)
+            for (int i = 0; i < Q; ++i) path[i] = i == 0 ? 0 : -1;
         if (!ok) {
+            if (path) path[0] = -1;
             num_accepted[b] = -1;
             next_token[b] = -1;
             ++n_invalid;
@@ -669,7 +731,26 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
             continue;
         }
         int j = 0, f = -1;
-        if (T == 0.0 && rN > 0) {
+        if (tree_parent) {
+            const int* par = tree_parent + (size_t)b * Q;
+            double mg;
+            int cur = 0;
+            int t = row_argmax(base, logits_dtype, V, &mg);
+            dg[0] = mg;
+            for (;;) {
+                int next = -1;
+                for (int c = cur + 1; c < Q && next < 0; ++c)
+                    if (par[c] == cur && drafts[(size_t)b * K + c - 1] == t) next = c;
+                if (next < 0) break;
+                ++j;
+                if (path) path[j] = next;
+                out_tokens[(size_t)b * Q + j - 1] = t;
+                cur = next;
+                t = row_argmax(base + (size_t)cur * V * es, logits_dtype, V, &mg);
+                if (mg < dg[0]) dg[0] = mg;
+            }
+            f = t;
+        } else if (T == 0.0 && rN > 0) {
             /* Relaxed: draft n is accepted while it is a surviving top-N
              * candidate of row n-1; the final token is the argmax of row j. */
             while (j < K) {
@@ -737,7 +818,11 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
         }
         num_accepted[b] = j;
         next_token[b] = f;
-        for (int n = 0; n < j; ++n) out_tokens[(size_t)b * Q + n] = drafts[(size_t)b * K + n];
+        if (!tree_parent) {
+            for (int n = 0; n < j; ++n) out_tokens[(size_t)b * Q + n] = drafts[(size_t)b * K + n];
+            if (path)
+                for (int n = 1; n <= j; ++n) path[n] = n;
+        }
         out_tokens[(size_t)b * Q + j] = f;
         if (diag) memcpy(diag + 4 * (size_t)b, dg, sizeof dg);
     }
@@ -770,12 +855,20 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
  *             page_size)), freed_offsets[B+1].
  * seq_lens is updated in place.  If poison is set, the rejected slots of the
  * caches (every kv head; the latent row for MLA) are zeroed.
+ * Tree of drafts: accepted_nodes [B][K+1] (optional) is the accepted node
+ * path of each request (0, the j_b accepted nodes in increasing order, then
+ * -1).  Node a was appended at slot L_b + a, so the kept positions are not
+ * contiguous; the cache rows of slot L_b + path[t] are copied to slot
+ * L_b + t for t = 1 .. j_b, in increasing t (a destination is never a later
+ * source, since path[t] >= t), before any poisoning.  A path that does not
+ * start at 0, is not increasing or leaves 0 .. K counts as an invalid j_b.
  * Returns the count of invalid j_b.
  */
 int orc_kv_rollback(int B, int K, int page_size, int max_pages, const int* page_table,
                     const int* num_accepted, int* seq_lens, int* rb_slots, int* rb_offsets,
                     int* freed, int* freed_offsets, int poison, int n_kv_heads, int d_k,
-                    int d_v, int mla, int dtype, void* k_cache, void* v_cache) {
+                    int d_v, int mla, int dtype, void* k_cache, void* v_cache,
+                    const int* accepted_nodes) {
     int n_bad = 0;
     size_t es = elem_size(dtype);
     rb_offsets[0] = 0;
@@ -784,11 +877,41 @@ int orc_kv_rollback(int B, int K, int page_size, int max_pages, const int* page_
         long L = seq_lens[b];
         int j = num_accepted[b];
         long new_len;
-        if (j < 0 || j > K) {
+        const int* path = accepted_nodes ? accepted_nodes + (size_t)b * (K + 1) : NULL;
+        int path_ok = 1;
+        if (path && j >= 0 && j <= K) {
+            if (path[0] != 0) path_ok = 0;
+            for (int t = 1; t <= j && path_ok; ++t)
+                if (path[t] <= path[t - 1] || path[t] > K) path_ok = 0;
+        }
+        if (j < 0 || j > K || !path_ok) {
             ++n_bad;
             new_len = L;
         } else {
             new_len = L + j + 1;
+        }
+        if (path && new_len > L && (k_cache || v_cache)) {
+            for (int t = 1; t <= j; ++t) {
+                if (path[t] == t) continue;
+                long ps = L + path[t], pd = L + t;
+                long gs = page_table[(size_t)b * max_pages + ps / page_size];
+                long gd = page_table[(size_t)b * max_pages + pd / page_size];
+                long os = ps % page_size, od = pd % page_size;
+                if (mla) {
+                    memmove((char*)k_cache + ((size_t)gd * page_size + od) * d_k * es,
+                            (char*)k_cache + ((size_t)gs * page_size + os) * d_k * es,
+                            (size_t)d_k * es);
+                    continue;
+                }
+                for (int h = 0; h < n_kv_heads; ++h) {
+                    memmove((char*)k_cache + gqa_index(gd, h, n_kv_heads, page_size, od, d_k, 0) * es,
+                            (char*)k_cache + gqa_index(gs, h, n_kv_heads, page_size, os, d_k, 0) * es,
+                            (size_t)d_k * es);
+                    memmove((char*)v_cache + gqa_index(gd, h, n_kv_heads, page_size, od, d_v, 0) * es,
+                            (char*)v_cache + gqa_index(gs, h, n_kv_heads, page_size, os, d_v, 0) * es,
+                            (size_t)d_v * es);
+                }
+            }
         }
         int ns = 0;
         for (long p = new_len; p <= L + K; ++p) {
