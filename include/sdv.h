@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 3
+#define SD_ABI_VERSION 4
 
 /* status codes */
 #define SD_OK 0
@@ -84,6 +84,9 @@ extern "C" {
 #define SD_DERR_PARAM 16        /* temperature < 0 or NaN; top_p <= 0 or NaN while sampling;
                                    sampling with K > 0 but no draft_probs */
 #define SD_DERR_ACCEPT_COUNT 32 /* rollback given num_accepted > K */
+#define SD_DERR_TREE 64         /* a malformed draft tree (parent[0] != -1 or parent[i]
+                                   outside 0 .. i-1), a tree on a sampled or relaxed
+                                   request, or a malformed accepted-node path */
 
 /* Version of this header the library was built from (SD_ABI_VERSION). */
 int sd_abi_version(void);
@@ -124,6 +127,16 @@ const char* sd_last_error(void);
  *   out_lowp   optional, out rounded to nearest-even in `dtype`, laid out
  *              [B*(K+1)][n_q_heads*d_v] (ready as LM-head input); may be NULL
  * A request with a capacity or page-table fault gets NaN outputs.
+ *
+ * Tree of drafts (tree_parent != NULL; [TRT-MTP] "工作展望", Fig. 9: tree
+ * drafting instead of a chain).  The K+1 new positions of request b are the
+ * nodes of a tree in topological order: node 0 is the root (parent -1),
+ * every other node i has parent tree_parent[b][i] in 0 .. i-1.  Node i is
+ * still appended at position L_b+i, and query i attends to positions
+ * 0 .. L_b-1 and to L_b+a for a = i and every ancestor a of i (the causal
+ * rule is the chain parent[i] = i-1).  A malformed tree makes the request
+ * invalid (SD_DERR_TREE, NaN outputs).  Needs K+1 <= 64; GQA (either cache
+ * format) and the float32 path only.
  *
  * FP8 KV cache (kv_format = SD_KV_E4M3; GQA with dtype SD_BF16 only).  The
  * pages name FP8 attention kernels as prior art for this step ([TRT-MTP]
@@ -172,6 +185,7 @@ typedef struct sd_attn_desc {
     int kv_format;          /* SD_KV_AS_DTYPE (0) or SD_KV_E4M3 */
     const float* k_scale;   /* SD_KV_E4M3: device [n_kv_heads]; else unread */
     const float* v_scale;   /* SD_KV_E4M3: device [n_kv_heads]; else unread */
+    const int32_t* tree_parent; /* optional device [B][K+1]; NULL = chain (ABI version 4) */
 } sd_attn_desc;
 
 /* Bytes of device workspace sd_verify_attn needs for this descriptor
@@ -225,6 +239,16 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *   infinite or negative, makes the request invalid (SD_DERR_PARAM).
  * A draft id < 0 ends the chain early (the final token is then drawn from,
  *   or is the argmax of, the row that draft would have been judged by).
+ * Tree of drafts (tree_parent != NULL, the same array as sd_attn_desc's):
+ *   node n >= 1 carries draft n and logits row n is the prediction after
+ *   node n.  Greedy verification descends from the root: at accepted node c
+ *   it accepts the first child n (smallest n with parent n == c) whose draft
+ *   equals the argmax of row c, until no child matches; the final token is
+ *   the argmax of the last accepted node's row; the emitted tokens are the
+ *   drafts along the path, then the final token.  A negative draft id marks
+ *   an unused node.  Trees apply to strict greedy requests only: a sampled
+ *   or relaxed request with a tree, or a malformed tree, is invalid
+ *   (SD_DERR_TREE).
  * Each request emits j_b + 1 tokens: accepted drafts, then the final token.
  *
  * Layouts (device):
@@ -245,7 +269,11 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *   next_token   int32 [B]         the final token (or -1)
  *   out_offsets  int32 [B+1]       exclusive scan of emitted counts
  *   packed_tokens int32 [B*(K+1)]  emitted tokens back to back, then -1
- * Invalid requests (see SD_DERR_TOKEN/NONFINITE/PARAM) emit nothing.
+ *   accepted_nodes int32 [B][K+1]  optional: the accepted node path (0, the
+ *                  accepted nodes, then -1; a chain gives 0 .. j_b; all -1
+ *                  for an invalid request), the input sd_kv_rollback
+ *                  gathers a tree's kept rows with
+ * Invalid requests (see SD_DERR_TOKEN/NONFINITE/PARAM/TREE) emit nothing.
  * Returns SD_EINVAL for NULL required pointers, batch < 1, K < 0, vocab < 1
  * or an unknown logits dtype, and SD_EUNSUPPORTED for vocab > 262144.
  * ---------------------------------------------------------------------- */
@@ -269,6 +297,8 @@ typedef struct sd_accept_desc {
     int32_t* dev_error; /* optional */
     const int32_t* relaxed_topk;  /* optional (ABI version 2) */
     const float* relaxed_delta;   /* optional (ABI version 2) */
+    const int32_t* tree_parent;   /* optional (ABI version 4) */
+    int32_t* accepted_nodes;      /* optional output (ABI version 4) */
 } sd_accept_desc;
 
 int sd_accept_workspace_size(const sd_accept_desc* d, size_t* bytes);
@@ -305,7 +335,17 @@ int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* s
  *                    kind, dtype, n_kv_heads, d_k, d_v describe the caches
  *                    as in sd_attn_desc (dtype = the cache element type:
  *                    SD_F32, SD_BF16, or SD_E4M3 for an FP8 cache, whose
- *                    zero code is +0) and are read only then.
+ *                    zero code is +0) and are read only then (and for a
+ *                    tree gather).
+ *   accepted_nodes:  optional int32 [B][K+1], the path sd_accept returned for
+ *                    a tree of drafts.  Node a was appended at L_b + a, so the
+ *                    kept drafts are not contiguous: before anything else the
+ *                    cache rows of position L_b + path[t] are copied to
+ *                    L_b + t for t = 1 .. j_b (every kv head; the latent row
+ *                    for MLA), in increasing t.  A path that does not start
+ *                    at 0, does not increase or leaves 0 .. K keeps nothing
+ *                    (new_len = L_b) and sets SD_DERR_TREE.  Needs the cache
+ *                    description.
  * The page table itself is left unchanged: the caller returns freed pages
  * to its pool.
  * ---------------------------------------------------------------------- */
@@ -331,6 +371,7 @@ typedef struct sd_rollback_desc {
     void* k_cache;
     void* v_cache;
     int32_t* dev_error; /* optional */
+    const int32_t* accepted_nodes; /* optional (ABI version 4) */
 } sd_rollback_desc;
 
 int sd_kv_rollback(const sd_rollback_desc* d, void* stream);

@@ -24,6 +24,7 @@ SD_KV_AS_DTYPE, SD_KV_E4M3 = 0, 1
 SD_ATTN_GQA, SD_ATTN_MLA = 0, 1
 SD_DERR_PAGE, SD_DERR_CAPACITY, SD_DERR_TOKEN = 1, 2, 4
 SD_DERR_NONFINITE, SD_DERR_PARAM, SD_DERR_ACCEPT_COUNT = 8, 16, 32
+SD_DERR_TREE = 64
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -42,7 +43,7 @@ class AttnDesc(ctypes.Structure):
         ("num_pages", _I), ("max_seq_len", _I), ("softmax_scale", ctypes.c_float),
         ("q", _P), ("k_new", _P), ("v_new", _P), ("k_cache", _P), ("v_cache", _P),
         ("page_table", _P), ("seq_lens", _P), ("out", _P), ("out_lowp", _P), ("dev_error", _P),
-        ("kv_format", _I), ("k_scale", _P), ("v_scale", _P),
+        ("kv_format", _I), ("k_scale", _P), ("v_scale", _P), ("tree_parent", _P),
     ]
 
 
@@ -52,7 +53,7 @@ class AcceptDesc(ctypes.Structure):
         ("draft_tokens", _P), ("temperature", _P), ("top_p", _P), ("draft_probs", _P),
         ("u_accept", _P), ("u_sample", _P), ("num_accepted", _P), ("out_tokens", _P),
         ("next_token", _P), ("out_offsets", _P), ("packed_tokens", _P), ("dev_error", _P),
-        ("relaxed_topk", _P), ("relaxed_delta", _P),
+        ("relaxed_topk", _P), ("relaxed_delta", _P), ("tree_parent", _P), ("accepted_nodes", _P),
     ]
 
 
@@ -63,6 +64,7 @@ class RollbackDesc(ctypes.Structure):
         ("rollback_offsets", _P), ("freed_pages", _P), ("freed_offsets", _P),
         ("poison_rejected", _I), ("kind", _I), ("dtype", _I), ("n_kv_heads", _I), ("d_k", _I),
         ("d_v", _I), ("num_pages", _I), ("k_cache", _P), ("v_cache", _P), ("dev_error", _P),
+        ("accepted_nodes", _P),
     ]
 
 
@@ -189,14 +191,15 @@ def _keeping(tensors, desc):
 def attn_desc(*, q, k_cache, v_cache, page_table, seq_lens, out, n_kv_heads, num_pages,
               max_seq_len, k_new=None, v_new=None, mla=False, out_lowp=None,
               softmax_scale=0.0, dev_error=None, page_size=64, k_scale=None,
-              v_scale=None) -> AttnDesc:
+              v_scale=None, tree_parent=None) -> AttnDesc:
     """Caches of dtype uint8 or float8_e4m3fn hold E4M3 codes and take float32
-    per-kv-head k_scale / v_scale."""
+    per-kv-head k_scale / v_scale.  tree_parent: optional int32 [B, K+1]
+    parent of each new position (a tree of drafts)."""
     B, NQ, Hq, dqk = q.shape
     d_v = out.shape[-1]
     fp8 = sd_dtype(k_cache) == SD_E4M3
     return _keeping((q, k_cache, v_cache, page_table, seq_lens, out, k_new, v_new, out_lowp,
-                     dev_error, k_scale, v_scale), AttnDesc(
+                     dev_error, k_scale, v_scale, tree_parent), AttnDesc(
         batch=B, num_q=NQ, n_q_heads=Hq, n_kv_heads=n_kv_heads, d_qk=dqk, d_v=d_v,
         kind=SD_ATTN_MLA if mla else SD_ATTN_GQA, dtype=sd_dtype(q), page_size=page_size,
         max_pages=page_table.shape[1], num_pages=num_pages, max_seq_len=max_seq_len,
@@ -204,7 +207,8 @@ def attn_desc(*, q, k_cache, v_cache, page_table, seq_lens, out, n_kv_heads, num
         k_cache=_ptr(k_cache), v_cache=_ptr(v_cache), page_table=_ptr(page_table),
         seq_lens=_ptr(seq_lens), out=_ptr(out), out_lowp=_ptr(out_lowp),
         dev_error=_ptr(dev_error), kv_format=SD_KV_E4M3 if fp8 else SD_KV_AS_DTYPE,
-        k_scale=_ptr(k_scale) if fp8 else None, v_scale=_ptr(v_scale) if fp8 else None))
+        k_scale=_ptr(k_scale) if fp8 else None, v_scale=_ptr(v_scale) if fp8 else None,
+        tree_parent=_ptr(tree_parent)))
 
 
 def verify_attn(desc: AttnDesc, ws=None, stream=None):
@@ -228,18 +232,20 @@ def lm_head(H, W, logits, stream=None):
 def accept_desc(*, logits, draft_tokens, temperature, u_accept, u_sample, num_accepted,
                 out_tokens, next_token, out_offsets, packed_tokens, top_p=None,
                 draft_probs=None, dev_error=None, relaxed_topk=None,
-                relaxed_delta=None) -> AcceptDesc:
+                relaxed_delta=None, tree_parent=None, accepted_nodes=None) -> AcceptDesc:
     B, Q, V = logits.shape
     return _keeping((logits, draft_tokens, temperature, u_accept, u_sample, num_accepted,
                      out_tokens, next_token, out_offsets, packed_tokens, top_p, draft_probs,
-                     dev_error, relaxed_topk, relaxed_delta), AcceptDesc(
+                     dev_error, relaxed_topk, relaxed_delta, tree_parent, accepted_nodes),
+                    AcceptDesc(
         batch=B, K=Q - 1, vocab=V, logits_dtype=sd_dtype(logits), logits=_ptr(logits),
         draft_tokens=_ptr(draft_tokens), temperature=_ptr(temperature), top_p=_ptr(top_p),
         draft_probs=_ptr(draft_probs), u_accept=_ptr(u_accept), u_sample=_ptr(u_sample),
         num_accepted=_ptr(num_accepted), out_tokens=_ptr(out_tokens),
         next_token=_ptr(next_token), out_offsets=_ptr(out_offsets),
         packed_tokens=_ptr(packed_tokens), dev_error=_ptr(dev_error),
-        relaxed_topk=_ptr(relaxed_topk), relaxed_delta=_ptr(relaxed_delta)))
+        relaxed_topk=_ptr(relaxed_topk), relaxed_delta=_ptr(relaxed_delta),
+        tree_parent=_ptr(tree_parent), accepted_nodes=_ptr(accepted_nodes)))
 
 
 def accept(desc: AcceptDesc, ws=None, stream=None):
@@ -255,17 +261,18 @@ def accept(desc: AcceptDesc, ws=None, stream=None):
 def rollback_desc(*, page_table, num_accepted, seq_lens, K, rollback_slots, rollback_offsets,
                   freed_pages, freed_offsets, poison=False, k_cache=None, v_cache=None,
                   mla=False, n_kv_heads=1, d_k=0, d_v=0, num_pages=0, dev_error=None,
-                  page_size=64) -> RollbackDesc:
+                  page_size=64, accepted_nodes=None) -> RollbackDesc:
     dtype = sd_dtype(k_cache) if k_cache is not None else SD_BF16
     return _keeping((page_table, num_accepted, seq_lens, rollback_slots, rollback_offsets,
-                     freed_pages, freed_offsets, k_cache, v_cache, dev_error), RollbackDesc(
+                     freed_pages, freed_offsets, k_cache, v_cache, dev_error, accepted_nodes),
+                    RollbackDesc(
         batch=seq_lens.shape[0], K=K, page_size=page_size, max_pages=page_table.shape[1],
         page_table=_ptr(page_table), num_accepted=_ptr(num_accepted), seq_lens=_ptr(seq_lens),
         rollback_slots=_ptr(rollback_slots), rollback_offsets=_ptr(rollback_offsets),
         freed_pages=_ptr(freed_pages), freed_offsets=_ptr(freed_offsets),
         poison_rejected=int(poison), kind=SD_ATTN_MLA if mla else SD_ATTN_GQA, dtype=dtype,
         n_kv_heads=n_kv_heads, d_k=d_k, d_v=d_v, num_pages=num_pages, k_cache=_ptr(k_cache),
-        v_cache=_ptr(v_cache), dev_error=_ptr(dev_error)))
+        v_cache=_ptr(v_cache), dev_error=_ptr(dev_error), accepted_nodes=_ptr(accepted_nodes)))
 
 
 def kv_rollback(desc: RollbackDesc, stream=None):

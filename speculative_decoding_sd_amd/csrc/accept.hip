@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
     }
 }
 
-enum { kModeInvalid = 0, kModeDone = 1, kModeResidual = 2, kModeTarget = 3 };
+enum { kModeInvalid = 0, kModeDone = 1, kModeResidual = 2, kModeTarget = 3, kModeTree = 4 };
 
 // ---------------------------------------------------------------------------
 // Per-request decision and final-token draw.  One block of 1024 threads (16
@@ -661,7 +661,8 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
     const int32_t* __restrict__ relaxed_topk, const RowStat* __restrict__ stats,
     int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ next_token, int32_t* err, int K, int V) {
+    int32_t* __restrict__ next_token, int32_t* err, int K, int V,
+    const int32_t* __restrict__ tree_parent, int32_t* __restrict__ accepted_nodes) {
     __shared__ double s_exptab[64];
     exp_table_init(s_exptab);
     __syncthreads();
@@ -679,8 +680,37 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         for (int n = 0; n < K; ++n)
             if (drafts[(size_t)b * K + n] >= V) flags |= SD_DERR_TOKEN;
         int mode = kModeInvalid, j = -1, row = 0, f = -1;
+        if (!flags && tree_parent) {
+            // A tree: strict greedy requests only, well-formed parents.
+            const int32_t* par = tree_parent + (size_t)b * Q;
+            bool bad = !(temperature[b] == 0.f) ||
+                       (relaxed_topk != nullptr && relaxed_topk[b] != 0) || par[0] != -1;
+            for (int n = 1; n < Q && !bad; ++n) bad = par[n] < 0 || par[n] >= n;
+            if (bad) flags |= SD_DERR_TREE;
+        }
         if (flags) {
             set_error(err, flags);
+        } else if (tree_parent) {
+            // Descend from the root through the first child whose draft is
+            // the current node's argmax; the path and its tokens are written
+            // here (node indices in accepted_nodes, drafts in out_tokens).
+            const int32_t* par = tree_parent + (size_t)b * Q;
+            int cur = 0;
+            j = 0;
+            int t = stats[(size_t)b * Q].argmax;
+            for (;;) {
+                int next = -1;
+                for (int c = cur + 1; c < Q && next < 0; ++c)
+                    if (par[c] == cur && drafts[(size_t)b * K + c - 1] == t) next = c;
+                if (next < 0) break;
+                ++j;
+                if (accepted_nodes) accepted_nodes[(size_t)b * Q + j] = next;
+                out_tokens[(size_t)b * Q + j - 1] = t;
+                cur = next;
+                t = stats[(size_t)b * Q + cur].argmax;
+            }
+            f = t;
+            mode = kModeTree;
         } else if (temperature[b] == 0.f) {
             // Strict: the draft must be the row's argmax.  Relaxed (top-N >
             // 0): it must survive the row's top-N / delta filter.
@@ -876,12 +906,21 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         num_accepted[b] = j;
         next_token[b] = f;
         for (int k = 0; k < Q; ++k) {
+            if (mode == kModeTree && k < j) continue;  // the path's drafts, written above
             int tok = -1;
             if (mode != kModeInvalid) {
                 if (k < j) tok = drafts[(size_t)b * K + k];
                 else if (k == j) tok = f;
             }
             out_tokens[(size_t)b * Q + k] = tok;
+        }
+        if (accepted_nodes) {
+            if (mode == kModeInvalid) accepted_nodes[(size_t)b * Q] = -1;
+            else accepted_nodes[(size_t)b * Q] = 0;
+            for (int k = 1; k < Q; ++k) {
+                if (mode == kModeTree && k <= j) continue;  // written above
+                accepted_nodes[(size_t)b * Q + k] = (mode != kModeInvalid && k <= j) ? k : -1;
+            }
         }
     }
 }
@@ -1024,7 +1063,7 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
         accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
             d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
-            K, V);
+            K, V, d->tree_parent, d->accepted_nodes);
     } else {
         const float* lg = (const float*)d->logits;
         if (d->relaxed_topk)
@@ -1047,7 +1086,7 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
         accept_decide<float><<<B, kDecThreads, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
             d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
-            K, V);
+            K, V, d->tree_parent, d->accepted_nodes);
     }
     if ((rc = check_launch("accept_decide")) != SD_OK) return rc;
     accept_pack<<<1, 1024, 0, s>>>(d->num_accepted, d->out_tokens, d->out_offsets,

@@ -82,12 +82,14 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
                                      float* __restrict__ out, void* __restrict__ out_lowp,
                                      int lowp_f32, int Hq, int Dv,
                                      const float* __restrict__ k_scale,
-                                     const float* __restrict__ v_scale) {
+                                     const float* __restrict__ v_scale,
+                                     const int32_t* __restrict__ tree_parent,
+                                     uint64_t* __restrict__ anc) {
     const int i = blockIdx.x, b = blockIdx.y;
     const int L = seq_lens[b];
     const bool cap_ok =
         L >= 0 && L <= max_seq_len && (long)L + NQ <= (long)max_pages * kPage;
-    int bad_page = 0;
+    int bad_page = 0, bad_tree = 0;
     if (cap_ok) {
         const int npg = (L + NQ + kPage - 1) / kPage;
         for (int lp = threadIdx.x; lp < npg; lp += blockDim.x) {
@@ -95,12 +97,26 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
             if (pg < 0 || pg >= num_pages) bad_page = 1;
         }
     }
+    if (tree_parent)
+        for (int a = threadIdx.x; a < NQ; a += blockDim.x) {
+            const int p = tree_parent[(size_t)b * NQ + a];
+            if (a == 0 ? p != -1 : (p < 0 || p >= a)) bad_tree = 1;
+        }
     bad_page = __syncthreads_or(bad_page);
-    const bool ok = cap_ok && !bad_page;
+    bad_tree = __syncthreads_or(bad_tree);
+    const bool ok = cap_ok && !bad_page && !bad_tree;
     if (threadIdx.x == 0 && i == 0) {
         valid[b] = ok ? 1 : 0;
         if (!cap_ok) set_error(err, SD_DERR_CAPACITY);
         if (bad_page) set_error(err, SD_DERR_PAGE);
+        if (bad_tree) set_error(err, SD_DERR_TREE);
+    }
+    if (tree_parent && ok && threadIdx.x == 0) {
+        // Node i's mask: bit a set for a = i and every ancestor of i (the walk
+        // ends because parents decrease).
+        uint64_t m = 0;
+        for (int a = i; a >= 0; a = tree_parent[(size_t)b * NQ + a]) m |= 1ull << a;
+        anc[(size_t)b * NQ + i] = m;
     }
     if (!ok) {
         // Invalid request: NaN output rows (the attention kernels skip it).
@@ -333,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     const float* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     float* __restrict__ out, float* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int D,
-    int max_pages, float scale) {
+    int max_pages, float scale, const uint64_t* __restrict__ anc) {
     __shared__ float s_q[256];
     __shared__ float s_e[256];
     __shared__ float s_red[256];
@@ -349,7 +365,9 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     }
     const int G = Hq / Hkv;
     const int kvh = h / G;
-    const int n = seq_lens[b] + i + 1;
+    const int L = seq_lens[b];
+    const int n = L + i + 1;
+    const uint64_t vis = anc ? anc[(size_t)b * NQ + i] : ~0ull;  // new keys visible to node i
     for (int d = tid; d < D; d += blockDim.x) s_q[d] = q[oi + d];
     __syncthreads();
     const int NG = 256 / D;
@@ -358,7 +376,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     for (int t0 = 0; t0 < n; t0 += 256) {
         const int p = t0 + tid;
         float s = -INFINITY;
-        if (p < n) {
+        if (p < n && (p < L || ((vis >> (p - L)) & 1ull))) {
             const int pg = page_table[(size_t)b * max_pages + p / kPage];
             const float* kp = k_cache + (((size_t)pg * Hkv + kvh) * kPage + p % kPage) * D;
             float dot = 0.f;
@@ -373,7 +391,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
         }
         const float mnew = fmaxf(m, s_red[0]);
         const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
-        const float e = (p < n) ? expf(s - mnew) : 0.f;
+        const float e = (s != -INFINITY) ? expf(s - mnew) : 0.f;
         __syncthreads();
         s_e[tid] = e;
         s_red[tid] = e;
@@ -411,7 +429,8 @@ struct AttnPlan {
     int G = 0, R = 0, chunk = 0, max_splits = 0;
     int max_waves = 0;  // GQA streaming kernel: waves sized for (two slots each)
     int path = 0;  // 0 gqa bf16 (MFMA), 1 gqa f32, 2 mla bf16
-    size_t off_valid = 0, off_first = 0, off_flags = 0, off_po = 0, off_pml = 0, total = 0;
+    size_t off_valid = 0, off_first = 0, off_flags = 0, off_anc = 0, off_po = 0, off_pml = 0,
+           total = 0;
 };
 
 int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
@@ -429,6 +448,8 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
     if (d->kv_format == SD_KV_E4M3 &&
         (d->kind != SD_ATTN_GQA || d->dtype != SD_BF16))
         return fail(SD_EUNSUPPORTED, "sd_verify_attn: an E4M3 cache needs GQA with bf16 q");
+    if (d->tree_parent && (d->kind != SD_ATTN_GQA || d->num_q > 64))
+        return fail(SD_EUNSUPPORTED, "sd_verify_attn: a draft tree needs GQA and K+1 <= 64");
     if (d->n_q_heads % d->n_kv_heads != 0)
         return fail(SD_EINVAL, "sd_verify_attn: n_q_heads %% n_kv_heads != 0");
     if (d->page_size != kPage)
@@ -481,6 +502,8 @@ int plan_attn(const sd_attn_desc* d, AttnPlan* p) {
     off = align_up(off + sizeof(int32_t) * d->batch, 256);
     p->off_first = off;
     off = align_up(off + sizeof(int32_t) * (d->batch + 1), 256);
+    p->off_anc = off;
+    off = align_up(off + sizeof(uint64_t) * (size_t)d->batch * d->num_q, 256);
     p->off_flags = off;
     if (p->path == 2)
         off = align_up(off + sizeof(int32_t) *
@@ -544,20 +567,21 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     int32_t* valid = (int32_t*)(ws + p.off_valid);
+    uint64_t* anc = (uint64_t*)(ws + p.off_anc);
     const int B = d->batch, NQ = d->num_q;
     attn_validate_append<<<dim3(NQ, B), 256, 0, s>>>(
         d->seq_lens, d->page_table, valid, d->dev_error, (const uint8_t*)d->k_new,
         (const uint8_t*)d->v_new, (uint8_t*)d->k_cache, (uint8_t*)d->v_cache, NQ, d->n_kv_heads,
         d->d_qk * es, d->d_v * es, d->max_pages, d->num_pages, d->max_seq_len,
         d->kind == SD_ATTN_MLA, d->out, d->out_lowp, p.path == 1, d->n_q_heads, d->d_v,
-        fp8 ? d->k_scale : nullptr, fp8 ? d->v_scale : nullptr);
+        fp8 ? d->k_scale : nullptr, fp8 ? d->v_scale : nullptr, d->tree_parent, anc);
     if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {
         attn_f32_rows<<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
             (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
             d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ, d->n_q_heads,
-            d->n_kv_heads, d->d_qk, d->max_pages, scale);
+            d->n_kv_heads, d->d_qk, d->max_pages, scale, d->tree_parent ? anc : nullptr);
         return check_launch("attn_f32_rows");
     }
     float* po = (float*)(ws + p.off_po);
@@ -576,8 +600,8 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     }
     int32_t* first = (int32_t*)(ws + p.off_first);
     int nw = 0;
-    if ((rc = gqa_launch(d, valid, first, po, pml, p.R, p.max_waves, scale_log2, &nw, s)) !=
-        SD_OK)
+    if ((rc = gqa_launch(d, valid, first, d->tree_parent ? anc : nullptr, po, pml, p.R,
+                         p.max_waves, scale_log2, &nw, s)) != SD_OK)
         return rc;
     attn_combine<<<dim3(d->n_kv_heads, B,
                         (p.R + kCombineRows - 1) / kCombineRows),

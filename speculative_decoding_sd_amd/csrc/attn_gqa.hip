@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ first,
     float* __restrict__ part_o, float2* __restrict__ part_ml, float* __restrict__ out,
     uint16_t* __restrict__ out_lowp, int B, int NQ, int Hq, int Hkv, int G, int R, int max_pages,
-    float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+    float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const uint64_t* __restrict__ anc) {
     using T = GqaTile<D, F8, gqa_kstages<D, RB, F8>()>;
     constexpr int NS = D / 16;   // MFMA k-steps over the head dimension
     constexpr int NDB = D / 32;  // 32-dim blocks of O^T
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
 
     u32x4 qf[RB][NS];
     int lim[RB];
+    uint32_t vis_lo[RB], vis_hi[RB];  // draft tree: new keys L_b + a the row's node sees
     float m_r[RB], l_r[RB];
     float sl2 = scale_log2, vsc = 1.f;  // per pair: key scale folded in; value scale
     f32x16 o[RB][NDB];
@@ -376,10 +378,14 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
                     for (int s = 0; s < NS; ++s)
                         qf[rb][s] = *(const u32x4*)(qp + (F8 ? 32 * (s >> 1) + 8 * (s & 1) : 16 * s));
                     lim[rb] = cc.L + i;  // causal: keys 0 .. L_b + i
+                    const uint64_t m = anc ? anc[(size_t)cc.b * NQ + i] : ~0ull;
+                    vis_lo[rb] = (uint32_t)m;
+                    vis_hi[rb] = (uint32_t)(m >> 32);
                 } else {
 #pragma unroll
                     for (int s = 0; s < NS; ++s) qf[rb][s] = u32x4{0, 0, 0, 0};
                     lim[rb] = cc.L + NQ - 1;
+                    vis_lo[rb] = vis_hi[rb] = ~0u;
                 }
                 m_r[rb] = -INFINITY;
                 l_r[rb] = 0.f;
@@ -456,7 +462,16 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
                 for (int r = 0; r < 16; ++r) {
                     const int key = ks + mfma_row(r, lane);
                     const float v = sacc[rb][r] * sl2;
-                    sacc[rb][r] = (key >= cend || key > lim[rb]) ? -INFINITY : v;
+                    bool seen;
+                    if (anc) {  // a tree: key L_b + a is seen iff bit a of the node's mask
+                        const int a = key - cc.L;
+                        seen = a < 0 ||
+                               (a < 64 &&
+                                ((a < 32 ? vis_lo[rb] >> a : vis_hi[rb] >> (a - 32)) & 1u) != 0);
+                    } else {
+                        seen = key <= lim[rb];
+                    }
+                    sacc[rb][r] = (key >= cend || !seen) ? -INFINITY : v;
                     tmax = fmaxf(tmax, sacc[rb][r]);
                 }
             }
@@ -626,8 +641,9 @@ int g_num_cus = 0;
 // Tile prefix, then the persistent kernel: gqa_groups_per_cu 4-wave
 // workgroups per CU, at most max_waves waves in all.  *nw receives the number
 // of waves launched (the combine needs it to find each pair's slots).
-int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, float* po,
-               float2* pml, int R, int max_waves, float scale_log2, int* nw, hipStream_t s) {
+int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, const uint64_t* anc,
+               float* po, float2* pml, int R, int max_waves, float scale_log2, int* nw,
+               hipStream_t s) {
     if (g_num_cus == 0) {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -650,7 +666,7 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, floa
     attn_gqa_stream<DD, RBB, F8><<<grid, 256, 0, s>>>(                                           \
         (const uint16_t*)d->q, (const char*)d->k_cache, (const char*)d->v_cache, d->page_table,  \
         d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp, d->batch, d->num_q,         \
-        d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, scale_log2, d->k_scale, d->v_scale)
+        d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, scale_log2, d->k_scale, d->v_scale, anc)
     if (d->d_qk == 128) {
         if (f8) {
             if (R <= 32) SDV_LAUNCH_GQA(128, 1, true); else SDV_LAUNCH_GQA(128, 2, true);

@@ -27,8 +27,11 @@ constexpr int kGqaMaxWaves = 2048;
 
 // GQA verify attention (attn_gqa.hip): persistent streaming kernel over at
 // most max_waves waves; *nw receives the number launched.
-int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, float* po,
-               float2* pml, int R, int max_waves, float scale_log2, int* nw, hipStream_t s);
+// anc: per (request, node) masks of the new keys each node sees, or NULL for
+// the causal chain.
+int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, const uint64_t* anc,
+               float* po, float2* pml, int R, int max_waves, float scale_log2, int* nw,
+               hipStream_t s);
 
 // MLA verify attention (attn_mla.hip).
 int mla_plan(int batch, int num_q, int n_q_heads, int max_seq_len, int* chunk, int* max_splits);

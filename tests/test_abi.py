@@ -71,6 +71,9 @@ def _attn_desc(**kw):
     (dict(kv_format=1, dtype=0), sdv.SD_EUNSUPPORTED),  # E4M3 cache with f32 q
     (dict(kv_format=1, kind=1, n_kv_heads=1, d_qk=576, d_v=512), sdv.SD_EUNSUPPORTED),  # MLA
     (dict(kv_format=1, d_qk=96, d_v=96), sdv.SD_EUNSUPPORTED),
+    (dict(tree_parent=4096, kind=1, n_kv_heads=1, d_qk=576, d_v=512), sdv.SD_EUNSUPPORTED),
+    (dict(tree_parent=4096, num_q=65, n_q_heads=2, n_kv_heads=2, max_pages=8),
+     sdv.SD_EUNSUPPORTED),                                # a tree of more than 64 nodes
 ])
 def test_attention_host_validation(kw, code):
     with pytest.raises(sdv.SdvError) as e:
