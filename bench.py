@@ -92,6 +92,10 @@ def parse():
     ap.add_argument("--kv-cache", choices=("as_dtype", "e4m3"), default="as_dtype",
                     help="KV cache format: the workload's dtype (default) or FP8 E4M3 codes "
                          "with per-kv-head scales (GQA bf16 workloads)")
+    ap.add_argument("--tree", choices=("binary",), default=None,
+                    help="verify a tree of K+1 drafts instead of a chain (all requests "
+                         "greedy; GQA workloads): the complete binary tree in "
+                         "breadth-first order")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
     return ap.parse_args()
@@ -133,11 +137,17 @@ def lm_head_work(cfg):
     return flops, byts
 
 
-def synthesize_drafts(cfg, seed, logits_host_f32, temperature, top_p):
-    """Draft-model stand-in from the target logits (see module docstring)."""
+def synthesize_drafts(cfg, seed, logits_host_f32, temperature, top_p, tree_parent=None):
+    """Draft-model stand-in from the target logits (see module docstring).
+    A tree: node n copies the target token after its parent with probability
+    0.6, else a token that avoids it."""
     import sdsynth
     B, Q, V = logits_host_f32.shape
     K = Q - 1
+    if tree_parent is not None:
+        tt = np.argmax(logits_host_f32, axis=-1)
+        return (sdsynth.tree_drafts(tt, tree_parent, V, seed, p_match=1.0 - cfg.geom_p),
+                np.zeros((B, K, V), np.float32))
     greedy = temperature == 0
     drafts = np.full((B, K), -1, np.int32)
     pd = np.zeros((B, K, V), np.float32)
@@ -169,12 +179,15 @@ def cpu_baseline(cfg, seed, wl, host_inputs, n_req):
     Q = cfg.num_q
     kc, vc = sel["k_cache"], sel["v_cache"]
     s = time.perf_counter()
+    tree = sel.get("tree_parent")
+    tree_b = np.tile(tree, (B, 1)) if tree is not None else None
     oracle.kv_append(sel["seq_lens"], sel["page_table"], sel["num_pages"], sel["k_new"],
                      sel["v_new"], kc, vc, mla=cfg.mla, k_scale=sel["k_scale"],
                      v_scale=sel["v_scale"])
     ref_o = oracle.verify_attn(sel["q"], kc, vc, sel["page_table"], sel["seq_lens"],
                                sel["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
-                               mla=cfg.mla, k_scale=sel["k_scale"], v_scale=sel["v_scale"])
+                               mla=cfg.mla, k_scale=sel["k_scale"], v_scale=sel["v_scale"],
+                               tree_parent=tree_b)
     timings["attention"] = time.perf_counter() - s
     H = sel["H"] if sel["H"] is not None else ref_o.reshape(B * Q, -1)
     W = sel["W"]
@@ -188,13 +201,17 @@ def cpu_baseline(cfg, seed, wl, host_inputs, n_req):
     logits = logits.reshape(B, Q, cfg.vocab)
     lf = oracle.bf16_to_f64(logits) if cfg.dtype == "bf16" else logits.astype(np.float64)
     temp, top_p = wl.temperature[:B], wl.top_p[:B]
-    drafts, pd = synthesize_drafts(cfg, seed, lf.astype(np.float32), temp, top_p)
+    drafts, pd = synthesize_drafts(cfg, seed, lf.astype(np.float32), temp, top_p, tree)
     s = time.perf_counter()
     acc = oracle.accept(logits, drafts, temp, top_p if (top_p < 1).any() else None, pd,
-                        wl.u_accept[:B], wl.u_sample[:B])
+                        wl.u_accept[:B], wl.u_sample[:B], tree_parent=tree_b)
     timings["accept"] = time.perf_counter() - s
     s = time.perf_counter()
-    oracle.kv_rollback(sel["page_table"], acc["num_accepted"], sel["seq_lens"], cfg.K)
+    oracle.kv_rollback(sel["page_table"], acc["num_accepted"], sel["seq_lens"], cfg.K,
+                       k_cache=kc if tree is not None else None,
+                       v_cache=vc if tree is not None else None, n_kv_heads=cfg.n_kv_heads,
+                       d_k=cfg.d_qk, d_v=cfg.d_v, mla=cfg.mla,
+                       accepted_nodes=acc["accepted_nodes"] if tree is not None else None)
     timings["rollback"] = time.perf_counter() - s
     total = sum(timings.values())
     return {"value": B * Q / total, "unit": "verified positions/s", "cores": oracle.num_threads(),
@@ -277,8 +294,17 @@ def main():
                               "config": args.config}))
             sys.exit(2)
         cfg = dataclasses.replace(cfg, kv_cache=args.kv_cache)
+    tree = None
+    if args.tree:
+        if cfg.mla or cfg.num_q > 64:
+            print(json.dumps({"error": "a draft tree needs a GQA workload with K+1 <= 64",
+                              "config": args.config}))
+            sys.exit(2)
+        cfg = dataclasses.replace(cfg, temperature=0.0, top_p=1.0, mixed_modes=None)
+        tree = sdsynth.tree_parents(args.tree, cfg.num_q)
     seed = sdsynth.config_seed(args.config)
-    workload = WORKLOAD_NAMES[args.config] + ("_e4m3" if cfg.kv_cache == "e4m3" else "")
+    workload = (WORKLOAD_NAMES[args.config] + ("_e4m3" if cfg.kv_cache == "e4m3" else "") +
+                ("_tree" if tree is not None else ""))
     dev = torch.device("cuda", 0)
     extra = (args.warmup + (2 if args.graph else 1) * args.steps + 4) * cfg.num_q
     wl = sdsynth.make_workload(cfg, seed, device=dev, extra_tokens=extra)
@@ -286,6 +312,7 @@ def main():
     n_cpu = args.cpu_sample_requests or cpu_sample_size(cfg, wl.seq_lens)
     if not args.no_cpu_baseline:
         sample = gather_sample(cfg, wl, n_cpu)
+        sample["tree_parent"] = tree
     t = wl.tensors
     L0 = wl.seq_lens.copy()
     seq_lens = torch.tensor(wl.seq_lens, device=dev)
@@ -303,13 +330,15 @@ def main():
                           u_accept=ua, u_sample=us, k_new=t["k_new"], v_new=t["v_new"],
                           mla=cfg.mla, d_v=cfg.d_v, H=t.get("H"), top_p=top_p,
                           draft_probs=pd if (wl.temperature > 0).any() else None,
-                          k_scale=t.get("k_scale"), v_scale=t.get("v_scale"))
+                          k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
+                          tree_parent=(torch.tensor(np.tile(tree, (cfg.batch, 1)), device=dev)
+                                       if tree is not None else None))
     # Target logits of the first step -> synthetic drafts (outside the timed region).
     step.attention()
     step.lm_head()
     torch.cuda.synchronize()
     lg = step.logits.float().cpu().numpy()
-    d_h, pd_h = synthesize_drafts(cfg, seed, lg, wl.temperature, wl.top_p)
+    d_h, pd_h = synthesize_drafts(cfg, seed, lg, wl.temperature, wl.top_p, tree)
     drafts.copy_(torch.from_numpy(d_h))
     pd.copy_(torch.from_numpy(pd_h))
     del lg, pd_h
@@ -403,7 +432,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"C{args.config} {cfg.name}" + (
-                       ", E4M3 KV cache" if cfg.kv_cache == "e4m3" else ""),
+                       ", E4M3 KV cache" if cfg.kv_cache == "e4m3" else "") + (
+                       f", greedy {args.tree} draft tree" if tree is not None else ""),
                    "batch": B, "K": cfg.K,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.d_qk, "kv_len": (int(cfg.seq_len) if cfg.seq_len
@@ -411,7 +441,9 @@ def main():
                    "mean_kv_len": float(L_mid.mean()), "hidden": cfg.hidden,
                    "vocab": cfg.vocab, "temperature": cfg.temperature or cfg.mixed_modes,
                    "top_p": cfg.top_p, "page_size": cfg.page_size,
-                   "kv_cache": "e4m3" if cfg.kv_cache == "e4m3" else cfg.dtype},
+                   "kv_cache": "e4m3" if cfg.kv_cache == "e4m3" else cfg.dtype,
+                   "drafts": (f"{args.tree} tree of {cfg.num_q} nodes" if tree is not None
+                              else f"chain of {cfg.K}")},
         "accepted_tokens_per_sec": tok_per_s,
         "mean_emitted_per_request": acc_total / args.steps / B,
         "event_ms_per_step": ev_step_ms,

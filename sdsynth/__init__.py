@@ -346,6 +346,44 @@ def greedy_drafts(target_tokens: np.ndarray, K: int, vocab: int, seed: int,
     return d
 
 
+def tree_parents(kind: str, Q: int) -> np.ndarray:
+    """Parent array of a draft tree of Q nodes in topological order (node 0
+    the root, parent -1).  "binary": the complete binary tree in
+    breadth-first order (parent[i] = (i - 1) / 2); "chain": parent[i] = i - 1."""
+    i = np.arange(Q)
+    if kind == "binary":
+        par = (i - 1) // 2
+    elif kind == "chain":
+        par = i - 1
+    else:
+        raise ValueError(f"unknown tree kind {kind!r}")
+    par[0] = -1
+    return par.astype(np.int32)
+
+
+def tree_drafts(target_tokens: np.ndarray, parent: np.ndarray, vocab: int, seed: int,
+                p_match: float = 0.6) -> np.ndarray:
+    """Drafts for a tree: node n (1-based draft n) copies the target's token
+    after its parent, target_tokens[b, parent[n]], with probability p_match
+    (Philox uniform (b, n-1, STREAM_GEOM)), else a uniform token that avoids
+    it (uniform (b, n-1, STREAM_DRAFT))."""
+    target_tokens = np.asarray(target_tokens)
+    B, Q = target_tokens.shape
+    K = Q - 1
+    um = philox_uniforms(seed, B, max(K, 1), STREAM_GEOM).astype(np.float64)
+    ud = philox_uniforms(seed, B, max(K, 1), STREAM_DRAFT).astype(np.float64)
+    d = np.full((B, K), -1, dtype=np.int32)
+    for b in range(B):
+        for n in range(1, Q):
+            want = int(target_tokens[b, parent[n]])
+            if um[b, n - 1] < p_match:
+                d[b, n - 1] = want
+            else:
+                r = int(ud[b, n - 1] * (vocab - 1))
+                d[b, n - 1] = r if r < want else r + 1
+    return d
+
+
 def draft_probs(logits_rows: np.ndarray, seed: int, sigma: float, temperature: float,
                 top_p: float = 1.0) -> np.ndarray:
     """Draft distribution rows: softmax((l + N(0, sigma^2)) / T), optionally

@@ -5,7 +5,9 @@ sd_verify_attn -> sd_lm_head -> sd_accept -> sd_kv_rollback, eagerly (run) or
 as one captured HIP graph (capture / replay).  The LM-head
 input is either a caller-supplied hidden matrix H [B*(K+1), hidden] or the
 attention output itself (rounded to q's dtype) when H is None.  An E4M3
-(uint8) cache takes its per-kv-head k_scale / v_scale.
+(uint8) cache takes its per-kv-head k_scale / v_scale.  A tree of drafts
+(tree_parent [B, K+1]) goes to the attention and the acceptance, and the
+accepted node path to the rollback.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ class VerifyStep:
     def __init__(self, *, q, k_cache, v_cache, page_table, seq_lens, num_pages, max_seq_len,
                  n_kv_heads, W, drafts, temperature, u_accept, u_sample, k_new=None,
                  v_new=None, mla=False, d_v=None, H=None, top_p=None, draft_probs=None,
-                 poison=False, k_scale=None, v_scale=None):
+                 poison=False, k_scale=None, v_scale=None, tree_parent=None):
         dev = q.device
         B, Q, Hq, dqk = q.shape
         self.B, self.Q, self.K = B, Q, Q - 1
@@ -35,7 +37,8 @@ class VerifyStep:
                               seq_lens=seq_lens, out=self.out, n_kv_heads=n_kv_heads,
                               num_pages=num_pages, max_seq_len=max_seq_len, k_new=k_new,
                               v_new=v_new, mla=mla, out_lowp=self.out_lowp,
-                              dev_error=self.dev_error, k_scale=k_scale, v_scale=v_scale)
+                              dev_error=self.dev_error, k_scale=k_scale, v_scale=v_scale,
+                              tree_parent=tree_parent)
         self.attn_ws = workspace(sd_verify_attn_workspace_size(self.attn), dev)
         hin = H if H is not None else self.out_lowp
         self.W = W
@@ -49,12 +52,15 @@ class VerifyStep:
         self.next_token = torch.empty(B, **i32)
         self.out_offsets = torch.empty(B + 1, **i32)
         self.packed = torch.empty(B * Q, **i32)
+        # A tree's accepted node path: the rollback gathers the kept rows by it.
+        self.accepted_nodes = torch.empty((B, Q), **i32) if tree_parent is not None else None
         self.acc = accept_desc(logits=self.logits, draft_tokens=drafts, temperature=temperature,
                                u_accept=u_accept, u_sample=u_sample,
                                num_accepted=self.num_accepted, out_tokens=self.out_tokens,
                                next_token=self.next_token, out_offsets=self.out_offsets,
                                packed_tokens=self.packed, top_p=top_p, draft_probs=draft_probs,
-                               dev_error=self.dev_error)
+                               dev_error=self.dev_error, tree_parent=tree_parent,
+                               accepted_nodes=self.accepted_nodes)
         self.acc_ws = workspace(sd_accept_workspace_size(self.acc), dev)
         ps = 64
         self.rb_slots = torch.empty(B * Q, **i32)
@@ -67,9 +73,10 @@ class VerifyStep:
                                 freed_offsets=self.freed_offsets, poison=poison,
                                 k_cache=k_cache, v_cache=v_cache, mla=mla,
                                 n_kv_heads=n_kv_heads, d_k=dqk, d_v=d_v, num_pages=num_pages,
-                                dev_error=self.dev_error)
+                                dev_error=self.dev_error, accepted_nodes=self.accepted_nodes)
         self._keep = (q, k_cache, v_cache, page_table, seq_lens, W, drafts, temperature,
-                      u_accept, u_sample, k_new, v_new, H, top_p, draft_probs, k_scale, v_scale)
+                      u_accept, u_sample, k_new, v_new, H, top_p, draft_probs, k_scale, v_scale,
+                      tree_parent)
 
     def _ws(self, t):
         return _aligned(t), t.numel() - (_aligned(t) - t.data_ptr())

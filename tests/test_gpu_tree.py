@@ -234,3 +234,56 @@ def test_tree_rollback_gather(poison, kv):
     assert np.array_equal(got_k, kch) and np.array_equal(got_v, vch)
     bad_path = ref["n_bad"] > 1
     assert bool(int(err.item()) & sdv.SD_DERR_TREE) == bad_path
+
+
+def test_chained_tiny_fp32_tree_step():
+    """The tiny fp32 configuration (B=1, 4 heads x 64, L=128) with its K=3
+    drafts as a binary tree, through VerifyStep (tree attention -> LM head on
+    the attention output -> tree acceptance -> rollback gather), against the
+    oracle's chain of the same calls.  The kept cache rows must equal the
+    oracle's gathered rows."""
+    import dataclasses
+    cfg = dataclasses.replace(sdsynth.CONFIGS[1], K=6)
+    seed = sdsynth.config_seed(1)
+    wl = sdsynth.make_workload(cfg, seed, device="cpu")
+    t = wl.tensors
+    Q = cfg.num_q
+    par = np.tile(sdsynth.tree_parents("binary", Q), (cfg.batch, 1))
+    ref_o, kc_ref, vc_ref = _oracle_attention(wl, par)
+    exact = oracle.lm_head(ref_o.reshape(cfg.batch * Q, -1), t["W"].numpy().astype(np.float64))
+    ref_logits = exact.reshape(cfg.batch, Q, cfg.vocab)
+    tt, margin = oracle.argmax(ref_logits)
+    drafts = sdsynth.tree_drafts(tt, par[0], cfg.vocab, seed, p_match=0.8)
+    ref_acc = oracle.accept(ref_logits, drafts, wl.temperature, None, None, wl.u_accept,
+                            wl.u_sample, tree_parent=par)
+    ref_rb = oracle.kv_rollback(wl.page_table, ref_acc["num_accepted"], wl.seq_lens, cfg.K,
+                                k_cache=kc_ref, v_cache=vc_ref, n_kv_heads=cfg.n_kv_heads,
+                                d_k=cfg.d_qk, d_v=cfg.d_v, accepted_nodes=ref_acc["accepted_nodes"])
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    sl = torch.tensor(wl.seq_lens, device=DEV)
+    step = sdv.VerifyStep(q=d["q"], k_cache=d["k_cache"], v_cache=d["v_cache"],
+                          page_table=torch.tensor(wl.page_table, device=DEV), seq_lens=sl,
+                          num_pages=wl.num_pages, max_seq_len=int(wl.seq_lens.max()),
+                          n_kv_heads=cfg.n_kv_heads, W=d["W"],
+                          drafts=torch.tensor(drafts, device=DEV),
+                          temperature=torch.tensor(wl.temperature, device=DEV),
+                          u_accept=torch.tensor(wl.u_accept, device=DEV),
+                          u_sample=torch.tensor(wl.u_sample, device=DEV),
+                          k_new=d["k_new"], v_new=d["v_new"],
+                          tree_parent=torch.tensor(par, device=DEV))
+    step.run()
+    torch.cuda.synchronize()
+    check_attention(step.out.cpu().numpy(), ref_o, where="tree attention")
+    assert int(step.dev_error.item()) == 0
+    assert margin.reshape(-1).min() >= 1e-3, "seeded case must not sit on an argmax tie"
+    assert step.num_accepted.cpu().numpy().tolist() == ref_acc["num_accepted"].tolist()
+    assert ref_acc["num_accepted"][0] >= 1
+    assert np.array_equal(step.out_tokens.cpu().numpy(), ref_acc["out_tokens"])
+    assert np.array_equal(step.accepted_nodes.cpu().numpy(), ref_acc["accepted_nodes"])
+    assert np.array_equal(sl.cpu().numpy(), ref_rb["seq_lens"])
+    # kept rows: the GPU's appended-and-gathered f32 rows equal the oracle's
+    kc = d["k_cache"].cpu().numpy()
+    L, new_len = int(wl.seq_lens[0]), int(ref_rb["seq_lens"][0])
+    for p in range(L, new_len):
+        pg, off = wl.page_table[0, p // 64], p % 64
+        assert np.array_equal(kc[pg, :, off], kc_ref[pg, :, off]), p
