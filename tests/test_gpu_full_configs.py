@@ -120,3 +120,112 @@ def test_full_config_step(ci):
     if n_excl == 0:
         assert np.array_equal(step.rb_offsets.cpu().numpy(), rb["rb_offsets"])
         assert np.array_equal(step.rb_slots.cpu().numpy(), rb["rb_slots"])
+
+
+@pytest.mark.parametrize("ci,kv,tree", [(5, "e4m3", None), (4, "e4m3", None),
+                                        (5, "as_dtype", "binary"), (5, "e4m3", "binary")])
+def test_full_config_variants(ci, kv, tree):
+    """The E4M3 cache and the draft-tree variants bench.py times, at full size:
+    sampled attention rows, sampled LM-head rows, acceptance over the whole
+    batch on the GPU's logits, and the rollback (with the tree gather)."""
+    import dataclasses
+    cfg = dataclasses.replace(sdsynth.CONFIGS[ci], kv_cache=kv)
+    if tree:
+        cfg = dataclasses.replace(cfg, temperature=0.0, top_p=1.0, mixed_modes=None)
+    seed = sdsynth.config_seed(ci)
+    torch.cuda.empty_cache()
+    wl = sdsynth.make_workload(cfg, seed, device=DEV, extra_tokens=cfg.num_q)
+    t = wl.tensors
+    B, Q = cfg.batch, cfg.num_q
+    par = sdsynth.tree_parents(tree, Q) if tree else None
+    par_b = np.tile(par, (B, 1)) if tree else None
+    rng = np.random.default_rng(ci + 10)
+    reqs = np.sort(rng.choice(B, 2, replace=False))
+    sample = gather_requests(wl, reqs)
+    if kv == "e4m3":   # host() keeps uint8 codes as they are
+        scales = dict(k_scale=t["k_scale"].cpu().numpy(), v_scale=t["v_scale"].cpu().numpy())
+    else:
+        scales = {}
+    print(f"config {ci} {kv} {tree}: sampled requests {reqs.tolist()}", flush=True)
+    L0 = wl.seq_lens.copy()
+    seq_lens = torch.tensor(L0, device=DEV)
+    page_table = torch.tensor(wl.page_table, device=DEV)
+    temp = torch.tensor(wl.temperature, device=DEV)
+    top_p = torch.tensor(wl.top_p, device=DEV) if (wl.top_p < 1).any() else None
+    drafts = torch.full((B, cfg.K), -1, dtype=torch.int32, device=DEV)
+    pd = torch.zeros((B, cfg.K, cfg.vocab), dtype=torch.float32, device=DEV)
+    step = sdv.VerifyStep(q=t["q"], k_cache=t["k_cache"], v_cache=t["v_cache"],
+                          page_table=page_table, seq_lens=seq_lens, num_pages=wl.num_pages,
+                          max_seq_len=int(L0.max()), n_kv_heads=cfg.n_kv_heads, W=t["W"],
+                          drafts=drafts, temperature=temp,
+                          u_accept=torch.tensor(wl.u_accept, device=DEV),
+                          u_sample=torch.tensor(wl.u_sample, device=DEV), k_new=t["k_new"],
+                          v_new=t["v_new"], d_v=cfg.d_v, H=t.get("H"), top_p=top_p,
+                          draft_probs=pd if (wl.temperature > 0).any() else None,
+                          k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
+                          tree_parent=torch.tensor(par_b, device=DEV) if tree else None)
+    step.attention()
+    step.lm_head()
+    torch.cuda.synchronize()
+    assert int(step.dev_error.item()) == 0
+
+    kc, vc = sample["k_cache"], sample["v_cache"]
+    oracle.kv_append(sample["seq_lens"], sample["page_table"], sample["num_pages"],
+                     sample["k_new"], sample["v_new"], kc, vc, **scales)
+    sel = np.stack([rng.integers(0, len(reqs), 24), rng.integers(0, Q, 24),
+                    rng.integers(0, cfg.n_q_heads, 24)], 1)
+    ref = oracle.verify_attn(sample["q"], kc, vc, sample["page_table"], sample["seq_lens"],
+                             sample["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
+                             sel=sel, tree_parent=par_b[:len(reqs)] if tree else None, **scales)
+    o = step.out.cpu().numpy()
+    check_attention(np.stack([o[reqs[b], i, h] for b, i, h in sel]), ref,
+                    where=f"config {ci} {kv} {tree} attention")
+
+    rows = rng.choice(B * Q, 4, replace=False).astype(np.int32)
+    ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
+    exact = oracle.lm_head(bits(step.hin.index_select(0, ridx)), bits(t["W"]))
+    check_logits_bf16(bits(step.logits.view(B * Q, -1).index_select(0, ridx)), exact,
+                      where=f"config {ci} {kv} {tree} lm head")
+
+    lg_bits = bits(step.logits)
+    lf = oracle.bf16_to_f64(lg_bits).astype(np.float32)
+    if tree:
+        d_h = sdsynth.tree_drafts(np.argmax(lf, axis=-1), par, cfg.vocab, seed)
+        pd_h = None
+    else:
+        d_h, pd_h = _drafts(cfg, seed, lf, wl.temperature, wl.top_p)
+        pd.copy_(torch.from_numpy(pd_h))
+    del lf
+    drafts.copy_(torch.from_numpy(d_h))
+    step.accept()
+    step.rollback()
+    torch.cuda.synchronize()
+    ref_acc = oracle.accept(lg_bits, d_h, wl.temperature,
+                            wl.top_p if (wl.top_p < 1).any() else None, pd_h, wl.u_accept,
+                            wl.u_sample, tree_parent=par_b)
+    gpu = {"num_accepted": step.num_accepted.cpu().numpy(),
+           "out_tokens": step.out_tokens.cpu().numpy(),
+           "next_token": step.next_token.cpu().numpy(),
+           "out_offsets": step.out_offsets.cpu().numpy(),
+           "packed_tokens": step.packed.cpu().numpy()}
+    n_excl = compare_accept(gpu, ref_acc, where=f"config {ci} {kv} {tree} accept")
+    assert n_excl <= max(1, B // 16)
+    assert int(step.dev_error.item()) == 0
+    if tree:
+        assert np.array_equal(step.accepted_nodes.cpu().numpy(), ref_acc["accepted_nodes"])
+        assert ref_acc["num_accepted"].mean() > 0.5
+    # Rollback: lengths for every kept request; the gathered cache rows of the
+    # sampled requests against the oracle's gather of their host copies.
+    rb = oracle.kv_rollback(sample["page_table"], ref_acc["num_accepted"][reqs],
+                            sample["seq_lens"], cfg.K, k_cache=kc, v_cache=vc,
+                            n_kv_heads=cfg.n_kv_heads, d_k=cfg.d_qk, d_v=cfg.d_v,
+                            accepted_nodes=ref_acc["accepted_nodes"][reqs] if tree else None)
+    keep = ref_acc["num_accepted"] >= 0
+    assert np.array_equal(seq_lens.cpu().numpy()[keep], (L0 + ref_acc["num_accepted"] + 1)[keep])
+    kc_gpu = t["k_cache"]
+    for k, b in enumerate(reqs):
+        for p in range(int(L0[b]), int(rb["seq_lens"][k])):
+            pg_g, pg_s, off = wl.page_table[b, p // 64], sample["page_table"][k, p // 64], p % 64
+            got = kc_gpu[pg_g, :, off]
+            got = got.cpu().numpy() if kv == "e4m3" else bits(got)
+            assert np.array_equal(got, kc[pg_s, :, off]), (b, p)
