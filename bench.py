@@ -278,8 +278,9 @@ def cpu_sample_size(cfg, seq_lens, budget_s=15.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not "
-                                   "part of it (the sharding plan is documented in DESIGN.md)",
+        print(json.dumps({"error": "the verify-step benchmark runs on one GPU only; the "
+                                   "kernels shard by request, kv head or vocabulary, but "
+                                   "no multi-GPU path is implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
