@@ -634,8 +634,6 @@ __global__ __launch_bounds__(1024) void attn_items(const int32_t* __restrict__ s
     if (threadIdx.x == 0) first[B] = s_carry;
 }
 
-int g_num_cus = 0;
-
 }  // namespace
 
 // Tile prefix, then the persistent kernel: gqa_groups_per_cu 4-wave
@@ -644,23 +642,18 @@ int g_num_cus = 0;
 int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, const uint64_t* anc,
                float* po, float2* pml, int R, int max_waves, float scale_log2, int* nw,
                hipStream_t s) {
-    if (g_num_cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            return fail(SD_EDEVICE, "sd_verify_attn: cannot query the CU count");
-        g_num_cus = n;
-    }
+    int num_cus = 0;
+    int rc = cu_count("sd_verify_attn", &num_cus);
+    if (rc != SD_OK) return rc;
     attn_items<<<1, 1024, 0, s>>>(d->seq_lens, valid, first, d->batch, d->num_q);
-    int rc = check_launch("attn_items");
+    rc = check_launch("attn_items");
     if (rc != SD_OK) return rc;
     const int G = d->n_q_heads / d->n_kv_heads;
     const bool f8 = d->kv_format == SD_KV_E4M3;
     // gqa_groups_per_cu of the variant launched (it does not depend on D)
     const int groups = (f8 && R <= 32) ? gqa_groups_per_cu<128, 1, true>()
                                        : gqa_groups_per_cu<128, 2, false>();
-    const int grid = std::min(g_num_cus * groups, max_waves / 4);
+    const int grid = std::min(num_cus * groups, max_waves / 4);
     *nw = 4 * grid;
 #define SDV_LAUNCH_GQA(DD, RBB, F8)                                                              \
     attn_gqa_stream<DD, RBB, F8><<<grid, 256, 0, s>>>(                                           \

@@ -465,8 +465,16 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
     }
     if (hidden % 128 == 0) {
         // Tile rows to the batch: all rows in one tile where possible, so each
-        // W tile is streamed from HBM once.
+        // W tile is streamed from HBM once.  When that leaves CUs idle (a small
+        // vocabulary), 128-row tiles double the workgroups: the W tile is then
+        // read twice, but the stream is spread over the whole chip.
         int TM = M > 128 ? 256 : (M > 64 ? 128 : 64);
+        if (TM == 256) {
+            int num_cus = 0;
+            const int rc = cu_count("sd_lm_head", &num_cus);
+            if (rc != SD_OK) return rc;
+            if ((long)((M + 255) / 256) * ((vocab + 255) / 256) < num_cus) TM = 128;
+        }
         const long tiles = (long)((M + TM - 1) / TM) * ((vocab + 255) / 256);
         if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");
         const uint16_t* h = (const uint16_t*)H;

@@ -24,6 +24,20 @@ int check_launch(const char* what) {
     return SD_OK;
 }
 
+int cu_count(const char* what, int* n) {
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            return fail(SD_EDEVICE, "%s: cannot query the CU count", what);
+        cached = c;
+    }
+    *n = cached;
+    return SD_OK;
+}
+
 }  // namespace sdv
 
 extern "C" int sd_abi_version(void) { return SD_ABI_VERSION; }

@@ -18,6 +18,10 @@ void clear_error();
 // SD_EDEVICE with the HIP error text if the last launch failed, else SD_OK.
 int check_launch(const char* what);
 
+// Compute units of the current device (queried once per process) in *n;
+// SD_EDEVICE, reported under `what`, if the query fails.
+int cu_count(const char* what, int* n);
+
 // Upper bound on the chunk partials of one (request, kv head) the combine
 // merges.
 constexpr int kCombineMaxSplits = 4096;

@@ -151,7 +151,7 @@ def test_lm_head_exact_small_integers(M, hidden, V):
     assert np.array_equal(bits(logits), oracle.round_bf16(exact))
 
 
-@pytest.mark.parametrize("M,hidden,V", [(192, 1024, 1500), (64, 5120, 1111)])
+@pytest.mark.parametrize("M,hidden,V", [(192, 1024, 1500), (64, 5120, 1111), (300, 512, 700)])
 def test_lm_head_bf16_random(M, hidden, V):
     H = sdsynth.normal((M, hidden), 1.0, 3, "H", torch.bfloat16, "cpu")
     W = sdsynth.normal((V, hidden), 0.02, 3, "W", torch.bfloat16, "cpu")
