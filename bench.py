@@ -42,7 +42,8 @@ MFMA_F32_PEAK_TFS = 157.3
 WORKLOAD_NAMES = {1: "c1_tiny_fp32", 2: "c2_gqa_stochastic", 3: "c3_mla_greedy",
                   4: "c4_long_context", 5: "c5_ragged_serving"}
 # Source files whose contents a kernel's PMC traffic figure is tied to.
-KERNEL_SOURCES = {"lm_head_dma": "lm_head.hip", "attn_gqa_stream": "attn_gqa.hip",
+KERNEL_SOURCES = {"lm_head_dma": "lm_head.hip", "lm_head_ring": "lm_head.hip",
+                  "attn_gqa_stream": "attn_gqa.hip",
                   "attn_mla_bf16": "attn_mla.hip"}
 
 
@@ -56,6 +57,20 @@ def kernel_source_hash(kernel):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def lm_head_kernel(M, hidden, vocab, dtype):
+    """Name of the kernel sd_lm_head launches for this shape (its dispatch rule:
+    256-row tiles while they number at least the CUs, else the generic DMA
+    kernel with 128- or 64-row tiles), or None for the fallback paths."""
+    import torch
+    if dtype != "bf16" or hidden % 128:
+        return None
+    if M > 128:
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        if ((M + 255) // 256) * ((vocab + 255) // 256) >= cus:
+            return "lm_head_ring"
+    return "lm_head_dma"
 
 
 def profiled_traffic(kernel, workload):
@@ -421,7 +436,7 @@ def main():
     dom = max(("attention", "lm_head"), key=lambda k: per_call[k])
     roof = dict(kernels[dom])
     if dom == "lm_head":
-        dom_kernel = "lm_head_dma" if (cfg.dtype == "bf16" and cfg.hidden % 128 == 0) else None
+        dom_kernel = lm_head_kernel(cfg.batch * cfg.num_q, cfg.hidden, cfg.vocab, cfg.dtype)
     else:
         dom_kernel = "attn_mla_bf16" if cfg.mla else ("attn_gqa_stream" if cfg.dtype == "bf16" else None)
     traffic = profiled_traffic(dom_kernel, workload) if dom_kernel else None

@@ -117,10 +117,8 @@ __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restric
 // (BK = 32: four, refilled up to three stages ahead; BK = 64: two).  With
 // BK = 64 every DMA request covers whole 128-byte rows of W and H (full L2
 // lines); with BK = 32 each request is half a line.
-// WN x WM waves each own a (TN/WN) x (TM/WM) sub-tile.  The 256 x 256 tile
-// runs 8 waves of 128 x 64 (two per SIMD, accumulators in 128 registers):
-// a wave stalled on an LDS read or a barrier leaves the matrix unit to the
-// other wave of its SIMD, which outweighs the half more fragment reads.
+// WN x WM waves each own a (TN/WN) x (TM/WM) sub-tile.  This kernel serves
+// the 128- and 64-row tiles; 256 x 256 tiles use lm_head_ring below.
 // LDS layout per stage: row r (W rows then H rows) holds BK/8 granules of 16
 // bytes; granule c sits at slot c ^ f(r) (f(r) = (r/4)%4 for BK = 32,
 // (r/2)%8 for BK = 64).  A ds_read_b128 is served 16 lanes (16 rows, one
@@ -423,6 +421,175 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_dma(const uint16_t* _
     }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles.  Eight waves of 128 (vocab) x 64 (rows), two per SIMD
+// (accumulators in 128 registers): a wave waiting on an LDS read or the barrier
+// leaves the matrix unit to the other wave of its SIMD.
+// The W and H k-slices (64 wide, 32 KB each) are staged separately in a ring of
+// five LDS slots: slice j of W in slot 2j % 5, of H in slot (2j+1) % 5.  While
+// stage kt computes from its two slots, stage kt+1 is resident or landing and
+// the fifth slot receives W of kt+2.  This lets a stage's DMAs be spread over
+// all four of its k-steps (two per wave and step) rather than issued as one
+// burst after the stage barrier; the burst kept the vector-memory queue full
+// and stalled MFMA issue for about a third of every stage.
+// Barrier B_kt sits at the start of stage kt's last k-step.  Past it, stage
+// kt+1 has landed and stage kt's slots are free (every wave then holds the last
+// step's fragments in registers).  DMA issue per stage kt:
+//   step 0:     H of kt+1, ops 2-3 (ops 0-1 went out after B_{kt-1})
+//   steps 1, 2: W of kt+2, ops 0-1, then 2-3
+//   B_kt, waiting until at most W of kt+2 is in flight; step 3: H of kt+2, ops 0-1
+// Within a step the next step's six fragment reads and the two DMAs are
+// interleaved with the eight MFMAs, so neither the LDS nor the vector-memory
+// queue takes the issue slot in one block.
+// ---------------------------------------------------------------------------
+constexpr int kRingSlotBytes = 256 * 64 * 2;
+constexpr int kRingSlots = 5;
+__shared__ __attribute__((aligned(1024))) uint16_t g_ring[kRingSlots * kRingSlotBytes / 2];
+
+// DMA op i (0..3) of one operand slice into the slot at byte offset slot_off:
+// lane l of wave w writes granule g = 64 (8 i + w) + l, i.e. row g / 8, stored
+// granule g % 8 (the sources were set up by the same mapping).
+__device__ __forceinline__ void ring_dma(const uint16_t* const* src, int i, int kt,
+                                         uint32_t slot_off, int wave) {
+    const int g0 = (i * 8 + wave) * 64;
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * 64,
+                                     (__attribute__((address_space(3))) void*)(
+                                         g_ring + (slot_off + g0 * 16) / 2),
+                                     16, 0, 0);
+}
+
+// One k-step: the eight MFMAs on (ca, cb); after MFMA r < 6 the read of the
+// next step's fragment r (four of W from slot rW, then two of H from slot rH,
+// at k-step `step`); DMA op o0 after MFMA 1, op o0+1 after MFMA 3.  Every group
+// is fenced so that this order survives scheduling.
+__device__ __forceinline__ void ring_step(f32x16 (&acc)[4][2], const u32x4 (&ca)[4],
+                                          const u32x4 (&cb)[2], u32x4 (&na)[4], u32x4 (&nb)[2],
+                                          uint32_t rW, uint32_t rH, int step, int wn, int wm,
+                                          int lane, const uint16_t* const* src, int o0, int kt,
+                                          uint32_t slot_off, int wave) {
+    const int ln = lane & 31, c = 2 * step + (lane >> 5);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) {
+        acc[idx / 2][idx % 2] = mfma_32x32x16(ca[idx / 2], cb[idx % 2], acc[idx / 2][idx % 2]);
+        if (idx < 4)
+            na[idx] = ds_read16(rW + swz<64>(wn * 128 + idx * 32 + ln, c) * 16);
+        else if (idx < 6)
+            nb[idx - 4] = ds_read16(rH + swz<64>(wm * 64 + (idx - 4) * 32 + ln, c) * 16);
+        if (idx == 1) ring_dma(src, o0, kt, slot_off, wave);
+        if (idx == 3) ring_dma(src, o0 + 1, kt, slot_off, wave);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void lm_head_ring(const uint16_t* __restrict__ H,
+                                                       const uint16_t* __restrict__ W,
+                                                       uint16_t* __restrict__ C, int M, int N,
+                                                       int K) {
+    constexpr uint32_t S = kRingSlotBytes;
+    const int tiles_m = (M + 255) / 256;
+    const int tiles_n = (N + 255) / 256;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int n0 = tn * 256, m0 = tm * 256;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % 2, wm = wave / 2;
+    const int ln = lane & 31, lh = lane >> 5;
+    const uint32_t lds0 = lds_addr(g_ring);
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = K / 64;
+    // Per-lane sources of the four DMA ops of a W and an H slice at k = 0.
+    // Rows past the matrix ends re-read the last row (never stored).
+    const uint16_t* sw[4];
+    const uint16_t* sh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = (i * 8 + wave) * 64 + lane;
+        const int row = g / 8, c = (g % 8) ^ ((row >> 1) & 7);
+        sw[i] = W + (size_t)min(n0 + row, N - 1) * K + 8 * c;
+        sh[i] = H + (size_t)min(m0 + row, M - 1) * K + 8 * c;
+    }
+    // Prologue: W and H of slice 0, W of slice 1, ops 0-1 of H of slice 1
+    // (slots 0-3), then wait for slice 0.  Slices past the end re-read the
+    // last one into free slots; the kernel waits for them before it ends.
+    const int kn = min(1, nk - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ring_dma(sw, i, 0, 0, wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ring_dma(sh, i, 0, S, wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ring_dma(sw, i, kn, 2 * S, wave);
+    ring_dma(sh, 0, kn, 3 * S, wave);
+    ring_dma(sh, 1, kn, 3 * S, wave);
+    wait_vmcnt<6>();
+    block_barrier_lds();
+    u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa0[i] = ds_read16(lds0 + swz<64>(wn * 128 + i * 32 + ln, lh) * 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        fb0[j] = ds_read16(lds0 + S + swz<64>(wm * 64 + j * 32 + ln, lh) * 16);
+    wait_frags(fa0, fb0);
+    // No branch may separate an asm fragment read from its lgkmcnt wait (at a
+    // control-flow merge the compiler may copy the not yet loaded registers):
+    // the loop body is straight-line, slot indices are computed.
+    int q = 0;  // slot of W of slice kt: (2 kt) % 5
+    for (int kt = 0; kt < nk; ++kt) {
+        const int q1 = q + 1 - (q + 1 >= 5 ? 5 : 0), q2 = q + 2 - (q + 2 >= 5 ? 5 : 0);
+        const int q3 = q + 3 - (q + 3 >= 5 ? 5 : 0), q4 = q + 4 - (q + 4 >= 5 ? 5 : 0);
+        const uint32_t aW = lds0 + q * S, aH = lds0 + q1 * S;
+        const uint32_t nW = lds0 + q2 * S, nH = lds0 + q3 * S;
+        const int k1 = min(kt + 1, nk - 1), k2 = min(kt + 2, nk - 1);
+        ring_step(acc, fa0, fb0, fa1, fb1, aW, aH, 1, wn, wm, lane, sh, 2, k1, q3 * S, wave);
+        wait_frags(fa1, fb1);
+        ring_step(acc, fa1, fb1, fa0, fb0, aW, aH, 2, wn, wm, lane, sw, 0, k2, q4 * S, wave);
+        wait_frags(fa0, fb0);
+        ring_step(acc, fa0, fb0, fa1, fb1, aW, aH, 3, wn, wm, lane, sw, 2, k2, q4 * S, wave);
+        wait_frags(fa1, fb1);
+        // B_kt: slice kt+1 landed (only W of kt+2 may still be in flight).
+        wait_vmcnt<4>();
+        block_barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        ring_step(acc, fa1, fb1, fa0, fb0, nW, nH, 0, wn, wm, lane, sh, 0, k2, q * S, wave);
+        wait_frags(fa0, fb0);
+        q = q2;
+    }
+    wait_vmcnt<0>();
+
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int m = m0 + wm * 64 + j * 32 + ln;
+        if (m >= M) continue;
+        uint16_t* crow = C + (size_t)m * N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 128 + i * 32 + 8 * g + 4 * lh;
+                const f32x16& a = acc[i][j];
+                if (vec && n + 3 < N) {
+                    u32x2 w;
+                    w.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+                    w.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                    *(u32x2*)(crow + n) = w;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (n + t < N) crow[n + t] = (uint16_t)f32_to_bf16_rne(a[4 * g + t]);
+                }
+            }
+        }
+    }
+}
+
 // fp32 path: one wave per output element, lanes split k (coalesced rows),
 // fixed-order butterfly reduction.
 __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ A,
@@ -481,15 +648,14 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         const uint16_t* w = (const uint16_t*)W;
         uint16_t* c = (uint16_t*)logits;
         if (TM == 256)
-            lm_head_dma<256, 256, 2, 4, kLmBK><<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab,
-                                                                               hidden);
+            lm_head_ring<<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab, hidden);
         else if (TM == 128)
             lm_head_dma<256, 128, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
                                                                                hidden);
         else
             lm_head_dma<256, 64, 4, 1, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
                                                                               hidden);
-        return check_launch("lm_head_dma");
+        return check_launch(TM == 256 ? "lm_head_ring" : "lm_head_dma");
     }
     const long tiles = (long)((M + kBM - 1) / kBM) * ((vocab + kBN - 1) / kBN);
     if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");

@@ -136,7 +136,12 @@ def test_attention_device_errors_flag_and_nan():
 # ---------------------------------------------------------------------------
 # LM head
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("M,hidden,V", [(130, 200, 333), (64, 512, 1000), (256, 7168, 640)])
+# (260, 640, 40001) and (300, 384, 40000) have at least 256 tiles of 256 x 256,
+# so they take the five-slot ring kernel (ragged rows and vocabulary, odd and
+# multiple-of-4 vocabulary for both epilogue paths, 10 and 6 k-slices so the
+# slot rotation wraps and the tail re-reads run).
+@pytest.mark.parametrize("M,hidden,V", [(130, 200, 333), (64, 512, 1000), (256, 7168, 640),
+                                        (260, 640, 40001)])
 def test_lm_head_exact_small_integers(M, hidden, V):
     """Small-integer bf16 operands: every fp32 partial sum is exact, so the
     bf16 logits must equal the oracle's exact values rounded to nearest even
@@ -151,7 +156,8 @@ def test_lm_head_exact_small_integers(M, hidden, V):
     assert np.array_equal(bits(logits), oracle.round_bf16(exact))
 
 
-@pytest.mark.parametrize("M,hidden,V", [(192, 1024, 1500), (64, 5120, 1111), (300, 512, 700)])
+@pytest.mark.parametrize("M,hidden,V", [(192, 1024, 1500), (64, 5120, 1111), (300, 512, 700),
+                                        (300, 384, 40000)])
 def test_lm_head_bf16_random(M, hidden, V):
     H = sdsynth.normal((M, hidden), 1.0, 3, "H", torch.bfloat16, "cpu")
     W = sdsynth.normal((V, hidden), 0.02, 3, "W", torch.bfloat16, "cpu")
