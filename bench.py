@@ -42,7 +42,7 @@ MFMA_F32_PEAK_TFS = 157.3
 WORKLOAD_NAMES = {1: "c1_tiny_fp32", 2: "c2_gqa_stochastic", 3: "c3_mla_greedy",
                   4: "c4_long_context", 5: "c5_ragged_serving"}
 # Source files whose contents a kernel's PMC traffic figure is tied to.
-KERNEL_SOURCES = {"lm_head_dma": "lm_head.hip", "lm_head_ring": "lm_head.hip",
+KERNEL_SOURCES = {"lm_head_stream": "lm_head.hip", "lm_head_ring": "lm_head.hip",
                   "attn_gqa_stream": "attn_gqa.hip",
                   "attn_mla_bf16": "attn_mla.hip"}
 
@@ -61,7 +61,7 @@ def kernel_source_hash(kernel):
 
 def lm_head_kernel(M, hidden, vocab, dtype):
     """Name of the kernel sd_lm_head launches for this shape (its dispatch rule:
-    256-row tiles while they number at least the CUs, else the generic DMA
+    256-row tiles while they number at least the CUs, else the streaming
     kernel with 128- or 64-row tiles), or None for the fallback paths."""
     import torch
     if dtype != "bf16" or hidden % 128:
@@ -70,7 +70,7 @@ def lm_head_kernel(M, hidden, vocab, dtype):
         cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
         if ((M + 255) // 256) * ((vocab + 255) // 256) >= cus:
             return "lm_head_ring"
-    return "lm_head_dma"
+    return "lm_head_stream"
 
 
 def profiled_traffic(kernel, workload):

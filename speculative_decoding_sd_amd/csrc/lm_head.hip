@@ -109,54 +109,28 @@ __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Main bf16 path.  Computes the transposed tile D[v][m] = sum_k W[v][k] H[m][k]
-// (A = W rows, B = H rows) so that each lane's MFMA accumulator holds four
-// consecutive vocab entries of one output row: the epilogue stores 8 bytes.
-// TN x TM tile (vocab x rows); k advances in stages of BK, staged in LDS by
-// direct global->LDS DMA (global_load_lds_dwordx4): NST stage buffers
-// (BK = 32: four, refilled up to three stages ahead; BK = 64: two).  With
-// BK = 64 every DMA request covers whole 128-byte rows of W and H (full L2
-// lines); with BK = 32 each request is half a line.
-// WN x WM waves each own a (TN/WN) x (TM/WM) sub-tile.  This kernel serves
-// the 128- and 64-row tiles; 256 x 256 tiles use lm_head_ring below.
-// LDS layout per stage: row r (W rows then H rows) holds BK/8 granules of 16
-// bytes; granule c sits at slot c ^ f(r) (f(r) = (r/4)%4 for BK = 32,
-// (r/2)%8 for BK = 64).  A ds_read_b128 is served 16 lanes (16 rows, one
-// logical granule) per pass over the 64 banks; with f those 16 rows land in 16
-// distinct 16-byte bank groups.
+// Main bf16 path (lm_head_ring for 256 x 256 tiles, lm_head_stream for 256 x
+// 128 and 256 x 64).  Both compute the transposed tile D[v][m] =
+// sum_k W[v][k] H[m][k] (A = W rows, B = H rows) so that each lane's MFMA
+// accumulator holds four consecutive vocab entries of one output row: the
+// epilogue stores 8 bytes.  k advances 64 per stage, staged in LDS by direct
+// global->LDS DMA (global_load_lds_dwordx4); every DMA request covers whole
+// 128-byte rows of W and H (full L2 lines).
+// LDS layout of a k-slice: row r holds 8 granules of 16 bytes; granule c sits
+// at slot c ^ ((r/2) % 8).  A ds_read_b128 is served 16 lanes (16 rows, one
+// logical granule) per pass over the 64 banks; with the XOR those 16 rows land
+// in 16 distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
-constexpr int kLmBK = 64;       // k per LDS stage of the DMA GEMM
-constexpr int kStageRows = 512;  // largest TN + TM
-constexpr int kLdsElems = 65536; // 128 KiB: 4 x 512 x 32 or 2 x 512 x 64 bf16
-__shared__ __attribute__((aligned(1024))) uint16_t g_lds[kLdsElems];
-
-template <int TN, int TM, int WN, int WM, int BK>
-struct LmTile {
-    static constexpr int NW = WN * WM;                         // waves per workgroup
-    static constexpr int NT = 64 * NW;                         // threads per workgroup
-    static constexpr int kRows = TN + TM;
-    static constexpr int kGran = BK / 8;                       // 16-byte granules per row
-    static constexpr int kStages = BK == 32 ? 4 : 2;
-    static constexpr int kSteps = BK / 16;                     // MFMA k-steps per stage
-    static constexpr int kStageElems = kStageRows * BK;
-    static constexpr int kDmaPerWave = kRows * kGran / NT;     // 1 KiB DMA ops per wave
-    static constexpr int FN = TN / WN / 32;                    // 32-row MFMA blocks (vocab)
-    static constexpr int FM = TM / WM / 32;                    // 32-col MFMA blocks (rows)
-    static_assert(kRows * kGran % NT == 0, "stage must split into whole wave DMAs");
-    static_assert(kRows <= kStageRows, "stage buffer too small");
-    static_assert(kStages * kStageElems <= kLdsElems, "stages exceed the LDS buffer");
-    static_assert(kSteps % 2 == 0, "fragment sets alternate per step");
-};
-
 template <int BK>
 __device__ __forceinline__ int swz(int row, int c) {
-    if constexpr (BK == 32) return row * 4 + (c ^ ((row >> 2) & 3));
-    else return row * 8 + (c ^ ((row >> 1) & 7));
+    static_assert(BK == 64, "64-wide k-slices only");
+    return row * 8 + (c ^ ((row >> 1) & 7));
 }
 
 // s_waitcnt vmcnt(n) (expcnt and lgkmcnt left free), gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
     __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
@@ -164,47 +138,6 @@ __device__ __forceinline__ void block_barrier_lds() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// Per-lane DMA sources for k = 0: op i of a stage covers LDS granules
-// g = 64 (NW i + wave) + lane, i.e. row g / kGran (W rows, then H rows),
-// logical granule c with swz(row, c) = g.  Rows past the matrix ends re-read
-// the last row (their results are never stored).
-template <int TN, int TM, int WN, int WM, int BK>
-__device__ __forceinline__ void lm_dma_bases(const uint16_t* __restrict__ W,
-                                             const uint16_t* __restrict__ H, int n0, int m0,
-                                             int M, int N, int K, int wave, int lane,
-                                             const uint16_t** src) {
-    using T = LmTile<TN, TM, WN, WM, BK>;
-#pragma unroll
-    for (int i = 0; i < T::kDmaPerWave; ++i) {
-        const int g = (i * T::NW + wave) * 64 + lane;
-        const int row = g / T::kGran;
-        const int slot = g % T::kGran;
-        const int c = BK == 32 ? (slot ^ ((row >> 2) & 3)) : (slot ^ ((row >> 1) & 7));
-        if (row < TN)
-            src[i] = W + (size_t)min(n0 + row, N - 1) * K + 8 * c;
-        else
-            src[i] = H + (size_t)min(m0 + row - TN, M - 1) * K + 8 * c;
-    }
-}
-
-// DMA op i into stage buffer S for k-slice kt.
-template <int TN, int TM, int WN, int WM, int BK, int S>
-__device__ __forceinline__ void lm_dma(const uint16_t* const* src, int i, int kt, int wave) {
-    using T = LmTile<TN, TM, WN, WM, BK>;
-    uint16_t* buf = g_lds + S * T::kStageElems;
-    const int g0 = (i * T::NW + wave) * 64;
-    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * BK,
-                                     (__attribute__((address_space(3))) void*)(buf + g0 * 8), 16, 0,
-                                     0);
-}
-
-template <int TN, int TM, int WN, int WM, int BK, int S>
-__device__ __forceinline__ void lm_issue(const uint16_t* const* src, int kt, int wave) {
-#pragma unroll
-    for (int i = 0; i < LmTile<TN, TM, WN, WM, BK>::kDmaPerWave; ++i)
-        lm_dma<TN, TM, WN, WM, BK, S>(src, i, kt, wave);
 }
 
 // LDS byte address of a __shared__ element (for the inline-asm reads).
@@ -237,188 +170,6 @@ __device__ __forceinline__ void wait_frags(u32x4 (&a)[NA], u32x4 (&b)[NB]) {
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
     else
         static_assert(NA < 0, "unsupported fragment counts");
-}
-
-// Fragments of k-step `step` from stage buffer S.
-template <int TN, int TM, int WN, int WM, int BK, int S>
-__device__ __forceinline__ void lm_read_frags(u32x4 (&fa)[TN / WN / 32],
-                                              u32x4 (&fb)[TM / WM / 32], int step, int wn, int wm,
-                                              int lane) {
-    const uint16_t* buf = g_lds + S * LmTile<TN, TM, WN, WM, BK>::kStageElems;
-    const int ln = lane & 31, lh = lane >> 5;
-    const int c = 2 * step + lh;
-#pragma unroll
-    for (int i = 0; i < TN / WN / 32; ++i)
-        fa[i] = ds_read16(lds_addr(buf + swz<BK>(wn * (TN / WN) + i * 32 + ln, c) * 8));
-#pragma unroll
-    for (int j = 0; j < TM / WM / 32; ++j)
-        fb[j] = ds_read16(lds_addr(buf + swz<BK>(TN + wm * (TM / WM) + j * 32 + ln, c) * 8));
-}
-
-template <int FN, int FM>
-__device__ __forceinline__ void lm_mfma(f32x16 (&acc)[FN][FM], const u32x4 (&fa)[FN],
-                                        const u32x4 (&fb)[FM]) {
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
-}
-
-// A k-step's MFMAs with the refill DMAs of buffer SD (k-slice kt)
-// interleaved, so the matrix pipe keeps working while they issue.
-template <int TN, int TM, int WN, int WM, int BK, int SD>
-__device__ __forceinline__ void lm_mfma_dma(f32x16 (&acc)[TN / WN / 32][TM / WM / 32],
-                                            const u32x4 (&fa)[TN / WN / 32],
-                                            const u32x4 (&fb)[TM / WM / 32],
-                                            const uint16_t* const* src, int kt, int wave) {
-    using T = LmTile<TN, TM, WN, WM, BK>;
-    constexpr int NM = T::FN * T::FM;
-    constexpr int per = NM / T::kDmaPerWave > 0 ? NM / T::kDmaPerWave : 1;
-    constexpr int ndma = NM / per < T::kDmaPerWave ? NM / per : T::kDmaPerWave;
-#pragma unroll
-    for (int idx = 0; idx < NM; ++idx) {
-        const int i = idx / T::FM, j = idx % T::FM;
-        acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
-        if ((idx + 1) % per == 0 && (idx + 1) / per <= ndma)
-            lm_dma<TN, TM, WN, WM, BK, SD>(src, (idx + 1) / per - 1, kt, wave);
-    }
-#pragma unroll
-    for (int i = ndma; i < T::kDmaPerWave; ++i) lm_dma<TN, TM, WN, WM, BK, SD>(src, i, kt, wave);
-    // Scheduling groups: `per` MFMAs, then one VMEM (the DMA), repeated.
-#pragma unroll
-    for (int i = 0; i < ndma; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-}
-
-// One pipeline stage kt (buffer S).  On entry fa0/fb0 hold the stage's step-0
-// fragments.  Each k-step's MFMAs run while the next step's fragments load;
-// before the last step the workgroup waits for stage kt+1 (barrier), starts
-// reading its step-0 fragments, and runs the last step's MFMAs with the refill
-// of buffer S (stage kt + kStages) interleaved.
-// No branch may separate an asm fragment read from its lgkmcnt wait: at a
-// control-flow merge the compiler may copy the (not yet loaded) registers.
-// So everything is unconditional: the last stage reads a spent buffer whose
-// values are never used, and the final refills re-read k-slice nk-1 (the
-// kernel waits for them before it ends).  nk is a multiple of kStages.
-template <int TN, int TM, int WN, int WM, int BK, int S, int STEP>
-__device__ __forceinline__ void lm_steps(const uint16_t* const* src,
-                                         f32x16 (&acc)[TN / WN / 32][TM / WM / 32],
-                                         u32x4 (&fa0)[TN / WN / 32], u32x4 (&fb0)[TM / WM / 32],
-                                         u32x4 (&fa1)[TN / WN / 32], u32x4 (&fb1)[TM / WM / 32],
-                                         int kt, int nk, int wave, int wn, int wm, int lane) {
-    using T = LmTile<TN, TM, WN, WM, BK>;
-    // Fragment sets alternate: even steps use set 0, odd steps set 1.
-    u32x4(&cur_a)[T::FN] = (STEP % 2 == 0) ? fa0 : fa1;
-    u32x4(&cur_b)[T::FM] = (STEP % 2 == 0) ? fb0 : fb1;
-    u32x4(&nxt_a)[T::FN] = (STEP % 2 == 0) ? fa1 : fa0;
-    u32x4(&nxt_b)[T::FM] = (STEP % 2 == 0) ? fb1 : fb0;
-    if constexpr (STEP + 1 < T::kSteps) {
-        lm_read_frags<TN, TM, WN, WM, BK, S>(nxt_a, nxt_b, STEP + 1, wn, wm, lane);
-        // sched_barrier(0) keeps the scheduler from moving the MFMA blocks
-        // across the waits and barriers (they do not depend on asm operands).
-        __builtin_amdgcn_sched_barrier(0);
-        lm_mfma<T::FN, T::FM>(acc, cur_a, cur_b);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_frags(nxt_a, nxt_b);
-        lm_steps<TN, TM, WN, WM, BK, S, STEP + 1>(src, acc, fa0, fb0, fa1, fb1, kt, nk, wave, wn,
-                                                  wm, lane);
-    } else {
-        // Stage kt+1 must have landed; with four stages the refills of kt+2
-        // and kt+3 may still be in flight.
-        if constexpr (T::kStages == 4) wait_vmcnt<2 * T::kDmaPerWave>();
-        else wait_vmcnt<0>();
-        block_barrier_lds();
-        __builtin_amdgcn_sched_barrier(0);
-        lm_read_frags<TN, TM, WN, WM, BK, (S + 1) % T::kStages>(nxt_a, nxt_b, 0, wn, wm, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        lm_mfma_dma<TN, TM, WN, WM, BK, S>(acc, cur_a, cur_b, src,
-                                           min(kt + T::kStages, nk - 1), wave);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_frags(nxt_a, nxt_b);
-    }
-}
-
-template <int TN, int TM, int WN, int WM, int BK>
-__global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_dma(const uint16_t* __restrict__ H,
-                                                      const uint16_t* __restrict__ W,
-                                                      uint16_t* __restrict__ C, int M, int N,
-                                                      int K) {
-    using T = LmTile<TN, TM, WN, WM, BK>;
-    const int tiles_m = (M + TM - 1) / TM;
-    const int tiles_n = (N + TN - 1) / TN;
-    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
-    const int tm = tile % tiles_m, tn = tile / tiles_m;
-    const int n0 = tn * TN, m0 = tm * TM;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wn = wave % WN, wm = wave / WN;
-    const int ln = lane & 31, lh = lane >> 5;
-
-    f32x16 acc[T::FN][T::FM];
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FM; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int nk = K / BK;
-    const uint16_t* src[T::kDmaPerWave];
-    lm_dma_bases<TN, TM, WN, WM, BK>(W, H, n0, m0, M, N, K, wave, lane, src);
-    lm_issue<TN, TM, WN, WM, BK, 0>(src, 0, wave);
-    lm_issue<TN, TM, WN, WM, BK, 1>(src, 1, wave);
-    if constexpr (T::kStages == 4) {
-        lm_issue<TN, TM, WN, WM, BK, 2>(src, 2, wave);
-        lm_issue<TN, TM, WN, WM, BK, 3>(src, 3, wave);
-    }
-    wait_vmcnt<(T::kStages - 1) * T::kDmaPerWave>();
-    block_barrier_lds();
-    u32x4 fa0[T::FN], fb0[T::FM], fa1[T::FN], fb1[T::FM];
-    lm_read_frags<TN, TM, WN, WM, BK, 0>(fa0, fb0, 0, wn, wm, lane);
-    wait_frags(fa0, fb0);
-    for (int kt = 0; kt < nk; kt += T::kStages) {
-        lm_steps<TN, TM, WN, WM, BK, 0, 0>(src, acc, fa0, fb0, fa1, fb1, kt, nk, wave, wn, wm, lane);
-        lm_steps<TN, TM, WN, WM, BK, 1, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 1, nk, wave, wn, wm,
-                                           lane);
-        if constexpr (T::kStages == 4) {
-            lm_steps<TN, TM, WN, WM, BK, 2, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 2, nk, wave, wn,
-                                               wm, lane);
-            lm_steps<TN, TM, WN, WM, BK, 3, 0>(src, acc, fa0, fb0, fa1, fb1, kt + 3, nk, wave, wn,
-                                               wm, lane);
-        }
-    }
-    // The last refills (re-reads of the final k-slice) must land before the
-    // workgroup's LDS is released.
-    wait_vmcnt<0>();
-
-    // Lane (ln, lh) holds D[n][m] for m = column ln of each block and, per
-    // group q of four registers, the four consecutive n = 8q + 4lh .. +3.
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int j = 0; j < T::FM; ++j) {
-        const int m = m0 + wm * (TM / WM) + j * 32 + ln;
-        if (m >= M) continue;
-        uint16_t* crow = C + (size_t)m * N;
-#pragma unroll
-        for (int i = 0; i < T::FN; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * (TN / WN) + i * 32 + 8 * q + 4 * lh;
-                const f32x16& a = acc[i][j];
-                if (vec && n + 3 < N) {
-                    u32x2 w;
-                    w.x = pack_bf16x2(a[4 * q + 0], a[4 * q + 1]);
-                    w.y = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
-                    *(u32x2*)(crow + n) = w;
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (n + t < N) crow[n + t] = (uint16_t)f32_to_bf16_rne(a[4 * q + t]);
-                }
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -590,6 +341,180 @@ __global__ __launch_bounds__(512, 1) void lm_head_ring(const uint16_t* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// 128- and 64-row tiles (small batches, where the LM head streams W from HBM):
+// a ring of NST whole stages (W and H k-slices of 64, (TN + TM) rows each)
+// in the same 160 KB of LDS, three stages of 48 KB for 256 x 128 and four of
+// 40 KB for 256 x 64, so NST - 1 stages are in flight while one computes.
+// The refill of the stage buffer freed at a barrier is spread over the four
+// k-steps that follow it, a quarter of the ops per step, each interleaved with
+// the MFMAs and the next step's fragment reads.  Barrier B_kt at the start of
+// stage kt's last k-step: past it stage kt+1 has landed and stage kt's buffer
+// is free; after it go a quarter of the ops of slice kt + NST (into that
+// buffer), the other three quarters in steps 0-2 of stage kt+1.
+// ---------------------------------------------------------------------------
+template <int TN_, int TM_, int WN_, int WM_, int NST>
+struct StreamTile {
+    static constexpr int NW = WN_ * WM_;
+    static constexpr int NT = 64 * NW;
+    static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_;
+    static constexpr int kRows = TN + TM;
+    static constexpr int kStageBytes = kRows * 128;  // 64 bf16 of k per row
+    static constexpr int kOps = kRows * 8 / NT;      // DMA ops per wave per stage
+    static constexpr int FN = TN / WN / 32, FM = TM / WM / 32;
+    static_assert(kRows * 8 % NT == 0, "stage must split into whole wave DMAs");
+    static_assert(NST >= 3 && NST * kStageBytes <= kRingSlots * kRingSlotBytes, "LDS");
+    static_assert((NST - 2) * kOps + kOps / 4 < 64, "vmcnt field");
+};
+
+// DMA op i of a stage into the buffer at byte offset off: lane l of wave w
+// writes granule g = 64 (NW i + w) + l, row g / 8 (W rows, then H rows).
+template <class T>
+__device__ __forceinline__ void stream_dma(const uint16_t* const* src, int i, int kt,
+                                           uint32_t off, int wave) {
+    const int g0 = (i * T::NW + wave) * 64;
+    __builtin_amdgcn_global_load_lds(src[i] + (size_t)kt * 64,
+                                     (__attribute__((address_space(3))) void*)(
+                                         g_ring + (off + g0 * 16) / 2),
+                                     16, 0, 0);
+}
+
+// One k-step: the MFMAs on (ca, cb), the next step's fragment reads (stage at
+// LDS byte address rb, k-step `step`) and DMA ops [D0, D1) of k-slice kt into
+// buffer offset doff, spread evenly over the MFMAs in fenced groups.
+template <class T, int D0, int D1>
+__device__ __forceinline__ void stream_step(f32x16 (&acc)[T::FN][T::FM], const u32x4 (&ca)[T::FN],
+                                            const u32x4 (&cb)[T::FM], u32x4 (&na)[T::FN],
+                                            u32x4 (&nb)[T::FM], uint32_t rb, int step, int wn,
+                                            int wm, int lane, const uint16_t* const* src, int kt,
+                                            uint32_t doff, int wave) {
+    constexpr int FN = T::FN, FM = T::FM, NMF = FN * FM, NR = FN + FM, ND = D1 - D0;
+    const int ln = lane & 31, c = 2 * step + (lane >> 5);
+#pragma unroll
+    for (int idx = 0; idx < NMF; ++idx) {
+        acc[idx / FM][idx % FM] = mfma_32x32x16(ca[idx / FM], cb[idx % FM], acc[idx / FM][idx % FM]);
+#pragma unroll
+        for (int r = idx * NR / NMF; r < (idx + 1) * NR / NMF; ++r) {
+            if (r < FN)
+                na[r] = ds_read16(rb + swz<64>(wn * (FN * 32) + r * 32 + ln, c) * 16);
+            else
+                nb[r - FN] = ds_read16(
+                    rb + swz<64>(T::TN + wm * (FM * 32) + (r - FN) * 32 + ln, c) * 16);
+        }
+#pragma unroll
+        for (int d = idx * ND / NMF; d < (idx + 1) * ND / NMF; ++d)
+            stream_dma<T>(src, D0 + d, kt, doff, wave);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int TN, int TM, int WN, int WM, int NST>
+__global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_stream(const uint16_t* __restrict__ H,
+                                                             const uint16_t* __restrict__ W,
+                                                             uint16_t* __restrict__ C, int M,
+                                                             int N, int K) {
+    using T = StreamTile<TN, TM, WN, WM, NST>;
+    constexpr int FN = T::FN, FM = T::FM, OPS = T::kOps;
+    constexpr uint32_t SB = T::kStageBytes;
+    constexpr int C1 = OPS / 4, C2 = OPS / 2, C3 = 3 * OPS / 4;
+    const int tiles_m = (M + TM - 1) / TM;
+    const int tiles_n = (N + TN - 1) / TN;
+    const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int n0 = tn * TN, m0 = tm * TM;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wn = wave % WN, wm = wave / WN;
+    const int ln = lane & 31, lh = lane >> 5;
+    const uint32_t lds0 = lds_addr(g_ring);
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = K / 64;
+    // Rows past the matrix ends re-read the last row (never stored).
+    const uint16_t* src[OPS];
+#pragma unroll
+    for (int i = 0; i < OPS; ++i) {
+        const int g = (i * T::NW + wave) * 64 + lane;
+        const int row = g / 8, c = (g % 8) ^ ((row >> 1) & 7);
+        src[i] = row < TN ? W + (size_t)min(n0 + row, N - 1) * K + 8 * c
+                          : H + (size_t)min(m0 + row - TN, M - 1) * K + 8 * c;
+    }
+    // Prologue: slices 0 .. NST-2 whole, the first quarter of slice NST-1;
+    // slices past the end re-read the last one into free buffers (waited for
+    // before the kernel ends).
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+#pragma unroll
+        for (int i = 0; i < OPS; ++i) stream_dma<T>(src, i, min(st, nk - 1), st * SB, wave);
+#pragma unroll
+    for (int i = 0; i < C1; ++i) stream_dma<T>(src, i, min(NST - 1, nk - 1), (NST - 1) * SB, wave);
+    wait_vmcnt<(NST - 2) * OPS + C1>();
+    block_barrier_lds();
+    u32x4 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+        fa0[i] = ds_read16(lds0 + swz<64>(wn * (FN * 32) + i * 32 + ln, lh) * 16);
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+        fb0[j] = ds_read16(lds0 + swz<64>(TN + wm * (FM * 32) + j * 32 + ln, lh) * 16);
+    wait_frags(fa0, fb0);
+    // Straight-line body (no branch between an asm read and its wait).
+    int b = 0;  // buffer of stage kt
+    for (int kt = 0; kt < nk; ++kt) {
+        const int bp = b == 0 ? NST - 1 : b - 1;  // freed at B_{kt-1}: slice kt + NST - 1
+        const int bn = b + 1 == NST ? 0 : b + 1;  // stage kt + 1
+        const uint32_t cur = lds0 + b * SB, nxt = lds0 + bn * SB;
+        const int kr = min(kt + NST - 1, nk - 1), kr2 = min(kt + NST, nk - 1);
+        stream_step<T, C1, C2>(acc, fa0, fb0, fa1, fb1, cur, 1, wn, wm, lane, src, kr, bp * SB, wave);
+        wait_frags(fa1, fb1);
+        stream_step<T, C2, C3>(acc, fa1, fb1, fa0, fb0, cur, 2, wn, wm, lane, src, kr, bp * SB, wave);
+        wait_frags(fa0, fb0);
+        stream_step<T, C3, OPS>(acc, fa0, fb0, fa1, fb1, cur, 3, wn, wm, lane, src, kr, bp * SB,
+                                wave);
+        wait_frags(fa1, fb1);
+        // B_kt: slice kt+1 landed (slices kt+2 .. kt+NST-1 may be in flight).
+        wait_vmcnt<(NST - 2) * OPS>();
+        block_barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        stream_step<T, 0, C1>(acc, fa1, fb1, fa0, fb0, nxt, 0, wn, wm, lane, src, kr2, b * SB, wave);
+        wait_frags(fa0, fb0);
+        b = bn;
+    }
+    wait_vmcnt<0>();
+
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * (TM / WM) + j * 32 + ln;
+        if (m >= M) continue;
+        uint16_t* crow = C + (size_t)m * N;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * (TN / WN) + i * 32 + 8 * g + 4 * lh;
+                const f32x16& a = acc[i][j];
+                if (vec && n + 3 < N) {
+                    u32x2 w;
+                    w.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+                    w.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                    *(u32x2*)(crow + n) = w;
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (n + t < N) crow[n + t] = (uint16_t)f32_to_bf16_rne(a[4 * g + t]);
+                }
+            }
+        }
+    }
+}
+
 // fp32 path: one wave per output element, lanes split k (coalesced rows),
 // fixed-order butterfly reduction.
 __global__ __launch_bounds__(256) void lm_head_f32(const float* __restrict__ A,
@@ -650,12 +575,12 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         if (TM == 256)
             lm_head_ring<<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab, hidden);
         else if (TM == 128)
-            lm_head_dma<256, 128, 2, 2, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
-                                                                               hidden);
-        else
-            lm_head_dma<256, 64, 4, 1, kLmBK><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+            lm_head_stream<256, 128, 2, 2, 3><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
                                                                               hidden);
-        return check_launch(TM == 256 ? "lm_head_ring" : "lm_head_dma");
+        else
+            lm_head_stream<256, 64, 4, 1, 4><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+                                                                             hidden);
+        return check_launch(TM == 256 ? "lm_head_ring" : "lm_head_stream");
     }
     const long tiles = (long)((M + kBM - 1) / kBM) * ((vocab + kBN - 1) / kBN);
     if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");
