@@ -139,9 +139,13 @@ def test_attention_device_errors_flag_and_nan():
 # (260, 640, 40001) and (300, 384, 40000) have at least 256 tiles of 256 x 256,
 # so they take the five-slot ring kernel (ragged rows and vocabulary, odd and
 # multiple-of-4 vocabulary for both epilogue paths, 10 and 6 k-slices so the
-# slot rotation wraps and the tail re-reads run).
+# slot rotation wraps and the tail re-reads run).  hidden = 128 gives two
+# k-slices, fewer than any ring holds: (100, 128, 3000) and (40, 128, 5000)
+# take the three- and four-stage streaming kernels, (260, 128, 40001) the
+# five-slot ring, all with clamped prologue refills.
 @pytest.mark.parametrize("M,hidden,V", [(130, 200, 333), (64, 512, 1000), (256, 7168, 640),
-                                        (260, 640, 40001)])
+                                        (260, 640, 40001), (100, 128, 3000), (40, 128, 5000),
+                                        (260, 128, 40001)])
 def test_lm_head_exact_small_integers(M, hidden, V):
     """Small-integer bf16 operands: every fp32 partial sum is exact, so the
     bf16 logits must equal the oracle's exact values rounded to nearest even
