@@ -55,6 +55,7 @@ constexpr int kRowsPerBlock = 128;
 constexpr int kQSteps = kDqk / 16;     // 36 MFMA k-steps over the latent
 constexpr int kQReg = 18;              // Q^T steps held in registers
 constexpr int kQLds = kQSteps - kQReg; // Q^T steps read from LDS each tile
+static_assert(4 * (kDmaPerWave - 1) < kQSteps, "a tile's DMAs are issued within the S^T k-steps");
 
 __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
@@ -111,15 +112,14 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         return key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
     };
     const uint32_t lds0 = lds_byte_addr(&s_lat[0][0]);
-    auto issue_tile = [&](int t) {
+    auto tile_src = [&](int t) {
         const int ks = start + kTileKeys * t;
         const int pg = page_table[(size_t)b * max_pages + ks / kPage];
-        const uint16_t* base = lat + ((size_t)pg * kPage + (ks % kPage)) * kDqk;
-        const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileElems * 2);
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j)
-            dma16(base + goff(j),
-                  __builtin_amdgcn_readfirstlane(dst + (uint32_t)(1024 * (4 * j + wave))));
+        return lat + ((size_t)pg * kPage + (ks % kPage)) * kDqk;
+    };
+    auto tile_dst = [&](int t) { return lds0 + (uint32_t)((t % kStages) * kTileElems * 2); };
+    auto tile_dma = [&](const uint16_t* base, uint32_t dst, int j) {
+        dma16(base + goff(j), __builtin_amdgcn_readfirstlane(dst + (uint32_t)(1024 * (4 * j + wave))));
     };
 
     // Per-lane LDS byte offsets within a tile.
@@ -151,15 +151,25 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
 
     // Two stages: tile t+1 loads while tile t is computed.  At the top of
     // iteration t, tile t (issued one iteration earlier) has landed and every
-    // wave has left iteration t-1, so stage (t+1)%2 is free to refill.
-    issue_tile(0);
+    // wave has left iteration t-1, so stage (t+1)%2 is free to refill.  The
+    // refill's nine DMAs per wave go out one every four S^T k-steps rather
+    // than as one burst, which would hold up the wave's MFMA issue while the
+    // vector-memory queue drains.
+    {
+        const uint16_t* base0 = tile_src(0);
+        const uint32_t dst0 = tile_dst(0);
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) tile_dma(base0, dst0, j);
+    }
     for (int t = 0; t < ntiles; ++t) {
         wait_vmcnt<0>();
         // This wave's reads of tile t-1 must have returned before another
         // wave refills that stage after the barrier.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         barrier_only();
-        if (t + 1 < ntiles) issue_tile(t + 1);
+        const bool more = t + 1 < ntiles;
+        const uint16_t* nbase = more ? tile_src(t + 1) : lat;
+        const uint32_t ndst = tile_dst(t + 1);
         const char* tile = (const char*)&s_lat[t % kStages][0];
         const int ks = start + kTileKeys * t;
         if (t == ntiles - 1 && end - ks < kTileKeys) {
@@ -197,6 +207,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             if (s + PF < kQSteps)
                 kf[s % PF] = *(const u32x4*)(tile + koff[(s + PF) & 3] + 128 * ((s + PF) >> 2));
             sa = mfma_32x32x16(cur, qcur, sa);
+            if (s % 4 == 0 && s / 4 < kDmaPerWave && more) tile_dma(nbase, ndst, s / 4);
             // Bounds how far the scheduler hoists reads.
             __builtin_amdgcn_sched_barrier(0);
         }
