@@ -98,28 +98,6 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
-// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the
-// upper half of one copy with the lower half of the other: the pair then
-// holds both halves' values in every lane).
-__device__ __forceinline__ float halves_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two floats -> packed bf16 (lo in the low half), round to nearest even
-// (v_cvt_pk_bf16_f32).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
 // The work is the sequence of 32-key tiles of every (kv head, request) pair,
 // kv-head-major: for each kv head, the requests in order, each request's
 // tiles 0 .. P_b - 1 (P_b = ceil((L_b + K + 1) / 32), 0 for an invalid

@@ -211,16 +211,26 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             // Bounds how far the scheduler hoists reads.
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Online softmax (lane holds 16 keys of query row ln).
+        // Online softmax (lane holds 16 keys of query row ln).  The wave's
+        // rows share one position, so whether the tile needs the mask (keys
+        // past the chunk end or past the causal limit) is wave-uniform.
         float tmax = -INFINITY;
+        if (ks + kTileKeys <= end && ks + kTileKeys - 1 <= lim) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = ks + mfma_row(r, lane);
-            const float v = sa[r] * scale_log2;
-            sa[r] = (key >= end || key > lim) ? -INFINITY : v;
-            tmax = fmaxf(tmax, sa[r]);
+            for (int r = 0; r < 16; ++r) {
+                sa[r] *= scale_log2;
+                tmax = fmaxf(tmax, sa[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = ks + mfma_row(r, lane);
+                const float v = sa[r] * scale_log2;
+                sa[r] = (key >= end || key > lim) ? -INFINITY : v;
+                tmax = fmaxf(tmax, sa[r]);
+            }
         }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        tmax = halves_max(tmax);
         // The chunk's first tile sets each row's reference max; later tiles
         // are exponentiated against it (P up to 2^64 is exact enough in the
         // hi/lo split and safe in fp32).  A row whose later scores exceed the
@@ -234,12 +244,13 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         for (int r = 0; r < 16; r += 2) {
             const float p0 = __builtin_amdgcn_exp2f(sa[r] - msafe);
             const float p1 = __builtin_amdgcn_exp2f(sa[r + 1] - msafe);
-            const uint32_t hi = pack_bf16_finite(p0, p1);
+            const uint32_t hi = cvt_pk_bf16(p0, p1);
             psum += p0 + p1;
             pk[r >> 1] = hi;
-            pl[r >> 1] = pack_bf16_finite(p0 - bf16_to_f32(hi & 0xffffu), p1 - bf16_to_f32(hi >> 16));
+            pl[r >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
+                                     p1 - __uint_as_float(hi & 0xffff0000u));
         }
-        psum += shfl_xor(psum, 32);
+        psum = halves_sum(psum);
         l_r += psum;
         // Block 15 back from LDS (S^T is dead now; the barrier keeps the load
         // from being hoisted into S^T's live range).

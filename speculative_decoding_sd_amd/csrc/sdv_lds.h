@@ -67,6 +67,28 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
 // chunks of a ds_read_b64_tr_b16 phase each land in distinct bank groups.
 __device__ __forceinline__ int chunk_xor(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the
+// upper half of one copy with the lower half of the other: the pair then
+// holds both halves' values in every lane).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two floats -> packed bf16 (lo in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // bf16 bits of two finite floats (lo in the low half), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16_finite(float lo, float hi) {
     uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
