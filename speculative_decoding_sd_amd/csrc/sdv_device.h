@@ -63,12 +63,6 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-    return v;
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);

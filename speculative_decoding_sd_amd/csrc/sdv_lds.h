@@ -1,6 +1,7 @@
-// Device helpers for the attention kernels' LDS traffic on gfx950: direct
+// Device helpers for the attention kernels on gfx950: direct
 // global->LDS DMA issued outside the compiler's view, explicit vmcnt waits,
-// the transposing 8-byte LDS read, and the chunk swizzle of a K/V tile.
+// the transposing LDS reads, the chunk swizzle of a K/V tile, half-wave
+// reductions and hardware bf16 packing.
 #pragma once
 
 #include "sdv_device.h"
@@ -87,14 +88,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
-// bf16 bits of two finite floats (lo in the low half), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16_finite(float lo, float hi) {
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    a += 0x7fffu + ((a >> 16) & 1u);
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (a >> 16) | (b & 0xffff0000u);
 }
 
 }  // namespace sdv
