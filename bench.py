@@ -59,17 +59,15 @@ def kernel_source_hash(kernel):
     return h.hexdigest()
 
 
-def lm_head_kernel(M, hidden, vocab, dtype):
-    """Name of the kernel sd_lm_head launches for this shape (its dispatch rule:
-    256-row tiles while they number at least the CUs, else the streaming
-    kernel with 128- or 64-row tiles), or None for the fallback paths."""
-    import torch
+def lm_head_kernel(M, hidden, vocab, dtype, cus):
+    """Name of the kernel sd_lm_head launches for this shape on a device with
+    `cus` compute units (its dispatch rule: 256 x 256 tiles while they number
+    at least the CUs, else the streaming kernel with 128- or 64-row tiles), or
+    None for the fallback paths."""
     if dtype != "bf16" or hidden % 128:
         return None
-    if M > 128:
-        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-        if ((M + 255) // 256) * ((vocab + 255) // 256) >= cus:
-            return "lm_head_ring"
+    if M > 128 and ((M + 255) // 256) * ((vocab + 255) // 256) >= cus:
+        return "lm_head_ring"
     return "lm_head_stream"
 
 
@@ -436,7 +434,8 @@ def main():
     dom = max(("attention", "lm_head"), key=lambda k: per_call[k])
     roof = dict(kernels[dom])
     if dom == "lm_head":
-        dom_kernel = lm_head_kernel(cfg.batch * cfg.num_q, cfg.hidden, cfg.vocab, cfg.dtype)
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        dom_kernel = lm_head_kernel(cfg.batch * cfg.num_q, cfg.hidden, cfg.vocab, cfg.dtype, cus)
     else:
         dom_kernel = "attn_mla_bf16" if cfg.mla else ("attn_gqa_stream" if cfg.dtype == "bf16" else None)
     traffic = profiled_traffic(dom_kernel, workload) if dom_kernel else None
