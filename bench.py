@@ -150,6 +150,14 @@ def lm_head_work(cfg):
     return flops, byts
 
 
+def accept_bytes(cfg):
+    """Algorithmic HBM bytes of one sd_accept call, counted as its floor: every
+    logits row read once (the draft-probability rows a sampled request's draw
+    reads and the small per-row outputs are left out)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    return float(cfg.batch * cfg.num_q) * cfg.vocab * es
+
+
 def synthesize_drafts(cfg, seed, logits_host_f32, temperature, top_p, tree_parent=None):
     """Draft-model stand-in from the target logits (see module docstring).
     A tree: node n copies the target token after its parent with probability
@@ -427,6 +435,8 @@ def main():
                     if lm_bound == "mfma" else
                     {"bound": "hbm", "achieved": lm_bytes / (per_call["lm_head"] * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes": lm_bytes}),
+        "accept": {"bound": "hbm", "achieved": accept_bytes(cfg) / (per_call["accept"] * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes": accept_bytes(cfg)},
     }
     for k, v in kernels.items():
         v["frac"] = v["achieved"] / v["peak"]

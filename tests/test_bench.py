@@ -53,6 +53,11 @@ def test_lm_head_work_by_hand():
     assert b == (129280 * 7168 + M * 7168 + M * 129280) * 2
 
 
+def test_accept_bytes_by_hand():
+    cfg = sdsynth.CONFIGS[5]
+    assert bench.accept_bytes(cfg) == 256 * 5 * 129280 * 2
+
+
 def test_lm_head_kernel_follows_the_dispatch_rule():
     k = bench.lm_head_kernel
     assert k(1280, 7168, 129280, "bf16", 256) == "lm_head_ring"    # C5: 2525 tiles
