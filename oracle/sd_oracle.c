@@ -42,8 +42,10 @@
  *     even, saturating at 448, NaN kept) of value / scale;
  *   - a tree of drafts lists its nodes in topological order (root 0,
  *     parent[i] < i); a node attends to its ancestors and itself; greedy
- *     verification descends through the first child (by index) that matches
- *     the argmax; the accepted path's rows are gathered to contiguous slots.
+ *     verification keeps the longest accepted root-to-node path (a node is
+ *     accepted when its parent is and its draft is the parent row's argmax;
+ *     the smallest end-node index among equally long paths); the accepted
+ *     path's rows are gathered to contiguous slots.
  */
 #include <math.h>
 #include <stdint.h>
@@ -677,11 +679,14 @@ int orc_accept(int B, int K, int V, int logits_dtype, const void* logits,
  * relaxed requests diag[1] holds the smallest margin of relaxed_accepts.
  *
  * Tree of drafts (tree_parent [B][K+1], optional; node 0 is the root, node
- * n >= 1 carries draft n, parent[n] < n): greedy verification walks down
- * from the root, at node c accepting its first child (smallest node index)
- * whose draft equals the argmax of row c, until no child matches; the final
- * token is the argmax of the last accepted node's row, and the accepted
- * drafts are those along the path ([TRT-MTP] "工作展望", Fig. 9; a chain is
+ * n >= 1 carries draft n, parent[n] < n): node n is accepted when its parent
+ * is accepted (the root always is) and its draft equals the argmax of its
+ * parent's row; the accepted nodes form a subtree holding the root, and the
+ * verification keeps the longest accepted root-to-node path: the deepest
+ * accepted node, the smallest node index among equally deep ones.  The
+ * final token is the argmax of that node's row and the accepted drafts are
+ * those along its path ([TRT-MTP] "工作展望", Fig. 9: a tree offers several
+ * candidate continuations and the longest verified one is kept; a chain is
  * the case parent[n] = n - 1).  A negative draft id marks an unused node.
  * A malformed tree, a sampled request or a relaxed request with a tree is
  * invalid.  accepted_nodes [B][K+1] (optional, also without a tree) receives
@@ -732,24 +737,37 @@ int orc_accept_ex(int B, int K, int V, int logits_dtype, const void* logits,
         }
         int j = 0, f = -1;
         if (tree_parent) {
+            /* Every node's acceptance, in topological order (parents first),
+             * then the deepest accepted node (smallest index on ties). */
             const int* par = tree_parent + (size_t)b * Q;
+            int* acc = (int*)malloc(sizeof(int) * (size_t)Q);
+            int* depth = (int*)malloc(sizeof(int) * (size_t)Q);
+            int* amax = (int*)malloc(sizeof(int) * (size_t)Q);
             double mg;
-            int cur = 0;
-            int t = row_argmax(base, logits_dtype, V, &mg);
+            acc[0] = 1;
+            depth[0] = 0;
+            amax[0] = row_argmax(base, logits_dtype, V, &mg);
             dg[0] = mg;
-            for (;;) {
-                int next = -1;
-                for (int c = cur + 1; c < Q && next < 0; ++c)
-                    if (par[c] == cur && drafts[(size_t)b * K + c - 1] == t) next = c;
-                if (next < 0) break;
-                ++j;
-                if (path) path[j] = next;
-                out_tokens[(size_t)b * Q + j - 1] = t;
-                cur = next;
-                t = row_argmax(base + (size_t)cur * V * es, logits_dtype, V, &mg);
+            int best = 0;
+            for (int n = 1; n < Q; ++n) {
+                const int p = par[n], d = drafts[(size_t)b * K + n - 1];
+                depth[n] = depth[p] + 1;
+                acc[n] = acc[p] && d >= 0 && d == amax[p];
+                amax[n] = -1;
+                if (!acc[n]) continue;
+                amax[n] = row_argmax(base + (size_t)n * V * es, logits_dtype, V, &mg);
                 if (mg < dg[0]) dg[0] = mg;
+                if (depth[n] > depth[best]) best = n;
             }
-            f = t;
+            j = depth[best];
+            for (int c = best; c != 0; c = par[c]) {
+                if (path) path[depth[c]] = c;
+                out_tokens[(size_t)b * Q + depth[c] - 1] = drafts[(size_t)b * K + c - 1];
+            }
+            f = amax[best];
+            free(acc);
+            free(depth);
+            free(amax);
         } else if (T == 0.0 && rN > 0) {
             /* Relaxed: draft n is accepted while it is a surviving top-N
              * candidate of row n-1; the final token is the argmax of row j. */

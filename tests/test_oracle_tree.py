@@ -125,13 +125,36 @@ def test_tree_acceptance_hand_example(orc):
     assert list(out["accepted_nodes"][0]) == [0, 2, 4, -1, -1]
     assert out["next_token"][0] == 5
     assert list(out["packed"][:3]) == [2, 4, 5]
-    # duplicate sibling tokens: the first matching child (smaller index) wins
+    # Duplicate sibling tokens: nodes 1 and 2 both carry row 0's argmax 2.
+    # Through node 1 the path ends there (row 1's argmax is 3, its child
+    # node 4 carries 4); through node 2 it goes on to node 3 (row 2's argmax
+    # 4).  The longest accepted path 0-2-3 is kept, not the first match 0-1.
     par2 = np.array([[-1, 0, 0, 2, 1]], np.int32)
     drafts2 = np.array([[2, 2, 4, 4]], np.int32)
     out = orc.accept(logits, drafts2, np.zeros(1, np.float32), None, None, z, z, tree_parent=par2)
-    # node 1 (first child with token 2) is taken; row 1's argmax is 3, its
-    # only child (node 4) carries 4: the walk stops at node 1
-    assert out["num_accepted"][0] == 1
+    assert out["num_accepted"][0] == 2
+    assert list(out["accepted_nodes"][0]) == [0, 2, 3, -1, -1]
+    assert list(out["out_tokens"][0]) == [2, 4, 6, -1, -1]
+    assert out["next_token"][0] == 6
+    # Two accepted paths of equal length (0-1-3 and 0-2-4): the one ending at
+    # the smaller node index is kept; its final token is row 3's argmax.
+    par3 = np.array([[-1, 0, 0, 1, 2]], np.int32)
+    drafts3 = np.array([[2, 2, 3, 4]], np.int32)
+    out = orc.accept(logits, drafts3, np.zeros(1, np.float32), None, None, z, z, tree_parent=par3)
+    assert out["num_accepted"][0] == 2
+    assert list(out["accepted_nodes"][0]) == [0, 1, 3, -1, -1]
+    assert list(out["out_tokens"][0]) == [2, 3, 6, -1, -1]
+    # A deeper path behind a later sibling beats a shallower one that ends
+    # at a smaller index: node 2's subtree reaches depth 2 while node 1 is a
+    # leaf.
+    par4 = np.array([[-1, 0, 0, 2, 0]], np.int32)
+    drafts4 = np.array([[2, 2, 4, 2]], np.int32)
+    out = orc.accept(logits, drafts4, np.zeros(1, np.float32), None, None, z, z, tree_parent=par4)
+    assert list(out["accepted_nodes"][0]) == [0, 2, 3, -1, -1]
+    # A matching node under a rejected parent is not accepted: node 3
+    # (token 4 = row 2's argmax) hangs under node 2, whose draft 7 fails.
+    drafts5 = np.array([[2, 7, 4, 4]], np.int32)
+    out = orc.accept(logits, drafts5, np.zeros(1, np.float32), None, None, z, z, tree_parent=par2)
     assert list(out["accepted_nodes"][0]) == [0, 1, -1, -1, -1]
     assert list(out["out_tokens"][0]) == [2, 3, -1, -1, -1]
     # a negative draft marks an unused node: it is never accepted
