@@ -111,7 +111,32 @@ def parse():
                          "breadth-first order")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite a 1 GiB scratch buffer before every timed step, so that "
+                         "neither the L2 caches nor the 256 MB MALL hold the step's inputs; "
+                         "each step is then timed alone with HIP events")
     return ap.parse_args()
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sampling_modes(cfg):
+    """Per-request sampling modes of the workload, as a label."""
+    if cfg.mixed_modes is not None:
+        return f"even requests greedy, odd requests sampled at T={cfg.mixed_modes}"
+    if cfg.temperature == 0:
+        return "greedy"
+    return f"sampled at T={cfg.temperature}"
 
 
 def attention_bytes(cfg, seq_lens_before):
@@ -236,7 +261,7 @@ def cpu_baseline(cfg, seed, wl, host_inputs, n_req):
     timings["rollback"] = time.perf_counter() - s
     total = sum(timings.values())
     return {"value": B * Q / total, "unit": "verified positions/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {B} request(s) of the same workload ({B * Q} positions) through "
                       f"append+attention, LM head, accept and rollback; per-call seconds "
                       + ", ".join(f"{k} {v:.3f}" for k, v in timings.items()),
@@ -375,9 +400,12 @@ def main():
     calls = [step.attention, step.lm_head, step.accept, step.rollback]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     acc_total = 0
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(k & 0xFF)   # evicts the step's inputs from L2 and MALL
         ev[k][0].record()
         for c, fn in enumerate(calls):
             fn()
@@ -388,6 +416,10 @@ def main():
     per_call = {n: float(np.mean([ev[k][c].elapsed_time(ev[k][c + 1]) for k in range(args.steps)]))
                 for c, n in enumerate(names)}
     ev_step_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][4]) for k in range(args.steps)]))
+    if scratch is not None:
+        # The flush is not part of the step: the step time is the events'.
+        wall_ms = ev_step_ms
+        del scratch
     L_end = seq_lens.cpu().numpy()
     emitted = int(step.out_offsets[-1].item())
     acc_total = (L_end - L_start).sum()  # j_b + 1 per request per step
@@ -441,6 +473,16 @@ def main():
     for k, v in kernels.items():
         v["frac"] = v["achieved"] / v["peak"]
         v["ms"] = per_call[k]
+    # Whole step against its floor: every call at its own bound's peak.
+    floor_ms = 0.0
+    for k, v in kernels.items():
+        work = v.get("flops") if v["bound"] == "mfma" else v.get("bytes")
+        peak = v["peak"] * (1e12 if v["unit"] == "TFLOP/s" else 1e9)
+        floor_ms += work / peak * 1e3
+    step_roof = {"floor_ms": floor_ms, "ms": ev_step_ms, "frac": floor_ms / ev_step_ms,
+                 "note": "sum over attention, LM head and accept of algorithmic work / peak "
+                         "at each call's bound (rollback: negligible bytes), over the event "
+                         "time of the four calls"}
     dom = max(("attention", "lm_head"), key=lambda k: per_call[k])
     roof = dict(kernels[dom])
     if dom == "lm_head":
@@ -464,8 +506,9 @@ def main():
                    "head_dim": cfg.d_qk, "kv_len": (int(cfg.seq_len) if cfg.seq_len
                                                     else list(cfg.seq_len_range)),
                    "mean_kv_len": float(L_mid.mean()), "hidden": cfg.hidden,
-                   "vocab": cfg.vocab, "temperature": cfg.temperature or cfg.mixed_modes,
+                   "vocab": cfg.vocab, "sampling": sampling_modes(cfg),
                    "top_p": cfg.top_p, "page_size": cfg.page_size,
+                   "l2_mall_flush": bool(args.flush),
                    "kv_cache": "e4m3" if cfg.kv_cache == "e4m3" else cfg.dtype,
                    "drafts": (f"{args.tree} tree of {cfg.num_q} nodes" if tree is not None
                               else f"chain of {cfg.K}")},
@@ -476,6 +519,7 @@ def main():
         "eager_ms_per_step": eager_ms,
         "per_call_ms": per_call,
         "roofline": roof,
+        "step_roofline": step_roof,
         "kernels": kernels,
         "device_error": n_err,
         "last_step_emitted": emitted,

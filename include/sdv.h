@@ -25,9 +25,9 @@
  *   - Pointers marked "device" are HIP device pointers; descriptors and size
  *     outputs are host memory.  The caller owns every buffer; the library
  *     allocates nothing and keeps no pointer after a call returns.
- *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
- *     default stream) and never synchronises the host.  Buffers must stay
- *     alive until the stream has passed the call.
+ *   - Every call but sd_get_device_error is asynchronous on `stream` (a
+ *     hipStream_t; NULL = the default stream) and never synchronises the
+ *     host.  Buffers must stay alive until the stream has passed the call.
  *   - Arrays are dense and row-major; element counts, not bytes, unless
  *     stated.  Tensor data pointers must be 16-byte aligned; workspaces
  *     256-byte aligned.
@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 4
+#define SD_ABI_VERSION 5
 
 /* status codes */
 #define SD_OK 0
@@ -94,6 +94,21 @@ int sd_abi_version(void);
 /* Text of this thread's last non-OK status ("" if none).  Valid until the
  * thread's next call into the library. */
 const char* sd_last_error(void);
+
+/* Device-side error report of a step ([VLLM-MTP] s3 stages 3-4: a verify
+ * step ends with 1 .. D+1 tokens per request; a request the kernels had to
+ * declare invalid ends with none, and this word says why).
+ *   dev_error  device int32: the word passed as `dev_error` to the step's
+ *              sd_verify_attn / sd_accept / sd_kv_rollback calls, into which
+ *              they OR their SD_DERR_* bits (0 = no device-side fault)
+ *   code       host int32, receives the word
+ *   stream     the stream those calls were issued on (NULL = default)
+ * Waits until `stream` has passed every call issued on it before this one,
+ * then copies the word to *code.  It is the one call that synchronises the
+ * host.  The word is not cleared: the caller zeroes it before the next
+ * step.  Returns SD_EINVAL for a NULL pointer, SD_EDEVICE (code untouched)
+ * if the copy or the wait fails. */
+int sd_get_device_error(const int32_t* dev_error, int32_t* code, void* stream);
 
 /* ------------------------------------------------------------------------
  * Verify attention.
@@ -239,16 +254,17 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *   infinite or negative, makes the request invalid (SD_DERR_PARAM).
  * A draft id < 0 ends the chain early (the final token is then drawn from,
  *   or is the argmax of, the row that draft would have been judged by).
- * Tree of drafts (tree_parent != NULL, the same array as sd_attn_desc's):
- *   node n >= 1 carries draft n and logits row n is the prediction after
- *   node n.  Greedy verification descends from the root: at accepted node c
- *   it accepts the first child n (smallest n with parent n == c) whose draft
- *   equals the argmax of row c, until no child matches; the final token is
- *   the argmax of the last accepted node's row; the emitted tokens are the
- *   drafts along the path, then the final token.  A negative draft id marks
- *   an unused node.  Trees apply to strict greedy requests only: a sampled
- *   or relaxed request with a tree, or a malformed tree, is invalid
- *   (SD_DERR_TREE).
+ * Tree of drafts (tree_parent != NULL, the same array as sd_attn_desc's;
+ *   [TRT-MTP] "工作展望", Fig. 9): node n >= 1 carries draft n and logits
+ *   row n is the prediction after node n.  Node n is accepted when its
+ *   parent is (the root always is) and its draft equals the argmax of the
+ *   parent's row.  The kept path is the longest accepted root-to-node path:
+ *   it ends at the deepest accepted node, the one with the smallest index
+ *   among equally deep ones.  The final token is the argmax of that node's
+ *   row; the emitted tokens are the drafts along the path, then the final
+ *   token.  A negative draft id marks an unused node.  Trees apply to strict
+ *   greedy requests only: a sampled or relaxed request with a tree, or a
+ *   malformed tree, is invalid (SD_DERR_TREE).  Needs K+1 <= 64.
  * Each request emits j_b + 1 tokens: accepted drafts, then the final token.
  *
  * Layouts (device):
@@ -275,7 +291,8 @@ int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H, const voi
  *                  gathers a tree's kept rows with
  * Invalid requests (see SD_DERR_TOKEN/NONFINITE/PARAM/TREE) emit nothing.
  * Returns SD_EINVAL for NULL required pointers, batch < 1, K < 0, vocab < 1
- * or an unknown logits dtype, and SD_EUNSUPPORTED for vocab > 262144.
+ * or an unknown logits dtype, and SD_EUNSUPPORTED for vocab > 262144 or a
+ * tree with K+1 > 64.
  * ---------------------------------------------------------------------- */
 typedef struct sd_accept_desc {
     int batch;

@@ -69,8 +69,9 @@ class RollbackDesc(ctypes.Structure):
 
 
 # Every symbol include/sdv.h declares.
-EXPORTS = ["sd_abi_version", "sd_last_error", "sd_verify_attn_workspace_size", "sd_verify_attn",
-           "sd_lm_head", "sd_accept_workspace_size", "sd_accept", "sd_kv_rollback"]
+EXPORTS = ["sd_abi_version", "sd_last_error", "sd_get_device_error",
+           "sd_verify_attn_workspace_size", "sd_verify_attn", "sd_lm_head",
+           "sd_accept_workspace_size", "sd_accept", "sd_kv_rollback"]
 
 _lib = None
 
@@ -93,6 +94,7 @@ def lib():
                                                ctypes.POINTER(ctypes.c_size_t)]
         L.sd_accept.argtypes = [ctypes.POINTER(AcceptDesc), _P, ctypes.c_size_t, _P]
         L.sd_kv_rollback.argtypes = [ctypes.POINTER(RollbackDesc), _P]
+        L.sd_get_device_error.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), _P]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or _I
         L.sd_last_error.restype = ctypes.c_char_p
@@ -143,6 +145,15 @@ def sd_accept(desc: AcceptDesc, workspace: int, ws_bytes: int, stream: int) -> N
 
 def sd_kv_rollback(desc: RollbackDesc, stream: int) -> None:
     _check(lib().sd_kv_rollback(ctypes.byref(desc), _P(stream)), "sd_kv_rollback")
+
+
+def sd_get_device_error(dev_error: int, stream: int) -> int:
+    """The SD_DERR_* word at device address dev_error, once `stream` has
+    passed the calls issued on it (synchronises the host)."""
+    code = ctypes.c_int32(0)
+    _check(lib().sd_get_device_error(_P(dev_error), ctypes.byref(code), _P(stream)),
+           "sd_get_device_error")
+    return code.value
 
 
 # ---------------------------------------------------------------------------
@@ -277,6 +288,12 @@ def rollback_desc(*, page_table, num_accepted, seq_lens, K, rollback_slots, roll
 
 def kv_rollback(desc: RollbackDesc, stream=None):
     sd_kv_rollback(desc, current_stream() if stream is None else stream)
+
+
+def device_error(dev_error, stream=None) -> int:
+    """sd_get_device_error on an int32 device tensor."""
+    return sd_get_device_error(dev_error.data_ptr(),
+                               current_stream() if stream is None else stream)
 
 
 from .step import VerifyStep  # noqa: E402  (uses the helpers above)

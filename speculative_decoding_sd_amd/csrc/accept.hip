@@ -671,6 +671,7 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
     __shared__ double s_wsum[kDecWaves];
     __shared__ double s_chunk_sum[kDecWaves * kDecMaxChunks];
     __shared__ int s_cand[kDecWaves];
+    __shared__ int s_depth[64];  // tree node depths (trees have K + 1 <= 64 nodes)
     const int Q = K + 1;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -683,7 +684,8 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         if (!flags && tree_parent) {
             // A tree: strict greedy requests only, well-formed parents.
             const int32_t* par = tree_parent + (size_t)b * Q;
-            bool bad = !(temperature[b] == 0.f) ||
+            s_depth[0] = 0;
+            bool bad = Q > 64 || !(temperature[b] == 0.f) ||
                        (relaxed_topk != nullptr && relaxed_topk[b] != 0) || par[0] != -1;
             for (int n = 1; n < Q && !bad; ++n) bad = par[n] < 0 || par[n] >= n;
             if (bad) flags |= SD_DERR_TREE;
@@ -691,25 +693,32 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         if (flags) {
             set_error(err, flags);
         } else if (tree_parent) {
-            // Descend from the root through the first child whose draft is
-            // the current node's argmax; the path and its tokens are written
-            // here (node indices in accepted_nodes, drafts in out_tokens).
+            // Node n is accepted when its parent is (the root always is) and
+            // its draft is the parent row's argmax.  One pass in node order
+            // (parents first) gives every node's depth and acceptance; the
+            // deepest accepted node, the first one found on ties (smallest
+            // index), ends the kept path.  The path and its drafts are
+            // written here, walking back up through the parents.
             const int32_t* par = tree_parent + (size_t)b * Q;
-            int cur = 0;
-            j = 0;
-            int t = stats[(size_t)b * Q].argmax;
-            for (;;) {
-                int next = -1;
-                for (int c = cur + 1; c < Q && next < 0; ++c)
-                    if (par[c] == cur && drafts[(size_t)b * K + c - 1] == t) next = c;
-                if (next < 0) break;
-                ++j;
-                if (accepted_nodes) accepted_nodes[(size_t)b * Q + j] = next;
-                out_tokens[(size_t)b * Q + j - 1] = t;
-                cur = next;
-                t = stats[(size_t)b * Q + cur].argmax;
+            uint64_t acc = 1;  // bit n: node n accepted (Q <= 64)
+            int best = 0, best_depth = 0;
+            for (int n = 1; n < Q; ++n) {
+                const int p = par[n], d = drafts[(size_t)b * K + n - 1];
+                s_depth[n] = s_depth[p] + 1;
+                if (((acc >> p) & 1) && d >= 0 && d == stats[(size_t)b * Q + p].argmax) {
+                    acc |= 1ull << n;
+                    if (s_depth[n] > best_depth) {
+                        best = n;
+                        best_depth = s_depth[n];
+                    }
+                }
             }
-            f = t;
+            j = best_depth;
+            for (int c = best; c != 0; c = par[c]) {
+                if (accepted_nodes) accepted_nodes[(size_t)b * Q + s_depth[c]] = c;
+                out_tokens[(size_t)b * Q + s_depth[c] - 1] = drafts[(size_t)b * K + c - 1];
+            }
+            f = stats[(size_t)b * Q + best].argmax;
             mode = kModeTree;
         } else if (temperature[b] == 0.f) {
             // Strict: the draft must be the row's argmax.  Relaxed (top-N >
@@ -816,16 +825,32 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
             int fc = -1;
             for (int w = 0; w < kDecWaves && fc < 0; ++w) {
                 if (run + s_wsum[w] > target) {
+                    // The crossing wave.  Its chunk sums are added one by
+                    // one here, in another order than its wave sum, so
+                    // rounding may leave every chunk short of the target:
+                    // then the wave's last chunk of positive weight is
+                    // taken (the in-chunk search below then ends on its
+                    // last positive token), not a token of a later wave.
                     const int cb = w * cpw, ce = min(nchunks, cb + cpw);
+                    const double run0 = run;
+                    int lastpos = -1;
+                    double pre_last = run0;
                     for (int c = cb; c < ce; ++c) {
                         const double cs = s_chunk_sum[w * kDecMaxChunks + (c - cb)];
                         if (run + cs > target) {
                             fc = c;
                             break;
                         }
+                        if (cs > 0.0) {
+                            lastpos = c;
+                            pre_last = run;
+                        }
                         run += cs;
                     }
-                    if (fc < 0) break;  // rounding: fall back below
+                    if (fc < 0) {
+                        fc = lastpos;  // >= 0: the wave's weight is positive
+                        run = pre_last;
+                    }
                 } else {
                     run += s_wsum[w];
                 }
@@ -1002,6 +1027,8 @@ int check_accept(const sd_accept_desc* d) {
     if ((long)d->vocab > (long)kDecWaves * kDecMaxChunks * kDecChunk)
         return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d",
                     kDecWaves * kDecMaxChunks * kDecChunk);
+    if (d->tree_parent && d->K + 1 > 64)
+        return fail(SD_EUNSUPPORTED, "sd_accept: a draft tree needs K+1 <= 64, got %d", d->K + 1);
     return SD_OK;
 }
 
@@ -1019,19 +1046,22 @@ extern "C" int sd_accept_workspace_size(const sd_accept_desc* d, size_t* bytes) 
     return SD_OK;
 }
 
-extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* stream) {
-    clear_error();
-    int rc = check_accept(d);
-    if (rc != SD_OK) return rc;
+namespace sdv {
+namespace {
+
+int check_accept_pointers(const sd_accept_desc* d, const char* what) {
     if (!d->logits || !d->temperature || !d->u_accept || !d->u_sample || !d->num_accepted ||
         !d->out_tokens || !d->next_token || !d->out_offsets || !d->packed_tokens ||
         (d->K > 0 && !d->draft_tokens))
-        return fail(SD_EINVAL, "sd_accept: NULL required pointer");
-    if (!workspace || !aligned256(workspace))
-        return fail(SD_EINVAL, "sd_accept: workspace NULL or not 256-byte aligned");
-    const size_t need = accept_ws_bytes(d);
-    if (ws_bytes < need) return fail(SD_EWORKSPACE, "sd_accept: workspace %zu < %zu", ws_bytes, need);
-    hipStream_t s = (hipStream_t)stream;
+        return fail(SD_EINVAL, "%s: NULL required pointer", what);
+    return SD_OK;
+}
+
+// The kernels of one acceptance call, with the row statistics and slice
+// records in `workspace` (accept_ws_bytes(d) bytes, 256-byte aligned; no
+// initialisation needed: every record is written before it is read).
+int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
+    int rc;
     const int B = d->batch, K = d->K, V = d->vocab, Q = K + 1;
     const int rows = B * Q;
     int splits, span;
@@ -1092,4 +1122,19 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
     accept_pack<<<1, 1024, 0, s>>>(d->num_accepted, d->out_tokens, d->out_offsets,
                                    d->packed_tokens, B, Q);
     return check_launch("accept_pack");
+}
+
+}  // namespace
+}  // namespace sdv
+
+extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    int rc = check_accept(d);
+    if (rc != SD_OK) return rc;
+    if ((rc = check_accept_pointers(d, "sd_accept")) != SD_OK) return rc;
+    if (!workspace || !aligned256(workspace))
+        return fail(SD_EINVAL, "sd_accept: workspace NULL or not 256-byte aligned");
+    const size_t need = accept_ws_bytes(d);
+    if (ws_bytes < need) return fail(SD_EWORKSPACE, "sd_accept: workspace %zu < %zu", ws_bytes, need);
+    return accept_launch(d, workspace, (hipStream_t)stream);
 }

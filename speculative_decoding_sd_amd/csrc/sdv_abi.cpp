@@ -43,3 +43,16 @@ int cu_count(const char* what, int* n) {
 extern "C" int sd_abi_version(void) { return SD_ABI_VERSION; }
 
 extern "C" const char* sd_last_error(void) { return sdv::g_last_error; }
+
+extern "C" int sd_get_device_error(const int32_t* dev_error, int32_t* code, void* stream) {
+    sdv::clear_error();
+    if (!dev_error || !code) return sdv::fail(SD_EINVAL, "sd_get_device_error: NULL pointer");
+    hipStream_t s = (hipStream_t)stream;
+    int32_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, dev_error, sizeof word, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return sdv::fail(SD_EDEVICE, "sd_get_device_error: %s", hipGetErrorString(e));
+    *code = word;
+    return SD_OK;
+}

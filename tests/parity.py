@@ -127,3 +127,47 @@ def gather_requests(wl, reqs):
         "k_cache": host(t["k_cache"].index_select(0, idx)),
         "v_cache": host(t["v_cache"].index_select(0, idx)) if t.get("v_cache") is not None else None,
     }
+
+
+def sample_requests(seq_lens, rng, n_random=2):
+    """Requests a full-size test checks row by row: the longest and the
+    shortest request, plus n_random others drawn at random."""
+    L = np.asarray(seq_lens)
+    picks = {int(np.argmax(L)), int(np.argmin(L))}
+    others = [b for b in range(len(L)) if b not in picks]
+    if others:
+        picks |= set(int(b) for b in rng.choice(others, min(n_random, len(others)),
+                                                 replace=False))
+    return np.array(sorted(picks))
+
+
+def gqa_wave_split_pairs(seq_lens, num_q, n_kv_heads, R, max_seq_len, e4m3, cus):
+    """(request, kv head) pairs whose key tiles the streaming GQA kernel
+    divides between two or more waves, so that their output goes through
+    the partial slots and the log-sum-exp combine.  Mirrors the launch: every
+    pair holds ceil((L_b + K + 1) / 32) tiles, kv-head-major then request;
+    waves = 4 x min(CUs x workgroups per CU, max_waves / 4), max_waves the
+    tile count at max_seq_len rounded up to 4 waves (at most 2048); wave w of
+    n = min(waves, T) takes tiles [floor(wT/n), floor((w+1)T/n))."""
+    L = np.asarray(seq_lens, np.int64)
+    B = len(L)
+    n_b = (L + num_q + 31) // 32
+    first = np.concatenate([[0], np.cumsum(n_b)])
+    T = n_kv_heads * int(first[-1])
+    groups = 2 if (e4m3 and R <= 32) else 1
+    max_tiles = B * n_kv_heads * ((max_seq_len + num_q + 31) // 32)
+    max_waves = min(2048, 4 * ((max_tiles + 3) // 4))
+    n = min(4 * min(cus * groups, max_waves // 4), T)
+
+    def wave(x):  # the wave that holds tile x: ceil((x + 1) n / T) - 1
+        return -(-(x + 1) * n // T) - 1
+
+    out = []
+    for h in range(n_kv_heads):
+        for b in range(B):
+            if n_b[b] == 0:
+                continue
+            g0 = h * int(first[-1]) + int(first[b])
+            if wave(g0) != wave(g0 + int(n_b[b]) - 1):
+                out.append((b, h))
+    return out

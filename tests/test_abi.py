@@ -136,6 +136,14 @@ def test_accept_and_rollback_host_validation():
     with pytest.raises(sdv.SdvError) as e:
         sdv.sd_accept_workspace_size(d)
     assert e.value.code == sdv.SD_EINVAL
+    d.logits_dtype = 1
+    d.K = 64                                    # a tree of 65 nodes
+    d.tree_parent = 4096
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_accept_workspace_size(d)
+    assert e.value.code == sdv.SD_EUNSUPPORTED
+    d.K = 63
+    assert sdv.sd_accept_workspace_size(d) % 256 == 0
     r = sdv.RollbackDesc(batch=2, K=3, page_size=64, max_pages=4, page_table=0,
                          num_accepted=256, seq_lens=512, rollback_slots=768,
                          rollback_offsets=1024, freed_pages=1280, freed_offsets=1536)
@@ -173,3 +181,13 @@ def test_descriptors_keep_their_tensors_alive():
     del d
     gc.collect()
     assert ref() is None
+
+
+def test_device_error_query_rejects_null_pointers():
+    """sd_get_device_error checks its pointers before touching the device."""
+    L = sdv.lib()
+    code = ctypes.c_int32(-7)
+    assert L.sd_get_device_error(None, ctypes.byref(code), None) == sdv.SD_EINVAL
+    assert code.value == -7 and "NULL" in sdv.last_error()
+    assert L.sd_get_device_error(ctypes.c_void_p(4096), None, None) == sdv.SD_EINVAL
+

@@ -4,7 +4,13 @@ The oracle cannot redo these in seconds, so each call is checked on samples
 it can compute one by one: attention rows of a few requests (their pages
 copied to the host before the step), LM-head rows against exact fp64 dot
 products, and acceptance plus rollback over the whole batch, with the GPU's
-own logits as the acceptance input."""
+own logits as the acceptance input.
+
+The sampled requests always include the longest and the shortest one; for
+the GQA kernel at least one sampled (request, kv head) pair is cut between
+waves (so its rows go through the partial slots and the combine), and the
+attention rows include every row of such a pair's first query head.  At
+least 64 attention rows and 32 LM-head rows are checked per configuration."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +19,7 @@ import oracle
 import sdsynth
 import speculative_decoding_sd_amd as sdv
 from parity import (DEV, bits, host, check_attention, check_logits_bf16, compare_accept,
-                    gather_requests)
+                    gather_requests, gqa_wave_split_pairs, sample_requests)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +54,7 @@ def test_full_config_step(ci):
     t = wl.tensors
     B, Q = cfg.batch, cfg.num_q
     rng = np.random.default_rng(ci)
-    reqs = np.sort(rng.choice(B, min(B, 2), replace=False))
+    reqs = sample_requests(wl.seq_lens, rng, n_random=1 if ci == 4 else 2)
     sample = gather_requests(wl, reqs)
     print(f"config {ci}: sampled requests {reqs.tolist()}", flush=True)
 
@@ -72,12 +78,13 @@ def test_full_config_step(ci):
     torch.cuda.synchronize()
     assert int(step.dev_error.item()) == 0
 
-    # Attention: 24 sampled rows of the sampled requests.
+    # Attention: at least 64 rows of the sampled requests.
     kc, vc = sample["k_cache"], sample["v_cache"]
     oracle.kv_append(sample["seq_lens"], sample["page_table"], sample["num_pages"],
                      sample["k_new"], sample["v_new"], kc, vc, mla=cfg.mla)
-    sel = np.stack([rng.integers(0, len(reqs), 24), rng.integers(0, Q, 24),
-                    rng.integers(0, cfg.n_q_heads, 24)], 1)
+    longest_first = np.argsort(-sample["seq_lens"], kind="stable")
+    sel, n_split = _attention_rows(cfg, wl, reqs, rng, cfg.mla, False)
+    print(f"config {ci}: {len(sel)} attention rows, {n_split} sampled split pairs", flush=True)
     ref = oracle.verify_attn(sample["q"], kc, vc, sample["page_table"], sample["seq_lens"],
                              sample["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
                              mla=cfg.mla, sel=sel)
@@ -85,8 +92,8 @@ def test_full_config_step(ci):
     got = np.stack([o[reqs[b], i, h] for b, i, h in sel])
     check_attention(got, ref, where=f"config {ci} attention")
 
-    # LM head: 6 sampled rows, exact fp64 logits from the kernel's own input.
-    rows = rng.choice(B * Q, 6, replace=False).astype(np.int32)
+    # LM head: at least 32 rows, exact fp64 logits from the kernel's own input.
+    rows = _lm_rows(B, Q, reqs[longest_first], rng)
     hin = bits(step.hin.index_select(0, torch.tensor(rows, dtype=torch.long, device=DEV)))
     exact = oracle.lm_head(hin, bits(t["W"]))
     lg_rows = bits(step.logits.view(B * Q, -1).index_select(
@@ -140,7 +147,7 @@ def test_full_config_variants(ci, kv, tree):
     par = sdsynth.tree_parents(tree, Q) if tree else None
     par_b = np.tile(par, (B, 1)) if tree else None
     rng = np.random.default_rng(ci + 10)
-    reqs = np.sort(rng.choice(B, 2, replace=False))
+    reqs = sample_requests(wl.seq_lens, rng, n_random=1 if ci == 4 else 2)
     sample = gather_requests(wl, reqs)
     if kv == "e4m3":   # host() keeps uint8 codes as they are
         scales = dict(k_scale=t["k_scale"].cpu().numpy(), v_scale=t["v_scale"].cpu().numpy())
@@ -172,8 +179,9 @@ def test_full_config_variants(ci, kv, tree):
     kc, vc = sample["k_cache"], sample["v_cache"]
     oracle.kv_append(sample["seq_lens"], sample["page_table"], sample["num_pages"],
                      sample["k_new"], sample["v_new"], kc, vc, **scales)
-    sel = np.stack([rng.integers(0, len(reqs), 24), rng.integers(0, Q, 24),
-                    rng.integers(0, cfg.n_q_heads, 24)], 1)
+    sel, n_split = _attention_rows(cfg, wl, reqs, rng, False, kv == "e4m3")
+    print(f"config {ci} {kv} {tree}: {len(sel)} attention rows, {n_split} sampled split "
+          f"pairs", flush=True)
     ref = oracle.verify_attn(sample["q"], kc, vc, sample["page_table"], sample["seq_lens"],
                              sample["num_pages"], n_kv_heads=cfg.n_kv_heads, d_v=cfg.d_v,
                              sel=sel, tree_parent=par_b[:len(reqs)] if tree else None, **scales)
@@ -181,7 +189,7 @@ def test_full_config_variants(ci, kv, tree):
     check_attention(np.stack([o[reqs[b], i, h] for b, i, h in sel]), ref,
                     where=f"config {ci} {kv} {tree} attention")
 
-    rows = rng.choice(B * Q, 4, replace=False).astype(np.int32)
+    rows = _lm_rows(B, Q, reqs[np.argsort(-sample["seq_lens"], kind="stable")], rng)
     ridx = torch.tensor(rows, dtype=torch.long, device=DEV)
     exact = oracle.lm_head(bits(step.hin.index_select(0, ridx)), bits(t["W"]))
     check_logits_bf16(bits(step.logits.view(B * Q, -1).index_select(0, ridx)), exact,
@@ -229,3 +237,37 @@ def test_full_config_variants(ci, kv, tree):
             got = kc_gpu[pg_g, :, off]
             got = got.cpu().numpy() if kv == "e4m3" else bits(got)
             assert np.array_equal(got, kc[pg_s, :, off]), (b, p)
+
+
+def _attention_rows(cfg, wl, reqs, rng, mla, e4m3, n_rows=64):
+    """Rows (index into reqs, position, query head) to check: every position
+    of one head of a wave-split pair among the sampled requests (GQA), then
+    random rows up to n_rows, at least one per position of every sampled
+    request."""
+    Q, Hq, Hkv = cfg.num_q, cfg.n_q_heads, cfg.n_kv_heads
+    rows = []
+    split = []
+    if not mla:
+        cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+        R = (Hq // Hkv) * Q
+        split = [(b, h) for b, h in gqa_wave_split_pairs(
+            wl.seq_lens, Q, Hkv, R, int(wl.seq_lens.max()), e4m3, cus) if b in set(reqs.tolist())]
+        assert split, "no sampled (request, kv head) pair is split between waves"
+        b, h = split[int(rng.integers(len(split)))]
+        k = int(np.nonzero(reqs == b)[0][0])
+        G = Hq // Hkv
+        rows += [(k, i, h * G + int(rng.integers(G))) for i in range(Q)]
+    for k in range(len(reqs)):
+        rows += [(k, i, int(rng.integers(Hq))) for i in range(Q)]
+    while len(rows) < n_rows:
+        rows.append((int(rng.integers(len(reqs))), int(rng.integers(Q)), int(rng.integers(Hq))))
+    return np.array(rows, np.int64), len(split)
+
+
+def _lm_rows(B, Q, reqs, rng, n_rows=32):
+    """LM-head rows to check: every row of the longest sampled request (the
+    first one listed), then random rows up to n_rows."""
+    rows = set(int(reqs[0]) * Q + i for i in range(Q))
+    while len(rows) < n_rows:
+        rows.add(int(rng.integers(B * Q)))
+    return np.array(sorted(rows), np.int32)

@@ -41,8 +41,11 @@ def _run_gpu_attention(wl, max_seq_len=None, append=True, lowp=True):
                       max_seq_len=int(max_seq_len or wl.seq_lens.max()), k_new=kn, v_new=vn,
                       out_lowp=out_lowp, dev_error=err)
     sdv.verify_attn(d)
+    # The error word through the C ABI's own query (it waits for the stream).
+    word = sdv.device_error(err)
     torch.cuda.synchronize()
-    return out, out_lowp, kc, vc, int(err.item())
+    assert word == int(err.item())
+    return out, out_lowp, kc, vc, word
 
 
 def _oracle_attention(wl, sel=None, append=True):

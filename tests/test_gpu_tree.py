@@ -154,6 +154,19 @@ def test_tree_accept_greedy(B, K, V, dtype):
                      ("packed_tokens", "packed"), ("accepted_nodes", "accepted_nodes")):
         assert np.array_equal(gpu[k_g], ref[k_r]), k_g
     assert ref["num_accepted"].max() >= 3        # the walk went deep somewhere
+    # The batch holds requests where descending through the first matching
+    # child would stop short of the longest accepted path.
+    shorter = 0
+    for b in range(B):
+        cur, depth = 0, 0
+        while True:
+            nxt = [c for c in range(cur + 1, Q)
+                   if par[b, c] == cur and drafts[b, c - 1] == tmax[b, cur]]
+            if not nxt:
+                break
+            cur, depth = nxt[0], depth + 1
+        shorter += depth < ref["num_accepted"][b]
+    assert shorter > 0
 
 
 def test_tree_accept_invalid_requests():
