@@ -323,6 +323,20 @@ int sd_accept_workspace_size(const sd_accept_desc* d, size_t* bytes);
 /* workspace: device, >= sd_accept_workspace_size, 256-byte aligned. */
 int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* stream);
 
+/* Allocation-free sd_accept, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same descriptor, outputs and semantics as sd_accept; the row
+ * statistics live in a fixed 4 MiB device array of the library instead of a
+ * caller workspace (one copy per GPU, held until the process ends).  That
+ * covers batches of up to about 65000 logits rows (B*(K+1)); a larger batch
+ * gets SD_EWORKSPACE before anything is launched.  Every call on one GPU
+ * uses that GPU's one array, so calls that overlap on one GPU (on different
+ * streams, or from host threads without an order between them) race: the
+ * caller serialises them.  The first call on a device looks the array's
+ * address up (hipGetSymbolAddress) with that device current; no call
+ * allocates or frees memory. */
+int sd_accept_noalloc(const sd_accept_desc* d, void* stream);
+
 /* ------------------------------------------------------------------------
  * KV rollback.  [TRT-MTP] "MTP Vanilla"/"MTP Eagle": the keys/values of
  * discarded drafts are cleared so later steps stay correct; "基本實現方式"

@@ -71,7 +71,7 @@ class RollbackDesc(ctypes.Structure):
 # Every symbol include/sdv.h declares.
 EXPORTS = ["sd_abi_version", "sd_last_error", "sd_get_device_error",
            "sd_verify_attn_workspace_size", "sd_verify_attn", "sd_lm_head",
-           "sd_accept_workspace_size", "sd_accept", "sd_kv_rollback"]
+           "sd_accept_workspace_size", "sd_accept", "sd_accept_noalloc", "sd_kv_rollback"]
 
 _lib = None
 
@@ -93,6 +93,7 @@ def lib():
         L.sd_accept_workspace_size.argtypes = [ctypes.POINTER(AcceptDesc),
                                                ctypes.POINTER(ctypes.c_size_t)]
         L.sd_accept.argtypes = [ctypes.POINTER(AcceptDesc), _P, ctypes.c_size_t, _P]
+        L.sd_accept_noalloc.argtypes = [ctypes.POINTER(AcceptDesc), _P]
         L.sd_kv_rollback.argtypes = [ctypes.POINTER(RollbackDesc), _P]
         L.sd_get_device_error.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), _P]
         for name in EXPORTS:
@@ -141,6 +142,10 @@ def sd_accept_workspace_size(desc: AcceptDesc) -> int:
 def sd_accept(desc: AcceptDesc, workspace: int, ws_bytes: int, stream: int) -> None:
     _check(lib().sd_accept(ctypes.byref(desc), _P(workspace), ws_bytes, _P(stream)),
            "sd_accept")
+
+
+def sd_accept_noalloc(desc: AcceptDesc, stream: int) -> None:
+    _check(lib().sd_accept_noalloc(ctypes.byref(desc), _P(stream)), "sd_accept_noalloc")
 
 
 def sd_kv_rollback(desc: RollbackDesc, stream: int) -> None:

@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sdv_device.h"
 #include "sdv_internal.h"
@@ -1124,6 +1125,40 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
     return check_launch("accept_pack");
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of sd_accept_noalloc: a fixed device array instead of a caller
+// workspace, for callers that cannot allocate.  Each GPU the library runs on
+// holds its own copy until the process ends.  Host code never names the
+// array in a launch or a copy: its name there is a host-side stand-in, so
+// the device address is looked up once per device with hipGetSymbolAddress
+// and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+constexpr size_t kAcceptScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with the device current).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(SD_EDEVICE, "sd_accept_noalloc: no usable current device");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SD_EDEVICE, "sd_accept_noalloc: scratch address on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SD_OK;
+}
+
 }  // namespace
 }  // namespace sdv
 
@@ -1137,4 +1172,19 @@ extern "C" int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_byt
     const size_t need = accept_ws_bytes(d);
     if (ws_bytes < need) return fail(SD_EWORKSPACE, "sd_accept: workspace %zu < %zu", ws_bytes, need);
     return accept_launch(d, workspace, (hipStream_t)stream);
+}
+
+extern "C" int sd_accept_noalloc(const sd_accept_desc* d, void* stream) {
+    clear_error();
+    int rc = check_accept(d);
+    if (rc != SD_OK) return rc;
+    if ((rc = check_accept_pointers(d, "sd_accept_noalloc")) != SD_OK) return rc;
+    const size_t need = accept_ws_bytes(d);
+    if (need > kAcceptScratchBytes)
+        return fail(SD_EWORKSPACE,
+                    "sd_accept_noalloc: this batch needs %zu bytes of scratch, above the fixed "
+                    "%zu (use sd_accept with a workspace)", need, kAcceptScratchBytes);
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws)) != SD_OK) return rc;
+    return accept_launch(d, ws, (hipStream_t)stream);
 }

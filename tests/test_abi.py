@@ -191,3 +191,18 @@ def test_device_error_query_rejects_null_pointers():
     assert code.value == -7 and "NULL" in sdv.last_error()
     assert L.sd_get_device_error(ctypes.c_void_p(4096), None, None) == sdv.SD_EINVAL
 
+
+def test_noalloc_accept_rejects_batches_beyond_its_scratch():
+    """sd_accept_noalloc checks the batch against its fixed scratch before it
+    touches the device: 70000 rows need more than the 4 MiB it holds."""
+    d = sdv.AcceptDesc(batch=70000, K=0, vocab=100, logits_dtype=1, logits=256,
+                       draft_tokens=0, temperature=768, top_p=0, draft_probs=0, u_accept=1024,
+                       u_sample=1280, num_accepted=1536, out_tokens=1792, next_token=2048,
+                       out_offsets=2304, packed_tokens=2560, dev_error=0)
+    with pytest.raises(sdv.SdvError) as e:
+        sdv.sd_accept_noalloc(d, 0)
+    assert e.value.code == sdv.SD_EWORKSPACE and "scratch" in e.value.args[0] + sdv.last_error()
+    d.out_tokens = 0
+    with pytest.raises(sdv.SdvError) as e:      # pointers are checked first
+        sdv.sd_accept_noalloc(d, 0)
+    assert e.value.code == sdv.SD_EINVAL
