@@ -52,6 +52,16 @@ constexpr int kStages = 2;
 constexpr int kDmaPerWave = kTileKeys * kRowChunks / 256;  // 9 x 1 KiB per wave
 constexpr float kRefSlack = 64.f;  // log2 units a later tile may exceed the reference max by
 constexpr int kRowsPerBlock = 128;
+
+// XOR applied to the 16-byte chunk index of latent row `row` of a tile
+// (values 0..7, so each aligned group of 8 chunks maps onto itself).  The
+// 1152-byte row stride puts odd rows 32 banks (8 chunks) over from even
+// ones, so a ds_read_b128 pass (16 rows, one logical chunk) is free of bank
+// conflicts when the 8 rows of each parity get 8 distinct values: the XOR is
+// a bijection of row bits 1..3.  A ds_read_b64_tr_b16 pass (lanes 0..31:
+// rows r, r+1, r+2, r+3 of one parity pair, four chunks of each) needs rows
+// r and r+2 to differ in bit 2 of the XOR, which bit 1 of the row gives.
+__device__ __forceinline__ int mla_swz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 constexpr int kQSteps = kDqk / 16;     // 36 MFMA k-steps over the latent
 constexpr int kQReg = 18;              // Q^T steps held in registers
 constexpr int kQLds = kQSteps - kQReg; // Q^T steps read from LDS each tile
@@ -105,11 +115,11 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
 
     // DMA slots of this lane: instruction j of wave w fills LDS chunks
     // n = 64 (4j + w) + lane of the tile; chunk n holds latent row n / 72,
-    // logical chunk (n % 72) ^ chunk_xor(row).
+    // logical chunk (n % 72) ^ mla_swz(row).
     auto goff = [&](int j) {
         const int n = 64 * (4 * j + wave) + lane;
         const int key = n / kRowChunks;
-        return key * kDqk + 8 * ((n - key * kRowChunks) ^ chunk_xor(key));
+        return key * kDqk + 8 * ((n - key * kRowChunks) ^ mla_swz(key));
     };
     const uint32_t lds0 = lds_byte_addr(&s_lat[0][0]);
     auto tile_src = [&](int t) {
@@ -124,16 +134,20 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
 
     // Per-lane LDS byte offsets within a tile.
     //  S^T reads: key ln, logical chunk 2s + lh -> slot 8(s/4) + (2(s%4) ^ kx).
-    const int kx = lh ^ chunk_xor(ln);
+    const int kx = lh ^ mla_swz(ln);
     int koff[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) koff[r] = ln * kRowBytes + 16 * ((2 * r) ^ kx);
     //  V^T reads (16-lane group g, lane sl): key 16tt + 4(g/2) + sl/4 (+8),
     //  logical chunk 4db + 2(g&1) + (sl&3)/2, byte 8(sl&1) of the chunk.
+    //  The two key rows of a fragment (kr and kr + 8) have different XORs.
     const int g = lane >> 4, sl = lane & 15;
-    const int vx = (2 * (g & 1) + ((sl & 3) >> 1)) ^ (2 * (sl >> 2) + ((g >> 1) & 1));
-    const int vrow = (4 * (g >> 1) + (sl >> 2)) * kRowBytes + 8 * (sl & 1);
-    const int voff_e = vrow + 16 * vx, voff_o = vrow + 16 * (4 ^ vx);
+    const int kr = 4 * (g >> 1) + (sl >> 2);
+    const int vll = 2 * (g & 1) + ((sl & 3) >> 1);
+    const int vx0 = vll ^ mla_swz(kr), vx1 = vll ^ mla_swz(kr + 8);
+    const int vrow = kr * kRowBytes + 8 * (sl & 1);
+    const int voff_e0 = vrow + 16 * vx0, voff_o0 = vrow + 16 * (4 ^ vx0);
+    const int voff_e1 = vrow + 8 * kRowBytes + 16 * vx1, voff_o1 = vrow + 8 * kRowBytes + 16 * (4 ^ vx1);
 
     // O^T blocks 0..14 live in registers; block 15 lives in this wave's LDS
     // slot between tiles (layout [q][lane][4] floats: conflict-free 16-byte
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             const int nv = end - ks;
             for (int idx = tid; idx < (kTileKeys - nv) * 64; idx += 256) {
                 const int key = nv + (idx >> 6), c = idx & 63;
-                *(u32x4*)(tile + key * kRowBytes + 16 * (c ^ chunk_xor(key))) = u32x4{0, 0, 0, 0};
+                *(u32x4*)(tile + key * kRowBytes + 16 * (c ^ mla_swz(key))) = u32x4{0, 0, 0, 0};
             }
             __syncthreads();
         }
@@ -269,9 +283,9 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         // V^T fragments are read ahead.
         auto vfrag = [&](int idx) {  // idx = tt * 16 + db
             const int tt = idx >> 4, db = idx & 15;
-            const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1) + ((db & 1) ? voff_o : voff_e);
-            const u32x2 v0 = lds_read_tr16(vp);
-            const u32x2 v1 = lds_read_tr16(vp + 8 * kRowBytes);
+            const char* vp = tile + 16 * tt * kRowBytes + 128 * (db >> 1);
+            const u32x2 v0 = lds_read_tr16(vp + ((db & 1) ? voff_o0 : voff_e0));
+            const u32x2 v1 = lds_read_tr16(vp + ((db & 1) ? voff_o1 : voff_e1));
             return u32x4{v0.x, v0.y, v1.x, v1.y};
         };
         constexpr int PV = 3;  // V^T fragments read this many blocks ahead

@@ -1,7 +1,6 @@
 // Device helpers for the attention kernels on gfx950: direct
 // global->LDS DMA issued outside the compiler's view, explicit vmcnt waits,
-// the transposing LDS reads, the chunk swizzle of a K/V tile, half-wave
-// reductions and hardware bf16 packing.
+// the transposing LDS reads, half-wave reductions and hardware bf16 packing.
 #pragma once
 
 #include "sdv_device.h"
@@ -61,12 +60,6 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const char* p) {
         (__attribute__((address_space(3))) v2i*)(p));
     return __builtin_bit_cast(u32x2, r);
 }
-
-// XOR applied to the 16-byte chunk index of tile row `row` (values 0..7, so
-// each aligned group of 8 chunks maps onto itself).  With it, the eight rows a
-// ds_read_b128 phase touches (same chunk, rows r..r+7) and the 4 rows x 2
-// chunks of a ds_read_b64_tr_b16 phase each land in distinct bank groups.
-__device__ __forceinline__ int chunk_xor(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the
 // upper half of one copy with the lower half of the other: the pair then
