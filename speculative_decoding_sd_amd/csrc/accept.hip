@@ -159,11 +159,20 @@ struct RowAcc {
 // only then is the group searched for the first id of its max and z
 // rescaled.  Sampled rows then add the group's terms eight at a time (all
 // eight table reads issued before the first is used) as pairwise trees.
+// FAST (sampled rows without a nucleus): each term is exp2 in float32 of
+// (x - best) * log2(e) / T, eight of them summed in float32, the group sums
+// accumulated in fp64.  A term is then within a few float32 ulps, so Z is
+// within about 1e-6 relative: Z of such a row only scales p_t of the draft
+// (an acceptance decision it could move lies within 1e-6 of u) and the
+// draw's weights (a common scale, which the draw's running sums cancel).
+// Rows with a nucleus keep fp64 terms: their threshold compares the kept
+// mass with top_p * Z.
 // RELAX rows also count the elements ranked before the draft d (logit xd)
 // in the order (logit desc, id asc).
-template <bool STOCH, bool RELAX, int N>
+template <bool STOCH, bool RELAX, bool FAST, int N>
 __device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const int (&v)[N],
-                                         double invT, const double* tab, float xd, int d) {
+                                         double invT, const double* tab, float xd, int d,
+                                         float k2) {
     if constexpr (RELAX) {
 #pragma unroll
         for (int e = 0; e < N; ++e) a.beat += (x[e] > xd) | ((x[e] == xd) & (v[e] < d));
@@ -185,7 +194,24 @@ __device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const i
         a.best = gm;
         a.bidx = id;
     }
-    if constexpr (STOCH) {
+    if constexpr (STOCH && FAST) {
+        constexpr int G = N < 8 ? N : 8;
+        const float mt = a.best;
+        double acc = 0.0;
+#pragma unroll
+        for (int g = 0; g < N; g += G) {
+            float w[G];
+#pragma unroll
+            for (int e = 0; e < G; ++e)  // max drops the NaN of -inf - -inf (term 0)
+                w[e] = __builtin_amdgcn_exp2f(fmaxf((x[g + e] - mt) * k2, -160.f));
+#pragma unroll
+            for (int h = 1; h < G; h <<= 1)
+#pragma unroll
+                for (int e = 0; e + h < G; e += 2 * h) w[e] += w[e + h];
+            acc += (double)w[0];
+        }
+        a.z += acc;
+    } else if constexpr (STOCH) {
         constexpr int G = N < 8 ? N : 8;
         const double mtd = (double)a.best;
         double acc = 0.0;
@@ -210,10 +236,12 @@ __device__ __forceinline__ void row_fold(RowAcc& a, const float (&x)[N], const i
 }
 
 // One pass over ids [v_lo, v_hi) of a row (v_lo a multiple of the vector
-// width when vec_ok); U vectors in flight per thread.
-template <typename T, bool STOCH, bool RELAX>
+// width when vec_ok); U vectors in flight per thread.  k2 = log2(e) / T in
+// float32 (FAST rows).
+template <typename T, bool STOCH, bool RELAX, bool FAST = false>
 __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool vec_ok, RowAcc& a,
-                                         double invT, const double* tab, float xd, int d) {
+                                         double invT, const double* tab, float xd, int d,
+                                         float k2 = 0.f) {
     constexpr int E = Logit<T>::kPerVec;
     constexpr int U = RELAX ? 2 : 4;  // vectors in flight (fewer with the rank count)
     int v0 = v_lo;
@@ -233,7 +261,7 @@ __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool v
                     x[u * E + e] = Logit<T>::lane(w[u], e);
                     v[u * E + e] = (c + u * 256) * E + e;
                 }
-            row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
+            row_fold<STOCH, RELAX, FAST>(a, x, v, invT, tab, xd, d, k2);
         }
         for (; c < c_hi; c += 256) {
             const u32x4 w = *(const u32x4*)(lr + (size_t)c * E);
@@ -244,14 +272,14 @@ __device__ __forceinline__ void row_pass(const T* lr, int v_lo, int v_hi, bool v
                 x[e] = Logit<T>::lane(w, e);
                 v[e] = c * E + e;
             }
-            row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
+            row_fold<STOCH, RELAX, FAST>(a, x, v, invT, tab, xd, d, k2);
         }
         v0 = c_hi * E;
     }
     for (int vv = v0 + (int)threadIdx.x; vv < v_hi; vv += 256) {
         const float x[1] = {Logit<T>::at(lr, vv)};
         const int v[1] = {vv};
-        row_fold<STOCH, RELAX>(a, x, v, invT, tab, xd, d);
+        row_fold<STOCH, RELAX, FAST>(a, x, v, invT, tab, xd, d, k2);
     }
 }
 
@@ -272,6 +300,7 @@ template <typename T, bool RX>
 __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logits,
                                                       const int32_t* __restrict__ drafts,
                                                       const float* __restrict__ temperature,
+                                                      const float* __restrict__ top_p,
                                                       const int32_t* __restrict__ relaxed_topk,
                                                       RowPart* __restrict__ parts, int Q, int V,
                                                       int splits, int span, int vec_ok) {
@@ -294,8 +323,13 @@ __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logi
     const bool stoch = Tb > 0.f || count;  // the slice's sum is needed
     const float xd = count ? Logit<T>::at(lr, d) : 0.f;
     const bool vk = vec_ok != 0;
+    // Sampled rows without a nucleus take float32 terms (see row_fold).
+    const bool fast = Tb > 0.f && !count && (top_p == nullptr || !(top_p[b] < 1.f));
     RowAcc a;
     if (count) row_pass<T, true, RX>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
+    else if (fast)
+        row_pass<T, true, false, true>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d,
+                                       (float)(1.4426950408889634 * invT));
     else if (stoch) row_pass<T, true, false>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
     else row_pass<T, false, false>(lr, v_lo, v_hi, vk, a, invT, s_exptab, xd, d);
     float best = a.best;
@@ -660,8 +694,9 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
     const T* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ draft_probs,
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
-    const int32_t* __restrict__ relaxed_topk, const RowStat* __restrict__ stats,
-    int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
+    const int32_t* __restrict__ relaxed_topk, const float* __restrict__ top_p,
+    const RowStat* __restrict__ stats, int32_t* __restrict__ num_accepted,
+    int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ next_token, int32_t* err, int K, int V,
     const int32_t* __restrict__ tree_parent, int32_t* __restrict__ accepted_nodes) {
     __shared__ double s_exptab[64];
@@ -771,7 +806,7 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
         const T* lr = logits + ((size_t)b * Q + row) * V;
         const float* pd = draft_probs ? draft_probs + ((size_t)b * K + row) * V : nullptr;
         const double invT = 1.0 / (double)temperature[b];
-        const double invZ = 1.0 / st.zkeep;
+        double invZ = 1.0 / st.zkeep;
         const int nchunks = (V + kDecChunk - 1) / kDecChunk;
         const int cpw = (nchunks + kDecWaves - 1) / kDecWaves;  // chunks per wave
         const int c_begin = wave * cpw, c_end = min(nchunks, c_begin + cpw);
@@ -786,6 +821,31 @@ __global__ __launch_bounds__(kDecThreads) void accept_decide(
             for (int e = 0; e < 8; ++e) t += w[e];
             return t;
         };
+        if (resid && (top_p == nullptr || !(top_p[b] < 1.f))) {
+            // The row pass summed Z of a row without a nucleus from float32
+            // terms.  A draw from p_t is indifferent to a common scale, but
+            // the residual max(0, p_t - p_d) compares p_t with p_d token by
+            // token, so its Z is summed again here from fp64 terms, in the
+            // draw's fixed chunk order.
+            resid = false;
+            invZ = 1.0;
+            double zs = 0.0;
+            for (int c = c_begin; c < c_end; ++c) {
+                double w[8];
+                zs += wave_sum(lane_sum(c, w));
+            }
+            if (lane == 0) s_wsum[wave] = zs;
+            __syncthreads();
+            if (tid == 0) {
+                double tot = 0.0;
+                for (int w = 0; w < kDecWaves; ++w) tot += s_wsum[w];
+                s_total = tot;
+            }
+            __syncthreads();
+            invZ = 1.0 / s_total;
+            resid = true;
+            __syncthreads();
+        }
         for (int pass = 0; pass < 2; ++pass) {
             double wsum = 0.0;
             int c = c_begin;
@@ -1076,11 +1136,12 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
         const uint16_t* lg = (const uint16_t*)d->logits;
         if (d->relaxed_topk)
             accept_rowpart<uint16_t, true><<<rows * splits, 256, 0, s>>>(
-                lg, d->draft_tokens, d->temperature, d->relaxed_topk, parts, Q, V, splits, span,
-                vec_ok);
+                lg, d->draft_tokens, d->temperature, d->top_p, d->relaxed_topk, parts, Q, V, splits,
+                span, vec_ok);
         else
             accept_rowpart<uint16_t, false><<<rows * splits, 256, 0, s>>>(
-                lg, d->draft_tokens, d->temperature, nullptr, parts, Q, V, splits, span, vec_ok);
+                lg, d->draft_tokens, d->temperature, d->top_p, nullptr, parts, Q, V, splits, span,
+                vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
         accept_rowmerge<uint16_t><<<(rows + 255) / 256, 256, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
@@ -1093,17 +1154,19 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
         }
         accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
-            d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
+            d->relaxed_topk, d->top_p, stats, d->num_accepted, d->out_tokens, d->next_token,
+            d->dev_error,
             K, V, d->tree_parent, d->accepted_nodes);
     } else {
         const float* lg = (const float*)d->logits;
         if (d->relaxed_topk)
             accept_rowpart<float, true><<<rows * splits, 256, 0, s>>>(
-                lg, d->draft_tokens, d->temperature, d->relaxed_topk, parts, Q, V, splits, span,
-                vec_ok);
+                lg, d->draft_tokens, d->temperature, d->top_p, d->relaxed_topk, parts, Q, V, splits,
+                span, vec_ok);
         else
             accept_rowpart<float, false><<<rows * splits, 256, 0, s>>>(
-                lg, d->draft_tokens, d->temperature, nullptr, parts, Q, V, splits, span, vec_ok);
+                lg, d->draft_tokens, d->temperature, d->top_p, nullptr, parts, Q, V, splits, span,
+                vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
         accept_rowmerge<float><<<(rows + 255) / 256, 256, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
@@ -1116,7 +1179,8 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
         }
         accept_decide<float><<<B, kDecThreads, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
-            d->relaxed_topk, stats, d->num_accepted, d->out_tokens, d->next_token, d->dev_error,
+            d->relaxed_topk, d->top_p, stats, d->num_accepted, d->out_tokens, d->next_token,
+            d->dev_error,
             K, V, d->tree_parent, d->accepted_nodes);
     }
     if ((rc = check_launch("accept_decide")) != SD_OK) return rc;

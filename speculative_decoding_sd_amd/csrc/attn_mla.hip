@@ -26,9 +26,9 @@
 // Latent tiles arrive by LDS DMA (global_load_lds_dwordx4), double-buffered,
 // so no registers stage them.  Register budget (one wave per SIMD, 512
 // registers): O^T blocks 0..14 (240) and S^T (16) in AGPRs, the last O^T block
-// kept in LDS between tiles so that S^T can use its registers; half of Q^T in
-// VGPRs and half in LDS (read once per tile); the rest is fragment
-// prefetch, P and addressing.  LDS: 72 KiB latent + 72 KiB Q^T + 16 KiB O^T.  The 16-byte chunks of each 1152-byte latent row
+// kept in LDS between tiles so that S^T can use its registers; all of Q^T
+// (144) in VGPRs; the rest is fragment prefetch, P and addressing.  LDS:
+// 72 KiB latent + 16 KiB O^T.  The 16-byte chunks of each 1152-byte latent row
 // are XOR-swizzled so that both LDS read patterns are free of bank conflicts.
 // With one chunk per request the kernel writes the normalised output itself;
 // otherwise it writes chunk partials for attn_combine.
@@ -63,8 +63,6 @@ constexpr int kRowsPerBlock = 128;
 // r and r+2 to differ in bit 2 of the XOR, which bit 1 of the row gives.
 __device__ __forceinline__ int mla_swz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 constexpr int kQSteps = kDqk / 16;     // 36 MFMA k-steps over the latent
-constexpr int kQReg = 18;              // Q^T steps held in registers
-constexpr int kQLds = kQSteps - kQReg; // Q^T steps read from LDS each tile
 static_assert(4 * (kDmaPerWave - 1) < kQSteps, "a tile's DMAs are issued within the S^T k-steps");
 
 __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
@@ -76,7 +74,6 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     float scale_log2) {
     __shared__ __attribute__((aligned(1024))) uint16_t s_lat[kStages][kTileElems];
     __shared__ __attribute__((aligned(16))) float s_o15[4][16 * 64];
-    __shared__ __attribute__((aligned(16))) u32x4 s_qh[4][kQLds][64];
     const int tile_id = xcd_tile(blockIdx.x, total);
     const int rblk = tile_id % rblks;
     const int split = (tile_id / rblks) % max_splits;
@@ -95,22 +92,16 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const int pos_i = rows_live ? row0 / Hq : 0;
     const int lim = L + pos_i;  // causal: keys 0 .. L_b + i
 
-    // Q^T fragments (B operand): lane (row ln, half lh), step s -> dims 16s+8lh..+8.
-    // Steps 0..kQReg-1 stay in registers; the rest go to this wave's LDS
-    // slot (lane order, so each step is one conflict-free 16-byte read).
-    u32x4 qf[kQReg];
+    // Q^T fragments (B operand): lane (row ln, half lh), step s -> dims
+    // 16s+8lh..+8, all 36 steps held in registers for the whole chunk.
+    u32x4 qf[kQSteps];
     {
         const int row = row0 + ln;
         const int i = rows_live ? row / Hq : 0, h = rows_live ? row - i * Hq : 0;
         const uint16_t* qp = q + (((size_t)b * NQ + i) * Hq + h) * kDqk + 8 * lh;
 #pragma unroll
-        for (int s = 0; s < kQReg; ++s)
+        for (int s = 0; s < kQSteps; ++s)
             qf[s] = rows_live ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int s = kQReg; s < kQSteps; ++s) {
-            s_qh[wave][s - kQReg][lane] = rows_live ? *(const u32x4*)(qp + 16 * s) : u32x4{0, 0, 0, 0};
-            if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
     }
 
     // DMA slots of this lane: instruction j of wave w fills LDS chunks
@@ -197,30 +188,20 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             __syncthreads();
         }
 
-        // S^T = K Q^T over 576 dims, K (and LDS-held Q^T) fragments read ahead.
+        // S^T = K Q^T over 576 dims, K fragments read ahead.
         f32x16 sa;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sa[r] = 0.f;
         constexpr int PF = 4;  // read-ahead distance in k-steps
-        u32x4 kf[PF], qx[PF];
+        u32x4 kf[PF];
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
-            kf[s] = *(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2));
-            qx[s] = s_qh[wave][s][lane];
-        }
+        for (int s = 0; s < PF; ++s) kf[s] = *(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2));
 #pragma unroll
         for (int s = 0; s < kQSteps; ++s) {
             const u32x4 cur = kf[s % PF];
-            u32x4 qcur;
-            if (s < kQReg) {
-                qcur = qf[s];
-            } else {
-                qcur = qx[(s - kQReg) % PF];
-                if (s - kQReg + PF < kQLds) qx[(s - kQReg) % PF] = s_qh[wave][s - kQReg + PF][lane];
-            }
             if (s + PF < kQSteps)
                 kf[s % PF] = *(const u32x4*)(tile + koff[(s + PF) & 3] + 128 * ((s + PF) >> 2));
-            sa = mfma_32x32x16(cur, qcur, sa);
+            sa = mfma_32x32x16(cur, qf[s], sa);
             if (s % 4 == 0 && s / 4 < kDmaPerWave && more) tile_dma(nbase, ndst, s / 4);
             // Bounds how far the scheduler hoists reads.
             __builtin_amdgcn_sched_barrier(0);

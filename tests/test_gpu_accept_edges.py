@@ -6,7 +6,8 @@ a draft whose draft probability is 0 (accepted when its target probability
 is positive, rejected when both are 0), an all-zero residual after a
 rejection (the replacement comes from p_t), and draws at u = 1, where no
 running sum exceeds u * S and the largest id of positive weight is taken,
-both for a residual and for the bonus token.  Each of these is exact on both
+both for a residual and for the bonus token, and rows whose leading logits
+are -inf (masked tokens) with the drafts among them.  Each of these is exact on both
 sides (the decisions do not depend on summation order), so every request is
 compared, with no exclusion window.
 """
@@ -32,7 +33,7 @@ def _edge_batch(V, dtype, seed):
     K = 3
     Q = K + 1
     kinds = ["pd0_accept", "pd0_pt0_reject", "zero_residual", "u1_residual", "u1_bonus",
-             "u1_bonus_full", "greedy"]
+             "u1_bonus_full", "neg_inf_reject", "greedy"]
     B = len(kinds) * 2
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     lg = (torch.randn((B, Q, V), generator=torch.Generator().manual_seed(seed)) * 1.7).to(tdt)
@@ -92,6 +93,15 @@ def _edge_batch(V, dtype, seed):
                 drafts[b, n] = int(np.argmax(lg.float().numpy()[b, n]))
                 pd[b, n, drafts[b, n]] = 0.0
             us[b, K] = 1.0
+        elif kind == "neg_inf_reject":
+            # The first 40% of every row are -inf (masked tokens, p_t = 0),
+            # the drafts sit there with p_d > 0: ratio 0, draft 1 rejected,
+            # and the residual is p_t over the finite tokens.
+            cut = (2 * V) // 5
+            lg[b, :, :cut] = float("-inf")
+            drafts[b] = rng.integers(0, cut, K)
+            for n in range(K):
+                pd[b, n, drafts[b, n]] = max(pd[b, n, drafts[b, n]], np.float32(1e-3))
         else:
             temp[b] = 0.0
     return kinds, lg, drafts, temp, top_p, pd, ua, us
@@ -118,7 +128,7 @@ def test_accept_edge_branches(V, dtype):
         j = ref["num_accepted"][b]
         if kind in ("pd0_accept", "u1_bonus", "u1_bonus_full"):
             assert j == Q - 1, (b, kind)
-        if kind in ("pd0_pt0_reject", "zero_residual", "u1_residual"):
+        if kind in ("pd0_pt0_reject", "zero_residual", "u1_residual", "neg_inf_reject"):
             assert j == 0, (b, kind)
         if kind == "u1_bonus_full":
             assert ref["next_token"][b] == V - 1
