@@ -71,13 +71,13 @@ def lm_head_kernel(M, hidden, vocab, dtype, cus):
     return "lm_head_stream"
 
 
-def profiled_traffic(kernel, workload):
-    """HBM bytes per launch from the committed PMC summary of this kernel and
-    workload, or None when there is none or the kernel's sources changed
+def profiled_fields(kernel, workload):
+    """The machine-readable lines of the committed PMC summary of this kernel
+    and workload, or {} when there is none or the kernel's sources changed
     since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     if kernel not in KERNEL_SOURCES or not os.path.exists(path):
-        return None
+        return {}
     fields = {}
     with open(path) as fh:
         for line in fh:
@@ -85,9 +85,27 @@ def profiled_traffic(kernel, workload):
             if sep:
                 fields[k] = v
     if fields.get("source_sha256") != kernel_source_hash(kernel):
-        return None
+        return {}
+    return fields
+
+
+def profiled_traffic(kernel, workload):
+    """HBM bytes per launch from the committed PMC summary (see
+    profiled_fields), or None."""
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(profiled_fields(kernel, workload)["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profiled_counters(kernel, workload):
+    """Shader-counter figures of the committed PMC summary: the fraction of
+    the kernel's cycles the matrix pipes were busy and the clock it sustained
+    (GRBM_GUI_ACTIVE per XCD over its duration), or None."""
+    f = profiled_fields(kernel, workload)
+    try:
+        return {"mfma_busy": float(f["mfma_busy"]), "clock_ghz": float(f["clock_ghz"]),
+                "source": f"profiles/{kernel}_{workload}.md"}
     except (KeyError, ValueError):
         return None
 
@@ -491,8 +509,10 @@ def main():
     else:
         dom_kernel = "attn_mla_bf16" if cfg.mla else ("attn_gqa_stream" if cfg.dtype == "bf16" else None)
     traffic = profiled_traffic(dom_kernel, workload) if dom_kernel else None
+    counters = profiled_counters(dom_kernel, workload) if dom_kernel else None
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],
-            "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": traffic}
+            "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": traffic,
+            "counters": counters}
     line = {
         "metric": "verified positions/sec", "value": pos_per_s, "unit": "positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,

@@ -23,12 +23,12 @@
 //                 reading 4 dims of key row key0 + s/4 gives lane t the 4-key
 //                 column of dim d0 + t); P split into bf16 hi + lo halves (two
 //                 MFMAs per fragment) to hold the fp32 output accuracy.
-// Latent tiles arrive by LDS DMA (global_load_lds_dwordx4), double-buffered,
-// so no registers stage them.  Register budget (one wave per SIMD, 512
+// Latent tiles arrive by LDS DMA (global_load_lds_dwordx4) into a three-stage
+// ring, so no registers stage them.  Register budget (one wave per SIMD, 512
 // registers): O^T blocks 0..14 (240) and S^T (16) in AGPRs, the last O^T block
 // kept in LDS between tiles so that S^T can use its registers; all of Q^T
 // (144) in VGPRs; the rest is fragment prefetch, P and addressing.  LDS:
-// 72 KiB latent + 16 KiB O^T.  The 16-byte chunks of each 1152-byte latent row
+// 108 KiB latent + 16 KiB O^T.  The 16-byte chunks of each 1152-byte latent row
 // are XOR-swizzled so that both LDS read patterns are free of bank conflicts.
 // With one chunk per request the kernel writes the normalised output itself;
 // otherwise it writes chunk partials for attn_combine.
@@ -48,7 +48,7 @@ constexpr int kTileKeys = 32;
 constexpr int kRowChunks = kDqk / 8;                       // 72 chunks of 16 bytes
 constexpr int kRowBytes = kDqk * 2;                        // 1152
 constexpr int kTileElems = kTileKeys * kDqk;               // 18432 bf16 = 36 KiB
-constexpr int kStages = 2;
+constexpr int kStages = 3;
 constexpr int kDmaPerWave = kTileKeys * kRowChunks / 256;  // 9 x 1 KiB per wave
 constexpr float kRefSlack = 64.f;  // log2 units a later tile may exceed the reference max by
 constexpr int kRowsPerBlock = 128;
@@ -63,7 +63,7 @@ constexpr int kRowsPerBlock = 128;
 // r and r+2 to differ in bit 2 of the XOR, which bit 1 of the row gives.
 __device__ __forceinline__ int mla_swz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 constexpr int kQSteps = kDqk / 16;     // 36 MFMA k-steps over the latent
-static_assert(4 * (kDmaPerWave - 1) < kQSteps, "a tile's DMAs are issued within the S^T k-steps");
+static_assert(2 * (kDmaPerWave - 1) < 32, "a tile's DMAs are issued within the PV steps");
 
 __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ lat,
@@ -154,27 +154,37 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) *(f32x4*)(o15_lds + (qd * 64 + lane) * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two stages: tile t+1 loads while tile t is computed.  At the top of
-    // iteration t, tile t (issued one iteration earlier) has landed and every
-    // wave has left iteration t-1, so stage (t+1)%2 is free to refill.  The
-    // refill's nine DMAs per wave go out one every four S^T k-steps rather
-    // than as one burst, which would hold up the wave's MFMA issue while the
-    // vector-memory queue drains.
+    // Three stages: tiles t+1 and t+2 load while tile t is computed.  At the
+    // top of iteration t, tile t (issued two iterations earlier) has landed
+    // once at most the nine DMAs of tile t+1 are in flight, and every wave
+    // has left iteration t-1, so stage (t+2)%3 is free to refill.  The
+    // refill's nine DMAs per wave go out during PV, one every two V^T
+    // blocks: a DMA instruction holds up the wave's issue for tens of cycles,
+    // which the two MFMAs queued per PV block cover and a single S^T MFMA
+    // does not (section timing: S^T 2330 -> 1700 cycles per tile, PV
+    // 2280 -> 2960, whole tile -4%).
     {
         const uint16_t* base0 = tile_src(0);
         const uint32_t dst0 = tile_dst(0);
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) tile_dma(base0, dst0, j);
+        if (ntiles > 1) {
+            const uint16_t* base1 = tile_src(1);
+            const uint32_t dst1 = tile_dst(1);
+#pragma unroll
+            for (int j = 0; j < kDmaPerWave; ++j) tile_dma(base1, dst1, j);
+        }
     }
     for (int t = 0; t < ntiles; ++t) {
-        wait_vmcnt<0>();
+        if (t + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
+        else wait_vmcnt<0>();
         // This wave's reads of tile t-1 must have returned before another
         // wave refills that stage after the barrier.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         barrier_only();
-        const bool more = t + 1 < ntiles;
-        const uint16_t* nbase = more ? tile_src(t + 1) : lat;
-        const uint32_t ndst = tile_dst(t + 1);
+        const bool more = t + 2 < ntiles;
+        const uint16_t* nbase = more ? tile_src(t + 2) : lat;
+        const uint32_t ndst = tile_dst(t + 2);
         const char* tile = (const char*)&s_lat[t % kStages][0];
         const int ks = start + kTileKeys * t;
         if (t == ntiles - 1 && end - ks < kTileKeys) {
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
         f32x16 sa;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sa[r] = 0.f;
-        constexpr int PF = 4;  // read-ahead distance in k-steps
+        constexpr int PF = 8;  // read-ahead distance in k-steps
         u32x4 kf[PF];
 #pragma unroll
         for (int s = 0; s < PF; ++s) kf[s] = *(const u32x4*)(tile + koff[s & 3] + 128 * (s >> 2));
@@ -202,7 +212,6 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
             if (s + PF < kQSteps)
                 kf[s % PF] = *(const u32x4*)(tile + koff[(s + PF) & 3] + 128 * ((s + PF) >> 2));
             sa = mfma_32x32x16(cur, qf[s], sa);
-            if (s % 4 == 0 && s / 4 < kDmaPerWave && more) tile_dma(nbase, ndst, s / 4);
             // Bounds how far the scheduler hoists reads.
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -285,6 +294,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla_bf16(
                 o15 = mfma_32x32x16(cur, pb[tt], o15);
                 o15 = mfma_32x32x16(cur, pbl[tt], o15);
             }
+            if ((idx & 1) == 0 && idx / 2 < kDmaPerWave && more) tile_dma(nbase, ndst, idx / 2);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
