@@ -130,8 +130,9 @@ def parse():
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
     ap.add_argument("--flush", action="store_true",
-                    help="overwrite a 1 GiB scratch buffer before every timed step, so that "
-                         "neither the L2 caches nor the 256 MB MALL hold the step's inputs; "
+                    help="read a 1 GiB scratch buffer before every timed step, so that "
+                         "neither the L2 caches nor the 256 MB MALL hold the step's inputs "
+                         "(a read leaves them clean, with no write-back for the step to pay); "
                          "each step is then timed alone with HIP events")
     return ap.parse_args()
 
@@ -418,12 +419,12 @@ def main():
     calls = [step.attention, step.lm_head, step.accept, step.rollback]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     acc_total = 0
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev) if args.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         if scratch is not None:
-            scratch.fill_(k & 0xFF)   # evicts the step's inputs from L2 and MALL
+            scratch.max()             # reads 1 GiB: evicts the step's inputs from L2 and MALL
         ev[k][0].record()
         for c, fn in enumerate(calls):
             fn()

@@ -202,7 +202,10 @@ def test_temperature_zero_is_greedy_even_with_probs(orc):
     assert (out["next_token"][::2] == tstar[::2, 1]).all()
 
 
-def _chi2_trials(orc, seed, T, top_p, N=200_000, V=16, K=3):
+def _chi2_trials(orc, seed, T, top_p, N=1_000_000, V=16, K=3, chunk=200_000):
+    """N independent verify steps of one request with fixed target logits and
+    draft distributions (drafts drawn from p_d), run through the oracle in
+    chunks.  Returns the concatenated outputs, the target rows and p_d."""
     rng = np.random.default_rng(seed)
     logits = rng.standard_normal((K + 1, V)) * 1.5
     pd_rows = rng.dirichlet(np.full(V, 0.7), size=K)
@@ -225,24 +228,32 @@ def _chi2_trials(orc, seed, T, top_p, N=200_000, V=16, K=3):
     pt = np.stack([target(logits[i]) for i in range(K + 1)])
     pdf = pd_rows.astype(np.float32)
     cdf = np.cumsum(pdf.astype(np.float64), -1)
-    ud = rng.random((N, K))
-    drafts = np.stack([np.minimum(np.searchsorted(cdf[n] / cdf[n, -1], ud[:, n], side="right"),
-                                  V - 1) for n in range(K)], 1).astype(np.int32)
-    L = np.broadcast_to(logits.astype(np.float64), (N, K + 1, V))
-    P = np.broadcast_to(pdf, (N, K, V))
-    ua = rng.random((N, K + 1)).astype(np.float32)
-    us = rng.random((N, K + 1)).astype(np.float32)
-    out = orc.accept(L, drafts, np.full(N, T, np.float32), np.full(N, top_p, np.float32), P,
-                     ua, us)
+    outs = []
+    for c0 in range(0, N, chunk):
+        n = min(chunk, N - c0)
+        ud = rng.random((n, K))
+        drafts = np.stack([np.minimum(np.searchsorted(cdf[k] / cdf[k, -1], ud[:, k],
+                                                      side="right"), V - 1)
+                           for k in range(K)], 1).astype(np.int32)
+        L = np.broadcast_to(logits.astype(np.float64), (n, K + 1, V))
+        P = np.broadcast_to(pdf, (n, K, V))
+        ua = rng.random((n, K + 1)).astype(np.float32)
+        us = rng.random((n, K + 1)).astype(np.float32)
+        outs.append(orc.accept(L, drafts, np.full(n, T, np.float32),
+                               np.full(n, top_p, np.float32), P, ua, us))
+    out = {k: np.concatenate([o[k] for o in outs]) for k in ("out_tokens", "num_accepted")}
     return out, pt, pdf
 
 
-@pytest.mark.parametrize("seed,T,top_p", [(11, 1.0, 1.0), (12, 0.7, 0.9)])
+@pytest.mark.parametrize("seed,T,top_p", [(11, 1.0, 1.0), (12, 0.7, 0.9), (13, 1.0, 1.0),
+                                         (14, 0.7, 0.9), (15, 1.3, 0.8)])
 def test_rejection_sampling_is_lossless_chi2(orc, seed, T, top_p):
     """The first emitted token is distributed as the target row 0, and the
     token emitted after an accepted first draft as target row 1 (the rows do
-    not depend on the drafts here), whatever the draft distribution."""
-    N, V, K = 200_000, 16, 3
+    not depend on the drafts here), whatever the draft distribution.  Five
+    seeds of 10^6 verify steps each, V = 16 (15 degrees of freedom at most),
+    each required to pass at p > 1e-4."""
+    N, V, K = 1_000_000, 16, 3
     out, pt, pdf = _chi2_trials(orc, seed, T, top_p, N, V, K)
     first = out["out_tokens"][:, 0]
     obs = np.bincount(first, minlength=V)
