@@ -65,6 +65,7 @@ def _oracle(wl, sel=None, append=True):
     (4, 4, 32, 8, 128, [512, 4097, 777, 64]),  # serving head layout, ragged
     (1, 0, 4, 1, 64, [33]),                 # K = 0: plain single-token decode
     (3, 3, 8, 1, 64, [95, 1, 2000]),        # one kv head, 32 rows, tails of 1..31 keys
+    (2, 15, 8, 2, 64, [33, 1500]),          # 64 rows per kv head: the largest supported
 ])
 def test_attention_gqa_e4m3(B, K, Hq, Hkv, D, lens):
     wl = _case(B, K, Hq, Hkv, D, lens, seed=20 + B + K)

@@ -65,6 +65,7 @@ def _oracle_attention(wl, sel=None, append=True):
     (2, 7, 40, 8, 128, [3000, 1000]),       # long-context head layout, two row blocks
     (4, 4, 32, 8, 128, [512, 4097, 777, 64]),  # serving head layout, ragged
     (1, 0, 4, 1, 64, [33]),                 # K = 0: plain single-token decode
+    (2, 7, 16, 2, 128, [100, 2000]),        # 64 rows per kv head: the largest supported
 ])
 def test_attention_gqa_bf16(B, K, Hq, Hkv, D, lens):
     wl = _gqa_case(B, K, Hq, Hkv, D, lens, "bf16", seed=10 + B + K)

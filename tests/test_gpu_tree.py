@@ -71,6 +71,7 @@ def _oracle_attention(wl, par):
     ("e4m3", "bf16", 4, 7, 16, 4, 128, [3, 64, 999, 4100]),
     ("e4m3", "bf16", 3, 15, 8, 2, 128, [10, 127, 3000]),          # 16 nodes, 64 rows
     ("as_dtype", "f32", 2, 5, 4, 2, 64, [7, 130]),                # float32 path
+    ("as_dtype", "bf16", 2, 63, 2, 2, 64, [17, 500]),             # 64 nodes: the largest tree
 ])
 def test_tree_attention(kv, dtype, B, K, Hq, Hkv, D, lens):
     rng = np.random.default_rng(K * 10 + B)
@@ -126,7 +127,7 @@ def _run_accept(lg_t, drafts, temp, par, relaxed=None):
 
 
 @pytest.mark.parametrize("B,K,V,dtype", [(40, 7, 5000, "bf16"), (25, 15, 1031, "f32"),
-                                         (8, 4, 129280, "bf16")])
+                                         (8, 4, 129280, "bf16"), (6, 63, 3000, "bf16")])
 def test_tree_accept_greedy(B, K, V, dtype):
     rng = np.random.default_rng(B + K)
     Q = K + 1
