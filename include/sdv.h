@@ -326,10 +326,12 @@ int sd_accept(const sd_accept_desc* d, void* workspace, size_t ws_bytes, void* s
 /* Allocation-free sd_accept, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same descriptor, outputs and semantics as sd_accept; the row
- * statistics live in a fixed 4 MiB device array of the library instead of a
- * caller workspace (one copy per GPU, held until the process ends).  That
- * covers batches of up to about 65000 logits rows (B*(K+1)); a larger batch
- * gets SD_EWORKSPACE before anything is launched.  Every call on one GPU
+ * statistics and draw sums live in a fixed 4 MiB device array of the library
+ * instead of a caller workspace (one copy per GPU, held until the process
+ * ends).  That holds about 136 bytes per logits row (B*(K+1)) plus 32 bytes
+ * per 512 vocabulary ids of each request: about 30000 rows for a small
+ * vocabulary, 495 requests at K = 4 and V = 129280.  A batch beyond it gets
+ * SD_EWORKSPACE before anything is launched.  Every call on one GPU
  * uses that GPU's one array, so calls that overlap on one GPU (on different
  * streams, or from host threads without an order between them) race: the
  * caller serialises them.  The first call on a device looks the array's

@@ -22,8 +22,11 @@
 //   accept_topp_*    sampled rows with top_p < 1: the nucleus threshold
 //                    lambda (exact: all tokens tied with the last kept logit
 //                    are kept), the kept mass, p_t of the draft
-//   accept_decide    one block per request: the sequential accept decision,
-//                    then the fp64 inverse-CDF draw of the final token
+//   accept_plan      one wave per request: the sequential accept decision
+//   accept_draw_*    the fp64 inverse-CDF draw of a sampled final token: one
+//                    pass over the drawn row in (request, slice) blocks sums
+//                    each 512-id chunk, then one block per request scans the
+//                    chunk sums and walks the crossing chunk
 //   accept_pack      exclusive scan of emitted counts, packed tokens
 // Statistics and running sums that decide integers are fp64 and reduced in a
 // fixed order, so results do not depend on scheduling.
@@ -626,28 +629,63 @@ __global__ __launch_bounds__(256) void accept_topp_f32(
 enum { kModeInvalid = 0, kModeDone = 1, kModeResidual = 2, kModeTarget = 3, kModeTree = 4 };
 
 // ---------------------------------------------------------------------------
-// Per-request decision and final-token draw.  One block of 1024 threads (16
-// waves) per request.  Thread 0 takes the sequential accept decision from the
-// row statistics.  A sampled final token is an inverse-CDF draw in token-id
-// order: wave w owns a contiguous run of ids, read 512 at a time (8 per lane,
-// one 16-byte load of bf16 logits); each 512-id chunk's fp64 weight sum is
-// reduced in a fixed lane order and kept in LDS.  A fixed-order scan over
-// waves, then over the crossing wave's chunks, finds the chunk whose running
-// sum first exceeds u * total; a lane-order prefix scan inside that chunk
-// finds the lane, whose 8 ids are then walked in order.
+// Per-request decision and final-token draw, spread over the chip:
+//   accept_plan       one wave per request, a lane per draft: the sequential
+//                     accept decision from the row statistics (greedy,
+//                     relaxed, rejection or tree); every output but a sampled
+//                     final token; the plan of the draw
+//   accept_draw_w     (request, slice) blocks, sampled final tokens: one fp64
+//                     pass over the drawn row, per 512-id chunk the sums the
+//                     draw needs (below)
+//   accept_draw_pick  one block per sampled request: the chunks' weight sums,
+//                     a fixed-order scan of them to the chunk whose running
+//                     sum first exceeds u * total, then the token inside it
+// The draw is an inverse CDF in token-id order.  A chunk is 512 consecutive
+// ids, 8 per lane (one 16-byte load of bf16 logits); its sums are the lanes'
+// sums reduced by a fixed butterfly, so every kernel that recomputes a chunk
+// gets the same value.
+// A residual draw compares p_t = e/Z (e = exp((x - m)/T)) with p_d token by
+// token.  Rows without a nucleus carry a Z summed from float32 terms (within
+// about 1e-6 of the fp64 sum), and the pass that computes the terms e is the
+// one that would sum Z in fp64.  So the pass classifies each token with that
+// Z: where p_t exceeds p_d by more than 1e-5 of p_d (then it does under the
+// fp64 Z too) it adds e to a and p_d to b; it counts the tokens within that
+// margin.  With Z = sum of e in fp64 (summed in the pick), the chunk's
+// residual weight is a / Z - b; a chunk with a token inside the margin is
+// summed again token by token with the fp64 Z.
 // ---------------------------------------------------------------------------
-constexpr int kDecThreads = 1024;
-constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecChunk = 512;      // tokens per chunk: 8 per lane
-constexpr int kDecMaxChunks = 32;   // per wave: V <= 16 * 32 * 512 = 262144
+constexpr int kDrawChunk = 512;       // ids per chunk: 8 per lane
+constexpr int kDrawMaxChunks = 512;   // chunks of a row: 8 per lane of the pick scan
+constexpr double kDrawMargin = 1e-5;  // relative margin of the row-pass Z's classification
 
-// Draw weights of the 8 consecutive tokens v0 .. v0+7 (0 past the row end),
-// with 16-byte loads when the rows are aligned.
+// What the draw kernels need of a request, in one record.
+struct Plan {
+    int mode;     // kMode*
+    int j;        // accepted drafts
+    int row;      // row of the draw (residual or target modes)
+    int fp64_z;   // residual draw of a row without a nucleus: Z summed again in fp64
+    float m;      // the drawn row's maximum
+    float lambda; // its nucleus threshold (-inf: every token)
+    double zkeep; // its Z from the row statistics
+    double invT;  // 1 / temperature
+};
+
+// Per-chunk sums of the draw pass (see above); b, a and unc only for
+// residual draws.
+struct ChunkRec {
+    double a;  // sum of e over the tokens counted in the residual
+    double b;  // sum of p_d over them
+    double e;  // sum of e over the chunk
+    int unc;   // tokens too close to p_t = p_d for the row-pass Z
+    int pad;
+};
+
+// Logits (and, for residual draws, p_d) of the 8 consecutive tokens v0 ..
+// v0+7 (-inf and 0 past the row end), with 16-byte loads when the rows are
+// aligned.
 template <typename T>
-__device__ __forceinline__ void weights8(const T* lr, const float* pd, int v0, int V, bool vec_ok,
-                                         bool resid, float lambda, float m, double invT,
-                                         double invZ, const double* tab, double (&w)[8]) {
-    float x[8], q[8];
+__device__ __forceinline__ void load8(const T* lr, const float* pd, int v0, int V, bool vec_ok,
+                                      bool resid, float (&x)[8], float (&q)[8]) {
     if (vec_ok && v0 + 8 <= V) {
         if constexpr (sizeof(T) == 2) {
             const u32x4 lw = *(const u32x4*)(lr + v0);
@@ -677,6 +715,16 @@ __device__ __forceinline__ void weights8(const T* lr, const float* pd, int v0, i
             q[e] = (resid && v < V) ? pd[v] : 0.f;
         }
     }
+}
+
+// Draw weights of the 8 consecutive tokens v0 .. v0+7 (0 past the row end):
+// p = e * invZ, or the residual max(0, p - p_d).
+template <typename T>
+__device__ __forceinline__ void weights8(const T* lr, const float* pd, int v0, int V, bool vec_ok,
+                                         bool resid, float lambda, float m, double invT,
+                                         double invZ, const double* tab, double (&w)[8]) {
+    float x[8], q[8];
+    load8(lr, pd, v0, V, vec_ok, resid, x, q);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const double p = (x[e] >= lambda) ? tempered(x[e], m, invT, tab) * invZ : 0.0;
@@ -689,325 +737,517 @@ __device__ __forceinline__ void weights8(const T* lr, const float* pd, int v0, i
     }
 }
 
+// The drawn row of a sampled request, as every draw block sees it.
 template <typename T>
-__global__ __launch_bounds__(kDecThreads) void accept_decide(
-    const T* __restrict__ logits, const int32_t* __restrict__ drafts,
-    const float* __restrict__ temperature, const float* __restrict__ draft_probs,
-    const float* __restrict__ u_accept, const float* __restrict__ u_sample,
-    const int32_t* __restrict__ relaxed_topk, const float* __restrict__ top_p,
-    const RowStat* __restrict__ stats, int32_t* __restrict__ num_accepted,
-    int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ next_token, int32_t* err, int K, int V,
-    const int32_t* __restrict__ tree_parent, int32_t* __restrict__ accepted_nodes) {
-    __shared__ double s_exptab[64];
-    exp_table_init(s_exptab);
-    __syncthreads();
-    __shared__ int s_mode, s_j, s_row, s_f, s_chunk;
-    __shared__ double s_u, s_pre, s_total;
-    __shared__ double s_wsum[kDecWaves];
-    __shared__ double s_chunk_sum[kDecWaves * kDecMaxChunks];
-    __shared__ int s_cand[kDecWaves];
-    __shared__ int s_depth[64];  // tree node depths (trees have K + 1 <= 64 nodes)
-    const int Q = K + 1;
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) {
-        int flags = 0;
-        for (int r = 0; r < Q; ++r) flags |= stats[(size_t)b * Q + r].flags;
-        for (int n = 0; n < K; ++n)
-            if (drafts[(size_t)b * K + n] >= V) flags |= SD_DERR_TOKEN;
-        int mode = kModeInvalid, j = -1, row = 0, f = -1;
-        if (!flags && tree_parent) {
-            // A tree: strict greedy requests only, well-formed parents.
-            const int32_t* par = tree_parent + (size_t)b * Q;
-            s_depth[0] = 0;
-            bool bad = Q > 64 || !(temperature[b] == 0.f) ||
-                       (relaxed_topk != nullptr && relaxed_topk[b] != 0) || par[0] != -1;
-            for (int n = 1; n < Q && !bad; ++n) bad = par[n] < 0 || par[n] >= n;
-            if (bad) flags |= SD_DERR_TREE;
+struct DrawRow {
+    const T* lr;
+    const float* pd;  // the draft's probabilities (residual draws)
+    Plan pl;
+    bool vec_ok;
+    bool resid;       // residual max(0, p_t - p_d) rather than p_t
+
+    __device__ DrawRow(const T* logits, const float* draft_probs, const Plan& p, int b, int K,
+                       int V)
+        : pl(p) {
+        const int Q = K + 1;
+        lr = logits + ((size_t)b * Q + pl.row) * V;
+        resid = pl.mode == kModeResidual;
+        pd = (resid && draft_probs) ? draft_probs + ((size_t)b * K + pl.row) * V : nullptr;
+        vec_ok = (V % 8) == 0 && ((uintptr_t)lr & 15) == 0 &&
+                 (pd == nullptr || ((uintptr_t)pd & 15) == 0);
+    }
+    // Lane `lane`'s 8 weights of chunk c and their sum (in id order).
+    __device__ double lane_sum(int c, int lane, int V, bool res, double invZ, const double* tab,
+                               double (&w)[8]) const {
+        weights8(lr, pd, c * kDrawChunk + 8 * lane, V, vec_ok, res, pl.lambda, pl.m, pl.invT,
+                 invZ, tab, w);
+        double t = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += w[e];
+        return t;
+    }
+    // Lane sums over its 8 ids of chunk c (see ChunkRec).
+    __device__ void lane_rec(int c, int lane, int V, const double* tab, double& a, double& b,
+                             double& e, int& unc) const {
+        float x[8], q[8];
+        load8(lr, pd, c * kDrawChunk + 8 * lane, V, vec_ok, resid, x, q);
+        const double izc = 1.0 / pl.zkeep;
+        const double margin = pl.fp64_z ? kDrawMargin : 0.0;
+        a = b = e = 0.0;
+        unc = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const double ev = (x[k] >= pl.lambda) ? tempered(x[k], pl.m, pl.invT, tab) : 0.0;
+            e += ev;
+            if (resid) {
+                const double qd = (double)q[k];
+                const double t = ev * izc - qd, tol = margin * fabs(qd);
+                if (t > tol) {
+                    a += ev;
+                    b += qd;
+                } else if (margin > 0.0 && t >= -tol && qd != 0.0) {
+                    ++unc;
+                }
+            }
         }
-        if (flags) {
-            set_error(err, flags);
-        } else if (tree_parent) {
-            // Node n is accepted when its parent is (the root always is) and
-            // its draft is the parent row's argmax.  One pass in node order
-            // (parents first) gives every node's depth and acceptance; the
-            // deepest accepted node, the first one found on ties (smallest
-            // index), ends the kept path.  The path and its drafts are
-            // written here, walking back up through the parents.
-            const int32_t* par = tree_parent + (size_t)b * Q;
-            uint64_t acc = 1;  // bit n: node n accepted (Q <= 64)
-            int best = 0, best_depth = 0;
-            for (int n = 1; n < Q; ++n) {
-                const int p = par[n], d = drafts[(size_t)b * K + n - 1];
-                s_depth[n] = s_depth[p] + 1;
-                if (((acc >> p) & 1) && d >= 0 && d == stats[(size_t)b * Q + p].argmax) {
-                    acc |= 1ull << n;
-                    if (s_depth[n] > best_depth) {
-                        best = n;
-                        best_depth = s_depth[n];
-                    }
+    }
+    // The ChunkRec of every chunk in [c_lo, c_hi), two in flight; f(c, rec)
+    // gets each one (wave-uniform).
+    template <typename F>
+    __device__ void chunk_recs(int c_lo, int c_hi, int lane, int V, const double* tab,
+                               F&& f) const {
+        auto reduce = [&](double a, double b, double e, int unc) {
+            ChunkRec r;
+            r.e = wave_sum(e);
+            if (resid) {
+                r.a = wave_sum(a);
+                r.b = wave_sum(b);
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) unc += shfl_xor(unc, m);
+                r.unc = unc;
+            } else {
+                r.a = r.e;
+                r.b = 0.0;
+                r.unc = 0;
+            }
+            r.pad = 0;
+            return r;
+        };
+        int c = c_lo;
+        for (; c + 1 < c_hi; c += 2) {
+            double a0, b0, e0, a1, b1, e1;
+            int u0, u1;
+            lane_rec(c, lane, V, tab, a0, b0, e0, u0);
+            lane_rec(c + 1, lane, V, tab, a1, b1, e1, u1);
+            f(c, reduce(a0, b0, e0, u0));
+            f(c + 1, reduce(a1, b1, e1, u1));
+        }
+        if (c < c_hi) {
+            double a0, b0, e0;
+            int u0;
+            lane_rec(c, lane, V, tab, a0, b0, e0, u0);
+            f(c, reduce(a0, b0, e0, u0));
+        }
+    }
+};
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v |= shfl_xor(v, m);
+    return v;
+}
+
+// Lane n's value of v (every lane active).
+__device__ __forceinline__ int lane_value(int v, int n) { return __shfl(v, n, 64); }
+
+// The accept decision of request b, taken by one wave (every lane returns
+// the same plan; loads are spread over the lanes, one per draft).  When
+// `writer`, the wave also writes the request's outputs: all of them, except
+// a sampled final token (next_token -1 and out_tokens[j] -1 until the draw
+// fills them in).
+__device__ Plan wave_plan(const int32_t* __restrict__ drafts, const float* __restrict__ temperature,
+                          const float* __restrict__ draft_probs, const float* __restrict__ u_accept,
+                          const int32_t* __restrict__ relaxed_topk, const float* __restrict__ top_p,
+                          const RowStat* __restrict__ stats, int32_t* err, int b, int K, int V,
+                          const int32_t* __restrict__ tree_parent, bool writer,
+                          int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
+                          int32_t* __restrict__ next_token, int32_t* __restrict__ accepted_nodes,
+                          int lane) {
+    const int Q = K + 1;
+    int fl = 0;
+    for (int r = lane; r < Q; r += 64) fl |= stats[(size_t)b * Q + r].flags;
+    for (int n = lane; n < K; n += 64)
+        if (drafts[(size_t)b * K + n] >= V) fl |= SD_DERR_TOKEN;
+    const float Tb = temperature[b];
+    // Trees (K + 1 <= 64 nodes, one per lane): node `lane`'s parent, draft
+    // and row argmax.
+    int par_l = -1, draft_l = -1, amax_l = -1;
+    if (tree_parent && lane < Q) {
+        par_l = tree_parent[(size_t)b * Q + lane];
+        if (lane > 0) draft_l = drafts[(size_t)b * K + lane - 1];
+    }
+    fl = wave_or(fl);
+    if (!fl && tree_parent) {
+        // Strict greedy requests only, well-formed parents.
+        const bool bad_l = lane < Q && (lane == 0 ? par_l != -1 : (par_l < 0 || par_l >= lane));
+        if (Q > 64 || !(Tb == 0.f) || (relaxed_topk != nullptr && relaxed_topk[b] != 0) ||
+            __ballot(bad_l) != 0)
+            fl |= SD_DERR_TREE;
+    }
+    int mode = kModeInvalid, j = -1, row = 0, f = -1;
+    unsigned long long path = 0;  // tree: bit n set for the kept path's nodes
+    int depth_l = 0;              // tree: depth of node `lane`
+    if (fl) {
+        if (writer && lane == 0) set_error(err, fl);
+    } else if (tree_parent) {
+        // Node n is accepted when its parent is (the root always is) and its
+        // draft is the parent row's argmax.  One pass in node order (parents
+        // first, every lane the same) gives every node's depth and
+        // acceptance; the deepest accepted node, the first one found on ties
+        // (smallest index), ends the kept path.
+        if (lane < Q) amax_l = stats[(size_t)b * Q + lane].argmax;
+        unsigned long long acc = 1;  // bit n: node n accepted
+        int best = 0, best_depth = 0;
+        for (int n = 1; n < Q; ++n) {
+            const int p = lane_value(par_l, n), d = lane_value(draft_l, n);
+            const int dn = lane_value(depth_l, p) + 1;
+            if (lane == n) depth_l = dn;
+            if (((acc >> p) & 1) && d >= 0 && d == lane_value(amax_l, p)) {
+                acc |= 1ull << n;
+                if (dn > best_depth) {
+                    best = n;
+                    best_depth = dn;
                 }
             }
-            j = best_depth;
-            for (int c = best; c != 0; c = par[c]) {
-                if (accepted_nodes) accepted_nodes[(size_t)b * Q + s_depth[c]] = c;
-                out_tokens[(size_t)b * Q + s_depth[c] - 1] = drafts[(size_t)b * K + c - 1];
+        }
+        for (int c = best; c != 0; c = lane_value(par_l, c)) path |= 1ull << c;
+        j = best_depth;
+        f = lane_value(amax_l, best);
+        mode = kModeTree;
+    } else if (Tb == 0.f) {
+        // Strict: the draft must be the row's argmax.  Relaxed (top-N > 0):
+        // it must survive the row's top-N / delta filter.  j = the first
+        // draft that fails.
+        const bool relaxed = relaxed_topk != nullptr && relaxed_topk[b] > 0;
+        j = K;
+        for (int base = 0; base < K; base += 64) {
+            const int n = base + lane;
+            bool fail = false;
+            if (n < K) {
+                const int d = drafts[(size_t)b * K + n];
+                const RowStat& st = stats[(size_t)b * Q + n];
+                fail = d < 0 || !(relaxed ? st.relaxed_ok != 0 : d == st.argmax);
             }
-            f = stats[(size_t)b * Q + best].argmax;
-            mode = kModeTree;
-        } else if (temperature[b] == 0.f) {
-            // Strict: the draft must be the row's argmax.  Relaxed (top-N >
-            // 0): it must survive the row's top-N / delta filter.
-            const bool relaxed = relaxed_topk != nullptr && relaxed_topk[b] > 0;
-            j = 0;
-            while (j < K) {
-                const int d = drafts[(size_t)b * K + j];
-                const RowStat& st = stats[(size_t)b * Q + j];
-                if (d < 0 || !(relaxed ? st.relaxed_ok != 0 : d == st.argmax)) break;
-                ++j;
-            }
-            f = stats[(size_t)b * Q + j].argmax;
-            mode = kModeDone;
-        } else {
-            j = K;
-            mode = kModeTarget;
-            row = K;
-            for (int n = 1; n <= K; ++n) {
-                const int d = drafts[(size_t)b * K + n - 1];
-                if (d < 0) {
-                    j = n - 1;
-                    row = n - 1;
-                    mode = kModeTarget;
-                    break;
-                }
-                const double a = stats[(size_t)b * Q + n - 1].pt_d;
-                const double qd = draft_probs[((size_t)b * K + n - 1) * V + d];
-                const double ratio = qd > 0.0 ? a / qd : (a > 0.0 ? INFINITY : 0.0);
-                const double acc = ratio < 1.0 ? ratio : 1.0;
-                if ((double)u_accept[(size_t)b * Q + n - 1] < acc) continue;
-                j = n - 1;
-                row = n - 1;
-                mode = kModeResidual;
+            const unsigned long long m = __ballot(fail);
+            if (m) {
+                j = base + __ffsll((long long)m) - 1;
                 break;
             }
         }
-        s_mode = mode;
-        s_j = j;
-        s_row = row;
-        s_f = f;
-        s_u = (double)u_sample[(size_t)b * Q + row];
+        f = stats[(size_t)b * Q + j].argmax;
+        mode = kModeDone;
+    } else {
+        // Rejection sampling: draft n+1 is kept while u < min(1, p_t/p_d);
+        // the first rejection draws from the residual of its row, a full
+        // chain (or a missing draft) from p_t of the next row.
+        j = K;
+        row = K;
+        mode = kModeTarget;
+        for (int base = 0; base < K; base += 64) {
+            const int n = base + lane;
+            int kind = 0;  // 0 kept, 1 missing draft, 2 rejected
+            if (n < K) {
+                const int d = drafts[(size_t)b * K + n];
+                if (d < 0) {
+                    kind = 1;
+                } else {
+                    const double a = stats[(size_t)b * Q + n].pt_d;
+                    const double qd = draft_probs[((size_t)b * K + n) * V + d];
+                    const double ratio = qd > 0.0 ? a / qd : (a > 0.0 ? INFINITY : 0.0);
+                    const double accp = ratio < 1.0 ? ratio : 1.0;
+                    if (!((double)u_accept[(size_t)b * Q + n] < accp)) kind = 2;
+                }
+            }
+            const unsigned long long m = __ballot(kind != 0);
+            if (m) {
+                const int first = __ffsll((long long)m) - 1;
+                j = row = base + first;
+                mode = lane_value(kind, first) == 2 ? kModeResidual : kModeTarget;
+                break;
+            }
+        }
+    }
+    if (writer) {
+        if (lane == 0) {
+            num_accepted[b] = j;
+            next_token[b] = f;  // -1 for invalid requests and sampled tokens
+        }
+        for (int k = lane; k < Q; k += 64) {
+            int tok = -1;
+            if (mode != kModeInvalid && mode != kModeTree && k < j) tok = drafts[(size_t)b * K + k];
+            else if (mode != kModeInvalid && k == j) tok = f;
+            if (!(mode == kModeTree && k < j)) out_tokens[(size_t)b * Q + k] = tok;
+            if (accepted_nodes && !(mode == kModeTree && k >= 1 && k <= j))
+                accepted_nodes[(size_t)b * Q + k] =
+                    mode == kModeInvalid ? -1 : (k == 0 ? 0 : (k <= j ? k : -1));
+        }
+        if (mode == kModeTree && lane < Q && ((path >> lane) & 1)) {
+            // The kept path's nodes, each at its depth.
+            if (accepted_nodes) accepted_nodes[(size_t)b * Q + depth_l] = lane;
+            out_tokens[(size_t)b * Q + depth_l - 1] = draft_l;
+        }
+    }
+    Plan pl;
+    pl.mode = mode;
+    pl.j = j;
+    pl.row = row;
+    pl.fp64_z = 0;
+    pl.m = 0.f;
+    pl.lambda = -INFINITY;
+    pl.zkeep = 1.0;
+    pl.invT = 1.0;
+    if (mode == kModeResidual || mode == kModeTarget) {
+        const RowStat st = stats[(size_t)b * Q + row];
+        pl.m = st.m;
+        pl.lambda = st.lambda;
+        pl.zkeep = st.zkeep;
+        pl.invT = 1.0 / (double)Tb;
+        // The row pass summed Z of a row without a nucleus from float32
+        // terms.  A draw from p_t is indifferent to a common scale, but the
+        // residual compares p_t with p_d token by token, so its Z is summed
+        // again in fp64.  A nucleus row's kept mass is fp64 already.
+        pl.fp64_z = mode == kModeResidual && (top_p == nullptr || !(top_p[b] < 1.f));
+    }
+    return pl;
+}
+
+// One wave per request, four per block.
+__global__ __launch_bounds__(256) void accept_plan(
+    const int32_t* __restrict__ drafts, const float* __restrict__ temperature,
+    const float* __restrict__ draft_probs, const float* __restrict__ u_accept,
+    const float* __restrict__ top_p, const int32_t* __restrict__ relaxed_topk,
+    const RowStat* __restrict__ stats, Plan* __restrict__ plans,
+    int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ next_token, int32_t* err, int B, int K, int V,
+    const int32_t* __restrict__ tree_parent, int32_t* __restrict__ accepted_nodes) {
+    const int lane = threadIdx.x & 63, b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= B) return;
+    const Plan pl = wave_plan(drafts, temperature, draft_probs, u_accept, relaxed_topk, top_p,
+                              stats, err, b, K, V, tree_parent, true, num_accepted, out_tokens,
+                              next_token, accepted_nodes, lane);
+    if (lane == 0) plans[b] = pl;
+}
+
+// Grid: batch x ns blocks of 256 threads; slice s covers chunks
+// [4 cpw s, 4 cpw (s + 1)), cpw per wave.
+template <typename T>
+__global__ __launch_bounds__(256) void accept_draw_w(const T* __restrict__ logits,
+                                                     const float* __restrict__ draft_probs,
+                                                     const Plan* __restrict__ plans,
+                                                     ChunkRec* __restrict__ recs, int K, int V,
+                                                     int ns, int cpw) {
+    const int b = blockIdx.x / ns, s = blockIdx.x - b * ns;
+    const Plan pl = plans[b];
+    if (pl.mode != kModeResidual && pl.mode != kModeTarget) return;
+    const DrawRow<T> dr(logits, draft_probs, pl, b, K, V);
+    __shared__ double s_exptab[64];
+    exp_table_init(s_exptab);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nchunks = (V + kDrawChunk - 1) / kDrawChunk;
+    ChunkRec* rc = recs + (size_t)b * nchunks;
+    const int c_lo = min(nchunks, (4 * s + wave) * cpw), c_hi = min(nchunks, c_lo + cpw);
+    dr.chunk_recs(c_lo, c_hi, lane, V, s_exptab, [&](int c, const ChunkRec& r) {
+        if (lane == 0) rc[c] = r;
+    });
+}
+
+// Wave 0 of the pick: lane l owns chunks [l cpl, (l+1) cpl); their sums are
+// added in chunk order per lane, then scanned across lanes in lane order.
+// Returns the row total; *pre = the lane's exclusive prefix, *own its sum.
+__device__ __forceinline__ double scan_chunks(const double* cs, int nchunks, int cpl, int lane,
+                                              double* pre, double* own) {
+    double t = 0.0;
+    const int c_lo = lane * cpl, c_hi = min(nchunks, c_lo + cpl);
+    for (int c = c_lo; c < c_hi; ++c) t += cs[c];
+    double incl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    *pre = incl - t;
+    *own = t;
+    return __shfl(incl, 63, 64);
+}
+
+// One block per request.
+template <typename T>
+__global__ __launch_bounds__(256) void accept_draw_pick(
+    const T* __restrict__ logits, const float* __restrict__ draft_probs,
+    const float* __restrict__ u_sample, const Plan* __restrict__ plans,
+    const ChunkRec* __restrict__ recs, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ next_token, int K, int V) {
+    const int b = blockIdx.x;
+    const Plan pl = plans[b];
+    if (pl.mode != kModeResidual && pl.mode != kModeTarget) return;
+    const DrawRow<T> dr(logits, draft_probs, pl, b, K, V);
+    __shared__ double s_exptab[64];
+    __shared__ double s_cs[kDrawMaxChunks], s_e[kDrawMaxChunks];
+    __shared__ int s_unc[kDrawMaxChunks];
+    __shared__ double s_total, s_pre, s_invz;
+    __shared__ int s_chunk, s_f;
+    __shared__ int s_cand[4];
+    exp_table_init(s_exptab);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Q = K + 1;
+    const int nchunks = (V + kDrawChunk - 1) / kDrawChunk;
+    const int cpl = (nchunks + 63) / 64;
+    const ChunkRec* rc = recs + (size_t)b * nchunks;
+    for (int c = tid; c < nchunks; c += 256) {
+        const ChunkRec r = rc[c];
+        s_e[c] = r.e;
+        s_cs[c] = r.a;  // (the residual's weight sum is formed below)
+        s_unc[c] = r.unc;
     }
     __syncthreads();
-    const int mode = s_mode;
-    if (mode == kModeResidual || mode == kModeTarget) {
-        const int row = s_row;
-        const RowStat st = stats[(size_t)b * Q + row];
-        const T* lr = logits + ((size_t)b * Q + row) * V;
-        const float* pd = draft_probs ? draft_probs + ((size_t)b * K + row) * V : nullptr;
-        const double invT = 1.0 / (double)temperature[b];
-        double invZ = 1.0 / st.zkeep;
-        const int nchunks = (V + kDecChunk - 1) / kDecChunk;
-        const int cpw = (nchunks + kDecWaves - 1) / kDecWaves;  // chunks per wave
-        const int c_begin = wave * cpw, c_end = min(nchunks, c_begin + cpw);
-        const bool vec_ok = (V % 8) == 0 && ((uintptr_t)lr & 15) == 0 &&
-                            (pd == nullptr || ((uintptr_t)pd & 15) == 0);
-        bool resid = mode == kModeResidual;
-        auto lane_sum = [&](int c, double (&w)[8]) {
-            weights8(lr, pd, c * kDecChunk + 8 * lane, V, vec_ok, resid, st.lambda, st.m, invT,
-                     invZ, s_exptab, w);
-            double t = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t += w[e];
-            return t;
-        };
-        if (resid && (top_p == nullptr || !(top_p[b] < 1.f))) {
-            // The row pass summed Z of a row without a nucleus from float32
-            // terms.  A draw from p_t is indifferent to a common scale, but
-            // the residual max(0, p_t - p_d) compares p_t with p_d token by
-            // token, so its Z is summed again here from fp64 terms, in the
-            // draw's fixed chunk order.
-            resid = false;
-            invZ = 1.0;
-            double zs = 0.0;
-            for (int c = c_begin; c < c_end; ++c) {
-                double w[8];
-                zs += wave_sum(lane_sum(c, w));
+    bool resid = dr.resid;
+    double invZ = 1.0;  // p_t unnormalised (the draw is scale-free), unless residual
+    if (resid) {
+        if (wave == 0) {
+            double z = 1.0 / pl.zkeep;
+            if (pl.fp64_z) {  // Z = the fp64 terms of every chunk, in a fixed order
+                double pre, own;
+                z = 1.0 / scan_chunks(s_e, nchunks, cpl, lane, &pre, &own);
             }
-            if (lane == 0) s_wsum[wave] = zs;
-            __syncthreads();
-            if (tid == 0) {
-                double tot = 0.0;
-                for (int w = 0; w < kDecWaves; ++w) tot += s_wsum[w];
-                s_total = tot;
-            }
-            __syncthreads();
-            invZ = 1.0 / s_total;
-            resid = true;
-            __syncthreads();
-        }
-        for (int pass = 0; pass < 2; ++pass) {
-            double wsum = 0.0;
-            int c = c_begin;
-            for (; c + 1 < c_end; c += 2) {  // two chunks in flight per wave
-                double w0[8], w1[8];
-                double t0 = lane_sum(c, w0), t1 = lane_sum(c + 1, w1);
-                t0 = wave_sum(t0);
-                t1 = wave_sum(t1);
-                if (lane == 0) {
-                    s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = t0;
-                    s_chunk_sum[wave * kDecMaxChunks + (c + 1 - c_begin)] = t1;
-                }
-                wsum += t0;
-                wsum += t1;
-            }
-            for (; c < c_end; ++c) {
-                double w0[8];
-                const double t0 = wave_sum(lane_sum(c, w0));
-                if (lane == 0) s_chunk_sum[wave * kDecMaxChunks + (c - c_begin)] = t0;
-                wsum += t0;
-            }
-            if (lane == 0) s_wsum[wave] = wsum;
-            __syncthreads();
-            if (tid == 0) {
-                double tot = 0.0;
-                for (int w = 0; w < kDecWaves; ++w) tot += s_wsum[w];
-                s_total = tot;
-            }
-            __syncthreads();
-            if (!(resid && s_total == 0.0)) break;
-            resid = false;  // residual empty: draw from p_t itself
-            __syncthreads();
-        }
-        if (tid == 0) {
-            // Locate the first chunk whose running sum exceeds u * total.
-            const double target = s_u * s_total;
-            double run = 0.0;
-            int fc = -1;
-            for (int w = 0; w < kDecWaves && fc < 0; ++w) {
-                if (run + s_wsum[w] > target) {
-                    // The crossing wave.  Its chunk sums are added one by
-                    // one here, in another order than its wave sum, so
-                    // rounding may leave every chunk short of the target:
-                    // then the wave's last chunk of positive weight is
-                    // taken (the in-chunk search below then ends on its
-                    // last positive token), not a token of a later wave.
-                    const int cb = w * cpw, ce = min(nchunks, cb + cpw);
-                    const double run0 = run;
-                    int lastpos = -1;
-                    double pre_last = run0;
-                    for (int c = cb; c < ce; ++c) {
-                        const double cs = s_chunk_sum[w * kDecMaxChunks + (c - cb)];
-                        if (run + cs > target) {
-                            fc = c;
-                            break;
-                        }
-                        if (cs > 0.0) {
-                            lastpos = c;
-                            pre_last = run;
-                        }
-                        run += cs;
-                    }
-                    if (fc < 0) {
-                        fc = lastpos;  // >= 0: the wave's weight is positive
-                        run = pre_last;
-                    }
-                } else {
-                    run += s_wsum[w];
-                }
-            }
-            s_chunk = fc;
-            s_pre = run;
+            if (lane == 0) s_invz = z;
         }
         __syncthreads();
-        if (s_chunk >= 0 && wave == 0) {
-            // Inside the chunk: lane-order inclusive scan of the lanes' sums,
-            // then the crossing lane walks its 8 tokens in order.  If rounding
-            // leaves the target beyond the chunk, take its last positive token.
-            const int c = s_chunk;
-            double w[8];
-            const double t = lane_sum(c, w);
-            double incl = t;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            const double target = s_u * s_total;
-            const unsigned long long mask = __ballot(s_pre + incl > target);
-            if (mask) {
-                const int hl = __ffsll((long long)mask) - 1;
-                if (lane == hl) {
-                    double run = s_pre + incl - t;
-                    int pick = -1, lastpos = -1;
-                    for (int e = 0; e < 8; ++e) {
-                        if (w[e] > 0.0) lastpos = e;
-                        run += w[e];
-                        if (run > target && pick < 0) pick = e;
-                    }
-                    if (pick < 0) pick = lastpos;
-                    s_f = c * kDecChunk + 8 * lane + pick;
-                }
-            } else {
-                int lp = -1;
-                for (int e = 0; e < 8; ++e)
-                    if (w[e] > 0.0) lp = e;
-                const unsigned long long pm = __ballot(lp >= 0);
-                const int top = pm ? 63 - __clzll((long long)pm) : -1;
-                if (lane == 0) s_f = -1;
-                if (top >= 0 && lane == top) s_f = c * kDecChunk + 8 * lane + lp;
-            }
-        }
+        invZ = s_invz;
+        for (int c = tid; c < nchunks; c += 256) s_cs[c] = fmax(s_cs[c] * invZ - rc[c].b, 0.0);
         __syncthreads();
-        if (s_chunk < 0 || s_f < 0) {
-            // Rounding left no bucket above the target: the largest id with
-            // positive weight.
-            int cand = -1;
-            for (int c = c_end - 1; c >= c_begin && cand < 0; --c) {
+        if (pl.fp64_z) {
+            // Chunks with a token inside the margin: summed again token by
+            // token with the fp64 Z.
+            for (int c = wave; c < nchunks; c += 4) {
+                if (s_unc[c] == 0) continue;
                 double w[8];
-                lane_sum(c, w);
-                int lp = -1;
-                for (int e = 0; e < 8; ++e)
-                    if (w[e] > 0.0) lp = e;
-                const unsigned long long pm = __ballot(lp >= 0);
-                if (pm) {
-                    const int top = 63 - __clzll((long long)pm);
-                    const int lpt = __shfl(lp, top, 64);
-                    cand = c * kDecChunk + 8 * top + lpt;
-                }
-            }
-            if (lane == 0) s_cand[wave] = cand;
-            __syncthreads();
-            if (tid == 0) {
-                int f = -1;
-                for (int w = 0; w < kDecWaves; ++w) f = max(f, s_cand[w]);
-                s_f = f;
+                const double t = wave_sum(dr.lane_sum(c, lane, V, true, invZ, s_exptab, w));
+                if (lane == 0) s_cs[c] = t;
             }
             __syncthreads();
         }
     }
+    const double u = (double)u_sample[(size_t)b * Q + pl.row];
+    if (wave == 0) {
+        double pre, own;
+        const double tot = scan_chunks(s_cs, nchunks, cpl, lane, &pre, &own);
+        if (lane == 0) s_total = tot;
+    }
+    __syncthreads();
+    if (resid && s_total == 0.0) {
+        // The residual is empty: the draw takes p_t itself (unnormalised).
+        for (int c = tid; c < nchunks; c += 256) s_cs[c] = s_e[c];
+        resid = false;
+        invZ = 1.0;
+        __syncthreads();
+    }
+    if (wave == 0) {
+        // The crossing lane: the first whose running sum exceeds u * total.
+        // It walks its chunks, added one by one (another order than its lane
+        // sum), so rounding may leave every chunk short of the target: then
+        // its last chunk of positive weight is taken (the search inside the
+        // chunk then ends on its last positive token).
+        double pre, own;
+        const double tot = scan_chunks(s_cs, nchunks, cpl, lane, &pre, &own);
+        const double target = u * tot;
+        const unsigned long long cross = __ballot(pre + own > target);
+        int fc = -1;
+        double run_at = 0.0;
+        if (cross) {
+            const int cl = __ffsll((long long)cross) - 1;
+            if (lane == cl) {
+                const int c_lo = lane * cpl, c_hi = min(nchunks, c_lo + cpl);
+                double run = pre, pre_last = pre;
+                int lastpos = -1;
+                for (int c = c_lo; c < c_hi; ++c) {
+                    const double v = s_cs[c];
+                    if (run + v > target) {
+                        fc = c;
+                        break;
+                    }
+                    if (v > 0.0) {
+                        lastpos = c;
+                        pre_last = run;
+                    }
+                    run += v;
+                }
+                if (fc < 0) {
+                    fc = lastpos;
+                    run = pre_last;
+                }
+                run_at = run;
+            }
+            fc = __shfl(fc, cl, 64);
+            run_at = __shfl(run_at, cl, 64);
+        }
+        if (lane == 0) {
+            s_chunk = fc;
+            s_pre = run_at;
+            s_total = tot;
+        }
+    }
+    __syncthreads();
+    if (s_chunk >= 0 && wave == 0) {
+        // Inside the chunk: lane-order inclusive scan of the lanes' sums,
+        // then the crossing lane walks its 8 tokens in order.  If rounding
+        // leaves the target beyond the chunk, take its last positive token.
+        const int c = s_chunk;
+        double w[8];
+        const double t = dr.lane_sum(c, lane, V, resid, invZ, s_exptab, w);
+        double incl = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const double target = u * s_total;
+        const unsigned long long mask = __ballot(s_pre + incl > target);
+        if (mask) {
+            const int hl = __ffsll((long long)mask) - 1;
+            if (lane == hl) {
+                double run = s_pre + incl - t;
+                int pick = -1, lastpos = -1;
+                for (int e = 0; e < 8; ++e) {
+                    if (w[e] > 0.0) lastpos = e;
+                    run += w[e];
+                    if (run > target && pick < 0) pick = e;
+                }
+                if (pick < 0) pick = lastpos;
+                s_f = c * kDrawChunk + 8 * lane + pick;
+            }
+        } else {
+            int lp = -1;
+            for (int e = 0; e < 8; ++e)
+                if (w[e] > 0.0) lp = e;
+            const unsigned long long pm = __ballot(lp >= 0);
+            const int top = pm ? 63 - __clzll((long long)pm) : -1;
+            if (lane == 0) s_f = -1;
+            if (top >= 0 && lane == top) s_f = c * kDrawChunk + 8 * lane + lp;
+        }
+    } else if (tid == 0) {
+        s_f = -1;
+    }
+    __syncthreads();
+    if (s_f < 0) {
+        // Rounding left no bucket above the target: the largest id with
+        // positive weight.
+        int cand = -1;
+        for (int c = nchunks - 1 - wave; c >= 0 && cand < 0; c -= 4) {
+            double w[8];
+            dr.lane_sum(c, lane, V, resid, invZ, s_exptab, w);
+            int lp = -1;
+            for (int e = 0; e < 8; ++e)
+                if (w[e] > 0.0) lp = e;
+            const unsigned long long pm = __ballot(lp >= 0);
+            if (pm) {
+                const int top = 63 - __clzll((long long)pm);
+                const int lpt = __shfl(lp, top, 64);
+                cand = c * kDrawChunk + 8 * top + lpt;
+            }
+        }
+        if (lane == 0) s_cand[wave] = cand;
+        __syncthreads();
+        if (tid == 0) {
+            int f = -1;
+            for (int w = 0; w < 4; ++w) f = max(f, s_cand[w]);
+            s_f = f;
+        }
+        __syncthreads();
+    }
     if (tid == 0) {
-        const int j = s_j;
-        const int f = mode == kModeInvalid ? -1 : s_f;
-        num_accepted[b] = j;
-        next_token[b] = f;
-        for (int k = 0; k < Q; ++k) {
-            if (mode == kModeTree && k < j) continue;  // the path's drafts, written above
-            int tok = -1;
-            if (mode != kModeInvalid) {
-                if (k < j) tok = drafts[(size_t)b * K + k];
-                else if (k == j) tok = f;
-            }
-            out_tokens[(size_t)b * Q + k] = tok;
-        }
-        if (accepted_nodes) {
-            if (mode == kModeInvalid) accepted_nodes[(size_t)b * Q] = -1;
-            else accepted_nodes[(size_t)b * Q] = 0;
-            for (int k = 1; k < Q; ++k) {
-                if (mode == kModeTree && k <= j) continue;  // written above
-                accepted_nodes[(size_t)b * Q + k] = (mode != kModeInvalid && k <= j) ? k : -1;
-            }
-        }
+        next_token[b] = s_f;
+        out_tokens[(size_t)b * Q + pl.j] = s_f;
     }
 }
 
@@ -1069,13 +1309,39 @@ void row_split(int rows, int V, int* splits, int* span) {
     *splits = (V + sn - 1) / sn;
 }
 
-size_t accept_ws_bytes(const sd_accept_desc* d) {
+// Chunks per wave of the draw pass (two loads in flight per lane; more per
+// wave measured slower).
+int draw_cpw(int, int) { return 2; }
+
+// Slices (blocks) per row of the draw passes.
+int draw_slices(int B, int V) {
+    const int nchunks = (V + kDrawChunk - 1) / kDrawChunk;
+    const int per_block = 4 * draw_cpw(B, V);
+    return (nchunks + per_block - 1) / per_block;
+}
+
+// Workspace: row statistics, slice records, then the draw's plans, Z slice
+// sums and chunk sums, each 256-byte aligned.
+struct AcceptWs {
+    size_t stats, parts, plans, recs, total;
+};
+
+AcceptWs accept_ws_layout(const sd_accept_desc* d) {
     const int rows = d->batch * (d->K + 1);
     int splits, span;
     row_split(rows, d->vocab, &splits, &span);
-    return align_up(sizeof(RowStat) * (size_t)rows, 256) +
-           align_up(sizeof(RowPart) * (size_t)rows * splits, 256);
+    const size_t B = (size_t)d->batch;
+    const size_t nchunks = (size_t)(d->vocab + kDrawChunk - 1) / kDrawChunk;
+    AcceptWs w;
+    w.stats = 0;
+    w.parts = w.stats + align_up(sizeof(RowStat) * (size_t)rows, 256);
+    w.plans = w.parts + align_up(sizeof(RowPart) * (size_t)rows * splits, 256);
+    w.recs = w.plans + align_up(sizeof(Plan) * B, 256);
+    w.total = w.recs + align_up(sizeof(ChunkRec) * B * nchunks, 256);
+    return w;
 }
+
+size_t accept_ws_bytes(const sd_accept_desc* d) { return accept_ws_layout(d).total; }
 
 int check_accept(const sd_accept_desc* d) {
     if (!d) return fail(SD_EINVAL, "sd_accept_desc is NULL");
@@ -1085,9 +1351,10 @@ int check_accept(const sd_accept_desc* d) {
         return fail(SD_EINVAL, "sd_accept: unknown logits dtype %d", d->logits_dtype);
     if ((long)d->batch * (d->K + 1) > 0x7fffffffL)
         return fail(SD_EUNSUPPORTED, "sd_accept: too many rows");
-    if ((long)d->vocab > (long)kDecWaves * kDecMaxChunks * kDecChunk)
-        return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d",
-                    kDecWaves * kDecMaxChunks * kDecChunk);
+    if ((long)d->vocab > (long)kDrawMaxChunks * kDrawChunk)
+        return fail(SD_EUNSUPPORTED, "sd_accept: vocab above %d", kDrawMaxChunks * kDrawChunk);
+    if ((long)d->batch * draw_slices(d->batch, d->vocab) > 0x7fffffffL)
+        return fail(SD_EUNSUPPORTED, "sd_accept: too many draw blocks");
     if (d->tree_parent && d->K + 1 > 64)
         return fail(SD_EUNSUPPORTED, "sd_accept: a draft tree needs K+1 <= 64, got %d", d->K + 1);
     return SD_OK;
@@ -1118,6 +1385,30 @@ int check_accept_pointers(const sd_accept_desc* d, const char* what) {
     return SD_OK;
 }
 
+// The decision and the draw.  A sampled request with drafts needs
+// draft_probs (otherwise the row merge marks it invalid), so without them
+// and K > 0 no request draws and the draw kernels are skipped.
+template <typename T>
+int draw_launch(const T* lg, const sd_accept_desc* d, const RowStat* stats, Plan* plans,
+                ChunkRec* recs, hipStream_t s) {
+    int rc;
+    const int B = d->batch, K = d->K, V = d->vocab;
+    accept_plan<<<(B + 3) / 4, 256, 0, s>>>(d->draft_tokens, d->temperature, d->draft_probs,
+                                            d->u_accept, d->top_p, d->relaxed_topk, stats, plans,
+                                            d->num_accepted, d->out_tokens, d->next_token,
+                                            d->dev_error, B, K, V, d->tree_parent,
+                                            d->accepted_nodes);
+    if ((rc = check_launch("accept_plan")) != SD_OK) return rc;
+    if (d->draft_probs == nullptr && K > 0) return SD_OK;
+    const int ns = draw_slices(B, V), cpw = draw_cpw(B, V);
+    const unsigned grid = (unsigned)((long)B * ns);
+    accept_draw_w<T><<<grid, 256, 0, s>>>(lg, d->draft_probs, plans, recs, K, V, ns, cpw);
+    if ((rc = check_launch("accept_draw_w")) != SD_OK) return rc;
+    accept_draw_pick<T><<<B, 256, 0, s>>>(lg, d->draft_probs, d->u_sample, plans, recs,
+                                          d->out_tokens, d->next_token, K, V);
+    return check_launch("accept_draw_pick");
+}
+
 // The kernels of one acceptance call, with the row statistics and slice
 // records in `workspace` (accept_ws_bytes(d) bytes, 256-byte aligned; no
 // initialisation needed: every record is written before it is read).
@@ -1127,8 +1418,12 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
     const int rows = B * Q;
     int splits, span;
     row_split(rows, V, &splits, &span);
-    RowStat* stats = (RowStat*)workspace;
-    RowPart* parts = (RowPart*)((char*)workspace + align_up(sizeof(RowStat) * (size_t)rows, 256));
+    const AcceptWs ws = accept_ws_layout(d);
+    char* w0 = (char*)workspace;
+    RowStat* stats = (RowStat*)(w0 + ws.stats);
+    RowPart* parts = (RowPart*)(w0 + ws.parts);
+    Plan* plans = (Plan*)(w0 + ws.plans);
+    ChunkRec* recs = (ChunkRec*)(w0 + ws.recs);
     const int es = d->logits_dtype == SD_BF16 ? 2 : 4;
     const int vec_ok = aligned16(d->logits) && ((size_t)V * es) % 16 == 0;
     const int has_probs = d->draft_probs != nullptr;
@@ -1152,11 +1447,7 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
                 lg, d->draft_tokens, d->temperature, d->top_p, stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_bf16")) != SD_OK) return rc;
         }
-        accept_decide<uint16_t><<<B, kDecThreads, 0, s>>>(
-            lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
-            d->relaxed_topk, d->top_p, stats, d->num_accepted, d->out_tokens, d->next_token,
-            d->dev_error,
-            K, V, d->tree_parent, d->accepted_nodes);
+        if ((rc = draw_launch(lg, d, stats, plans, recs, s)) != SD_OK) return rc;
     } else {
         const float* lg = (const float*)d->logits;
         if (d->relaxed_topk)
@@ -1177,13 +1468,8 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
                                                  stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_f32")) != SD_OK) return rc;
         }
-        accept_decide<float><<<B, kDecThreads, 0, s>>>(
-            lg, d->draft_tokens, d->temperature, d->draft_probs, d->u_accept, d->u_sample,
-            d->relaxed_topk, d->top_p, stats, d->num_accepted, d->out_tokens, d->next_token,
-            d->dev_error,
-            K, V, d->tree_parent, d->accepted_nodes);
+        if ((rc = draw_launch(lg, d, stats, plans, recs, s)) != SD_OK) return rc;
     }
-    if ((rc = check_launch("accept_decide")) != SD_OK) return rc;
     accept_pack<<<1, 1024, 0, s>>>(d->num_accepted, d->out_tokens, d->out_offsets,
                                    d->packed_tokens, B, Q);
     return check_launch("accept_pack");
