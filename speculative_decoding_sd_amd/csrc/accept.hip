@@ -16,9 +16,8 @@
 //                    blocks): the slice's argmax (smallest id on ties),
 //                    finiteness and, for sampled rows, its max and fp64
 //                    mass sum exp((l - max)/T)
-//   accept_rowmerge  one thread per row: merges the slices in order into the
-//                    row max m, argmax, Z = sum exp((l-m)/T) and p_t of the
-//                    row's draft
+//   accept_rowmerge  one wave per row: merges the slices into the row max m,
+//                    argmax, Z = sum exp((l-m)/T) and p_t of the row's draft
 //   accept_topp_*    sampled rows with top_p < 1: the nucleus threshold
 //                    lambda (exact: all tokens tied with the last kept logit
 //                    are kept), the kept mass, p_t of the draft
@@ -390,12 +389,13 @@ __global__ __launch_bounds__(256) void accept_rowpart(const T* __restrict__ logi
     }
 }
 
-// One thread per row: merges the row's slices in order (max, smallest id on
-// ties, Z = sum_s z_s exp((best_s - m)/T)), checks the request's parameters
-// and, for sampled rows that judge a draft, p_t of that draft.  Relaxed rows
-// ([TRT-MTP] "寬松接受"): the draft survives when fewer than N tokens rank
-// before it and its probability exp(l_d - m)/Z (T = 1) is not below the
-// top-1 probability 1/Z minus delta, i.e. exp(l_d - m) >= 1 - delta Z.
+// One wave per row, a lane per slice (at most 64): merges the row's slices
+// (max, smallest id on ties, Z = sum_s z_s exp((best_s - m)/T) reduced by a
+// fixed butterfly), checks the request's parameters and, for sampled rows
+// that judge a draft, p_t of that draft.  Relaxed rows ([TRT-MTP] "寬松接受"):
+// the draft survives when fewer than N tokens rank before it and its
+// probability exp(l_d - m)/Z (T = 1) is not below the top-1 probability 1/Z
+// minus delta, i.e. exp(l_d - m) >= 1 - delta Z.
 template <typename T>
 __global__ __launch_bounds__(256) void accept_rowmerge(
     const T* __restrict__ logits, const int32_t* __restrict__ drafts,
@@ -406,7 +406,8 @@ __global__ __launch_bounds__(256) void accept_rowmerge(
     __shared__ double s_exptab[64];
     exp_table_init(s_exptab);
     __syncthreads();
-    const int row = blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int Q = K + 1, b = row / Q, i = row - b * Q;
     const float Tb = temperature[b];
@@ -415,71 +416,79 @@ __global__ __launch_bounds__(256) void accept_rowmerge(
     const int rN = relaxed_topk ? relaxed_topk[b] : 0;
     const bool relaxed = Tb == 0.f && rN > 0;
     const double delta = (relaxed && relaxed_delta) ? (double)relaxed_delta[b] : 0.0;
+    const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
+    const T* lr = logits + (size_t)row * V;
+    const float xd = (d >= 0 && d < V) ? Logit<T>::at(lr, d) : 0.f;
     int flags = 0;
     if (isnan(Tb) || Tb < 0.f) flags |= SD_DERR_PARAM;
     if (stoch && (isnan(tp) || tp <= 0.f || (!has_probs && K > 0))) flags |= SD_DERR_PARAM;
     if (rN < 0) flags |= SD_DERR_PARAM;
     if (relaxed && (!relaxed_delta || !(delta >= 0.0) || isinf(delta))) flags |= SD_DERR_PARAM;
-    const RowPart* pr = parts + (size_t)row * splits;
-    float best = -INFINITY;
-    int bidx = 0x7fffffff, bits = 0;
-    for (int s = 0; s < splits; ++s) {
-        const RowPart p = pr[s];
-        bits |= p.bits;
-        if (p.best > best) {
-            best = p.best;
-            bidx = p.bidx;
+    RowPart p;
+    p.best = -INFINITY;
+    p.bidx = 0x7fffffff;
+    p.bits = 0;
+    p.beat = 0;
+    p.z = 0.0;
+    if (lane < splits) p = parts[(size_t)row * splits + lane];
+    float best = p.best;
+    int bidx = p.bidx, bits = p.bits, beat = p.beat;
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) {
+        const float ob = shfl_xor(best, msk);
+        const int oi = shfl_xor(bidx, msk);
+        if (ob > best || (ob == best && oi < bidx)) {
+            best = ob;
+            bidx = oi;
         }
+        bits |= shfl_xor(bits, msk);
+        beat += shfl_xor(beat, msk);
     }
     if ((bits & 1) || !(bits & 2)) flags |= SD_DERR_NONFINITE;
     double z = 0.0, pt_d = 0.0;
+    int relaxed_ok = 0;
     if (stoch && !flags) {
         const double invT = 1.0 / (double)Tb;
-        for (int s = 0; s < splits; ++s) {
-            const RowPart p = pr[s];
-            z += p.z * exp_neg(((double)p.best - (double)best) * invT, s_exptab);
-        }
-        const int d = (i < K) ? drafts[(size_t)b * K + i] : -1;
-        const T* lr = logits + (size_t)row * V;
-        if (d >= 0 && d < V) pt_d = tempered(Logit<T>::at(lr, d), best, invT, s_exptab) / z;
+        const double zt = lane < splits
+            ? p.z * exp_neg(((double)p.best - (double)best) * invT, s_exptab) : 0.0;
+        z = wave_sum(zt);
+        if (d >= 0 && d < V) pt_d = tempered(xd, best, invT, s_exptab) / z;
+    } else if (relaxed && !flags && i < K && d >= 0 && d < V) {
+        const double zt = lane < splits
+            ? p.z * exp_neg((double)p.best - (double)best, s_exptab) : 0.0;
+        z = wave_sum(zt);
+        const double e_d = exp_neg((double)xd - (double)best, s_exptab);
+        relaxed_ok = beat < rN && e_d >= 1.0 - delta * z;
     }
-    int relaxed_ok = 0;
-    if (relaxed && !flags && i < K) {
-        const int d = drafts[(size_t)b * K + i];
-        if (d >= 0 && d < V) {
-            int rank = 0;
-            for (int s = 0; s < splits; ++s) {
-                const RowPart p = pr[s];
-                rank += p.beat;
-                z += p.z * exp_neg((double)p.best - (double)best, s_exptab);
-            }
-            const T* lr = logits + (size_t)row * V;
-            const double e_d = exp_neg((double)Logit<T>::at(lr, d) - (double)best, s_exptab);
-            relaxed_ok = rank < rN && e_d >= 1.0 - delta * z;
-        }
+    if (lane == 0) {
+        RowStat st;
+        st.m = best;
+        st.lambda = -INFINITY;
+        st.argmax = bidx;
+        st.flags = flags;
+        st.zkeep = z;
+        st.pt_d = pt_d;
+        st.relaxed_ok = relaxed_ok;
+        st.pad = 0;
+        stats[row] = st;
     }
-    RowStat st;
-    st.m = best;
-    st.lambda = -INFINITY;
-    st.argmax = bidx;
-    st.flags = flags;
-    st.zkeep = z;
-    st.pt_d = pt_d;
-    st.relaxed_ok = relaxed_ok;
-    st.pad = 0;
-    stats[row] = st;
 }
 
 // ---------------------------------------------------------------------------
-// Nucleus threshold for bf16 rows.  Walks the 65536 orderable bf16 keys down
-// from the row maximum in windows of 8192: an exact u32 count per key (LDS
-// atomics), the mass of each level = count * exp((value - m) / T), a fixed
-// order prefix over levels until the running mass reaches top_p * Z.  The
-// level where it does is lambda; every token with logit >= lambda is kept.
+// Nucleus threshold for bf16 rows.  One block of 1024 threads per row walks
+// the 65536 orderable bf16 keys down from the row maximum in windows of 8192:
+// an exact u32 count per key (LDS atomics, four 16-byte loads in flight per
+// thread), the mass of each level = count * exp((value - m) / T), a
+// fixed-order prefix over levels (per thread over its 8 levels, then a lane
+// scan per wave, then the 16 waves in order) until the running mass reaches
+// top_p * Z.  The level where it does is lambda; every token with logit >=
+// lambda is kept.
 // ---------------------------------------------------------------------------
 constexpr int kWin = 8192;
+constexpr int kToppThreads = 1024;
+constexpr int kToppLevels = kWin / kToppThreads;  // levels per thread
 
-__global__ __launch_bounds__(256) void accept_topp_bf16(
+__global__ __launch_bounds__(kToppThreads) void accept_topp_bf16(
     const uint16_t* __restrict__ logits, const int32_t* __restrict__ drafts,
     const float* __restrict__ temperature, const float* __restrict__ top_p,
     RowStat* __restrict__ stats, int K, int V, int vec_ok) {
@@ -487,9 +496,9 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
     exp_table_init(s_exptab);
     __syncthreads();
     extern __shared__ __attribute__((aligned(16))) uint32_t s_hist[];  // kWin
-    __shared__ double s_part[257];
+    __shared__ double s_wtot[kToppThreads / 64];
     __shared__ int s_found, s_lkey;
-    __shared__ double s_zkeep;
+    __shared__ double s_zkeep, s_cum;
     const int Q = K + 1;
     const int row = blockIdx.x, b = row / Q, i = row - b * Q;
     const float Tb = temperature[b];
@@ -500,51 +509,78 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
     const double target = (double)tp * st.zkeep;
     const float m = st.m;
     const double invT = 1.0 / (double)Tb;
-    const int tid = threadIdx.x;
-    double cum = 0.0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double cum = 0.0;  // mass above the current window
     int lkey = -1;
     double zkeep = st.zkeep;
     for (int top = (int)bf16_key(__float_as_uint(m) >> 16);; top -= kWin) {
         const int bottom = top - (kWin - 1) > 0 ? top - (kWin - 1) : 0;
-        for (int w = tid; w < kWin; w += blockDim.x) s_hist[w] = 0;
+        for (int w = tid; w < kWin; w += kToppThreads) s_hist[w] = 0;
         __syncthreads();
-        for_row(lr, V, vec_ok != 0, [&](float x, int) {
-            const int k = (int)bf16_key(__float_as_uint(x) >> 16);
+        auto count = [&](uint32_t bits16) {
+            const int k = (int)bf16_key(bits16);
             if (k <= top && k >= bottom) atomicAdd(&s_hist[top - k], 1u);
-        });
-        __syncthreads();
-        // Thread t owns levels [nl*t, nl*t + nl) of the window, highest first.
-        const int nl = kWin / 256;
-        double part = 0.0;
-        for (int j = 0; j < nl; ++j) {
-            const int idx = tid * nl + j;
-            const uint32_t c = s_hist[idx];
-            if (c && top - idx >= bottom)
-                part += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT, s_exptab);
-        }
-        s_part[tid] = part;
-        __syncthreads();
-        if (tid == 0) {
-            double run = cum;
-            for (int t = 0; t < 256; ++t) {
-                const double p = s_part[t];
-                s_part[t] = run;  // exclusive prefix, offset by the mass above the window
-                run += p;
+        };
+        int v0 = 0;
+        if (vec_ok) {
+            const int nvec = V / 8;
+            int c = tid;
+            for (; c + 3 * kToppThreads < nvec; c += 4 * kToppThreads) {
+                u32x4 w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) w[u] = *(const u32x4*)(lr + (size_t)(c + u * kToppThreads) * 8);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) count((w[u][e >> 1] >> (16 * (e & 1))) & 0xffffu);
             }
-            s_part[256] = run;
-            s_found = 0;
+            for (; c < nvec; c += kToppThreads) {
+                const u32x4 w = *(const u32x4*)(lr + (size_t)c * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) count((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            }
+            v0 = nvec * 8;
         }
+        for (int v = v0 + tid; v < V; v += kToppThreads) count(lr[v]);
         __syncthreads();
-        const double pre = s_part[tid], nxt = s_part[tid + 1];
+        // Thread t owns levels [8 t, 8 t + 8) of the window, highest first.
+        double mass[kToppLevels];
+        double part = 0.0;
+#pragma unroll
+        for (int j = 0; j < kToppLevels; ++j) {
+            const int idx = tid * kToppLevels + j;
+            const uint32_t c = s_hist[idx];
+            mass[j] = (c && top - idx >= bottom)
+                ? (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT, s_exptab)
+                : 0.0;
+            part += mass[j];
+        }
+        // Exclusive prefix of the threads' parts in thread order: a lane scan
+        // per wave, then the waves in order (offset by the mass above).
+        double incl = part;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        double excl = __shfl_up(incl, 1, 64);
+        if (lane == 0) excl = 0.0;
+        if (lane == 63) s_wtot[wave] = incl;
+        if (tid == 0) s_found = 0;
+        __syncthreads();
+        // pre of thread t+1 is nxt of thread t bit for bit (same additions),
+        // so exactly one thread sees the crossing.
+        double wpre = cum;
+        for (int w = 0; w < wave; ++w) wpre += s_wtot[w];
+        const double pre = wpre + excl, nxt = wpre + incl;
         if (pre < target && nxt >= target) {
             double run = pre;
             int last = -1;
             double at_last = pre;
-            for (int j = 0; j < nl; ++j) {
-                const int idx = tid * nl + j;
-                const uint32_t c = s_hist[idx];
-                if (!c || top - idx < bottom) continue;
-                run += (double)c * tempered(bf16_to_f32(key_to_bf16(top - idx)), m, invT, s_exptab);
+            for (int j = 0; j < kToppLevels; ++j) {
+                const int idx = tid * kToppLevels + j;
+                if (!s_hist[idx] || top - idx < bottom) continue;
+                run += mass[j];
                 last = top - idx;
                 at_last = run;
                 if (run >= target) break;
@@ -553,13 +589,14 @@ __global__ __launch_bounds__(256) void accept_topp_bf16(
             s_zkeep = at_last;
             s_found = 1;
         }
+        if (tid == kToppThreads - 1) s_cum = nxt;
         __syncthreads();
         if (s_found) {
             lkey = s_lkey;
             zkeep = s_zkeep;
             break;
         }
-        cum = s_part[256];
+        cum = s_cum;
         __syncthreads();
         if (bottom == 0) break;  // never reached: keep every token
     }
@@ -1073,7 +1110,7 @@ __global__ __launch_bounds__(256) void accept_draw_pick(
     if (pl.mode != kModeResidual && pl.mode != kModeTarget) return;
     const DrawRow<T> dr(logits, draft_probs, pl, b, K, V);
     __shared__ double s_exptab[64];
-    __shared__ double s_cs[kDrawMaxChunks], s_e[kDrawMaxChunks];
+    __shared__ double s_cs[kDrawMaxChunks], s_e[kDrawMaxChunks], s_b[kDrawMaxChunks];
     __shared__ int s_unc[kDrawMaxChunks];
     __shared__ double s_total, s_pre, s_invz;
     __shared__ int s_chunk, s_f;
@@ -1084,10 +1121,12 @@ __global__ __launch_bounds__(256) void accept_draw_pick(
     const int nchunks = (V + kDrawChunk - 1) / kDrawChunk;
     const int cpl = (nchunks + 63) / 64;
     const ChunkRec* rc = recs + (size_t)b * nchunks;
+    const double u = (double)u_sample[(size_t)b * Q + pl.row];
     for (int c = tid; c < nchunks; c += 256) {
         const ChunkRec r = rc[c];
         s_e[c] = r.e;
         s_cs[c] = r.a;  // (the residual's weight sum is formed below)
+        s_b[c] = r.b;
         s_unc[c] = r.unc;
     }
     __syncthreads();
@@ -1104,7 +1143,7 @@ __global__ __launch_bounds__(256) void accept_draw_pick(
         }
         __syncthreads();
         invZ = s_invz;
-        for (int c = tid; c < nchunks; c += 256) s_cs[c] = fmax(s_cs[c] * invZ - rc[c].b, 0.0);
+        for (int c = tid; c < nchunks; c += 256) s_cs[c] = fmax(s_cs[c] * invZ - s_b[c], 0.0);
         __syncthreads();
         if (pl.fp64_z) {
             // Chunks with a token inside the margin: summed again token by
@@ -1118,7 +1157,6 @@ __global__ __launch_bounds__(256) void accept_draw_pick(
             __syncthreads();
         }
     }
-    const double u = (double)u_sample[(size_t)b * Q + pl.row];
     if (wave == 0) {
         double pre, own;
         const double tot = scan_chunks(s_cs, nchunks, cpl, lane, &pre, &own);
@@ -1438,12 +1476,12 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
                 lg, d->draft_tokens, d->temperature, d->top_p, nullptr, parts, Q, V, splits, span,
                 vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
-        accept_rowmerge<uint16_t><<<(rows + 255) / 256, 256, 0, s>>>(
+        accept_rowmerge<uint16_t><<<(rows + 3) / 4, 256, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
             d->relaxed_delta, parts, stats, rows, K, V, splits);
         if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;
         if (d->top_p) {
-            accept_topp_bf16<<<rows, 256, kWin * sizeof(uint32_t), s>>>(
+            accept_topp_bf16<<<rows, kToppThreads, kWin * sizeof(uint32_t), s>>>(
                 lg, d->draft_tokens, d->temperature, d->top_p, stats, K, V, vec_ok);
             if ((rc = check_launch("accept_topp_bf16")) != SD_OK) return rc;
         }
@@ -1459,7 +1497,7 @@ int accept_launch(const sd_accept_desc* d, void* workspace, hipStream_t s) {
                 lg, d->draft_tokens, d->temperature, d->top_p, nullptr, parts, Q, V, splits, span,
                 vec_ok);
         if ((rc = check_launch("accept_rowpart")) != SD_OK) return rc;
-        accept_rowmerge<float><<<(rows + 255) / 256, 256, 0, s>>>(
+        accept_rowmerge<float><<<(rows + 3) / 4, 256, 0, s>>>(
             lg, d->draft_tokens, d->temperature, d->top_p, has_probs, d->relaxed_topk,
             d->relaxed_delta, parts, stats, rows, K, V, splits);
         if ((rc = check_launch("accept_rowmerge")) != SD_OK) return rc;

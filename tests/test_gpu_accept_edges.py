@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from parity import DEV, host, run_accept
+from parity import DEV, compare_accept, host, run_accept
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +140,44 @@ def test_accept_edge_branches(V, dtype):
             cum = np.cumsum(p[order]) / p.sum()
             lam = row[order[np.argmax(cum >= top_p[b])]]
             assert ref["next_token"][b] == np.nonzero(row >= lam)[0].max(), (b, kind)
+
+
+@pytest.mark.parametrize("V", [32000, 129280])
+def test_accept_residual_near_equal(V):
+    """Residual draws where p_d sits within a few 1e-5 of p_t on every token
+    (the residual is the small negative part of that difference).  The GPU
+    sorts each token into or out of the residual's support with the row
+    pass's Z, and sums again with the fp64 Z every chunk holding a token
+    within 1e-5 (relative) of p_t = p_d.  Even requests only have tokens
+    outside that margin (every chunk takes a/Z - b), odd ones mostly inside
+    it.  Draft 1 has p_d = 2 p_t, so it is rejected at u = 1 - 2^-24 and the
+    final token is drawn from the residual of row 0.  Compared with the
+    oracle's draws under its exclusion windows."""
+    rng = np.random.default_rng(V + 11)
+    B, K = 12, 3
+    Q = K + 1
+    lg = (torch.randn((B, Q, V), generator=torch.Generator().manual_seed(V)) * 1.7).to(
+        torch.bfloat16)
+    lg_f = lg.float().numpy().astype(np.float64)
+    temp = np.ones(B, np.float32)
+    top_p = np.ones(B, np.float32)
+    drafts = rng.integers(0, V, (B, K)).astype(np.int32)
+    pd = np.zeros((B, K, V), np.float32)
+    clean = np.array([-3e-5, -1.2e-5, 1.2e-5, 3e-5])
+    mixed = np.array([-3e-5, -1.2e-5, -8e-6, -2e-6, 2e-6, 8e-6, 1.2e-5, 3e-5])
+    for b in range(B):
+        for n in range(K):
+            p = _softmax(lg_f[b, n])
+            eps = rng.choice(clean if b % 2 == 0 else mixed, V)
+            pd[b, n] = (p * (1.0 + eps)).astype(np.float32)
+            d = drafts[b, n]
+            pd[b, n, d] = np.float32(2.0 * p[d])
+    ua = np.full((B, Q), U_MAX, np.float32)
+    us = rng.random((B, Q)).astype(np.float32)
+    ref = oracle.accept(host(lg), drafts, temp, None, pd, ua, us)
+    assert (ref["num_accepted"] == 0).all()
+    t = lambda x: torch.tensor(x, device=DEV)
+    gpu = run_accept(lg.to(DEV), t(drafts), t(temp), None, t(pd), t(ua), t(us))
+    assert gpu["dev_error"] == 0
+    n_excl = compare_accept(gpu, ref, where=f"near-equal residual V={V}")
+    assert n_excl <= 1, n_excl
