@@ -61,8 +61,8 @@ def kernel_source_hash(kernel):
 
 def lm_head_kernel(M, hidden, vocab, dtype, cus):
     """Name of the kernel sd_lm_head launches for this shape on a device with
-    `cus` compute units (its dispatch rule: 256 x 256 tiles while they number
-    at least the CUs, else the streaming kernel with 128- or 64-row tiles), or
+    `cus` compute units (its dispatch rule: 256 x 256 tiles for more than 128
+    rows while they number at least the CUs, else the streaming kernel), or
     None for the fallback paths."""
     if dtype != "bf16" or hidden % 128:
         return None

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256, 1) void lm_head_bf16(const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // Main bf16 path (lm_head_ring for 256 x 256 tiles, lm_head_stream for 256 x
-// 128 and 256 x 64).  Both compute the transposed tile D[v][m] =
+// 128, 256 x 64 and 128 x 192, vocabulary x rows).  Both compute the transposed tile D[v][m] =
 // sum_k W[v][k] H[m][k] (A = W rows, B = H rows) so that each lane's MFMA
 // accumulator holds four consecutive vocab entries of one output row: the
 // epilogue stores 8 bytes.  k advances 64 per stage, staged in LDS by direct
@@ -168,6 +168,9 @@ __device__ __forceinline__ void wait_frags(u32x4 (&a)[NA], u32x4 (&b)[NB]) {
                      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]));
     else if constexpr (NA == 2 && NB == 2)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]));
+    else if constexpr (NA == 2 && NB == 3)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]));
     else
         static_assert(NA < 0, "unsupported fragment counts");
 }
@@ -557,23 +560,29 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
     }
     if (hidden % 128 == 0) {
         // Tile rows to the batch: all rows in one tile where possible, so each
-        // W tile is streamed from HBM once.  When that leaves CUs idle (a small
-        // vocabulary), 128-row tiles double the workgroups: the W tile is then
-        // read twice, but the stream is spread over the whole chip.
+        // W tile is streamed from HBM once.  When 256 x 256 tiles would leave
+        // CUs idle (a small vocabulary), batches of up to 192 rows take 128 x
+        // 192 tiles (all rows, twice the W tiles), larger ones 128-row tiles
+        // (the W tile is then read by two workgroups of one XCD).
         int TM = M > 128 ? 256 : (M > 64 ? 128 : 64);
         if (TM == 256) {
             int num_cus = 0;
             const int rc = cu_count("sd_lm_head", &num_cus);
             if (rc != SD_OK) return rc;
-            if ((long)((M + 255) / 256) * ((vocab + 255) / 256) < num_cus) TM = 128;
+            if ((long)((M + 255) / 256) * ((vocab + 255) / 256) < num_cus)
+                TM = M <= 192 ? 192 : 128;
         }
-        const long tiles = (long)((M + TM - 1) / TM) * ((vocab + 255) / 256);
+        const int TN = TM == 192 ? 128 : 256;
+        const long tiles = (long)((M + TM - 1) / TM) * ((vocab + TN - 1) / TN);
         if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");
         const uint16_t* h = (const uint16_t*)H;
         const uint16_t* w = (const uint16_t*)W;
         uint16_t* c = (uint16_t*)logits;
         if (TM == 256)
             lm_head_ring<<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab, hidden);
+        else if (TM == 192)
+            lm_head_stream<128, 192, 2, 2, 4><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+                                                                              hidden);
         else if (TM == 128)
             lm_head_stream<256, 128, 2, 2, 3><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
                                                                               hidden);

@@ -63,6 +63,7 @@ def test_lm_head_kernel_follows_the_dispatch_rule():
     assert k(1280, 7168, 129280, "bf16", 256) == "lm_head_ring"    # C5: 2525 tiles
     assert k(256, 7168, 129280, "bf16", 256) == "lm_head_ring"     # C3: 505 tiles
     assert k(192, 4096, 32000, "bf16", 256) == "lm_head_stream"    # C2: 125 tiles < 256 CUs
+    assert k(192, 7168, 129280, "bf16", 256) == "lm_head_ring"     # 505 tiles
     assert k(64, 5120, 152064, "bf16", 256) == "lm_head_stream"    # C4: 64-row tiles
     assert k(300, 384, 40000, "bf16", 256) == "lm_head_ring"       # 2 x 157 tiles
     assert k(300, 384, 40000, "bf16", 512) == "lm_head_stream"     # fewer tiles than CUs

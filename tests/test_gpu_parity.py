@@ -146,10 +146,13 @@ def test_attention_device_errors_flag_and_nan():
 # slot rotation wraps and the tail re-reads run).  hidden = 128 gives two
 # k-slices, fewer than any ring holds: (100, 128, 3000) and (40, 128, 5000)
 # take the three- and four-stage streaming kernels, (260, 128, 40001) the
-# five-slot ring, all with clamped prologue refills.
+# five-slot ring, all with clamped prologue refills.  (150, 256, 3001) and
+# (190, 128, 2003) take the 128 x 192 streaming tiles (more than 128 rows,
+# fewer 256 x 256 tiles than CUs), with ragged rows and vocabulary and four or
+# two k-slices for its four stages.
 @pytest.mark.parametrize("M,hidden,V", [(130, 200, 333), (64, 512, 1000), (256, 7168, 640),
                                         (260, 640, 40001), (100, 128, 3000), (40, 128, 5000),
-                                        (260, 128, 40001)])
+                                        (260, 128, 40001), (150, 256, 3001), (190, 128, 2003)])
 def test_lm_head_exact_small_integers(M, hidden, V):
     """Small-integer bf16 operands: every fp32 partial sum is exact, so the
     bf16 logits must equal the oracle's exact values rounded to nearest even
