@@ -332,6 +332,59 @@ def test_accept_mixed_modes_and_invalid_requests():
     assert e & sdv.SD_DERR_NONFINITE and e & sdv.SD_DERR_TOKEN and e & sdv.SD_DERR_PARAM
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_random_mixed_batches(seed):
+    """Randomised batches that mix, request by request, greedy rows, sampled
+    rows with and without a nucleus (temperatures 0.5-1.5), drafts that end
+    early (-1), and draft distributions of three kinds: a noisy softmax, one
+    equal to p_t within a few 1e-6 on most tokens (the residual's near-ties),
+    and a one-hot.  K from 0 to 7, vocabularies from 999 to 32000, bf16 and
+    float32 logits.  Compared with the oracle under its exclusion windows."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 41))
+    K = int(rng.integers(0, 8))
+    V = int(rng.choice([999, 4096, 5003, 32000]))
+    dtype = "f32" if seed % 3 == 2 else "bf16"
+    Q = K + 1
+    lg = _logits(B, Q, V, sdsynth.torch_dtype(dtype), seed=600 + seed)
+    lgh = host(lg)
+    lf = oracle.bf16_to_f64(lgh) if dtype == "bf16" else lgh.astype(np.float64)
+    temp = np.where(rng.random(B) < 0.3, 0.0, rng.uniform(0.5, 1.5, B)).astype(np.float32)
+    top_p = np.where(rng.random(B) < 0.5, 1.0, rng.choice([0.5, 0.9, 0.97], B)).astype(np.float32)
+    pd = np.zeros((B, K, V), np.float32)
+    drafts = np.full((B, K), -1, np.int32)
+    tt, _ = oracle.argmax(lgh)
+    for b in range(B):
+        T = float(temp[b]) if temp[b] > 0 else 1.0
+        for n in range(K):
+            kind = int(rng.integers(3))
+            if kind == 0:
+                x = lf[b, n] / T + rng.normal(0, 0.5, V)
+                q = np.exp(x - x.max())
+            elif kind == 1:
+                x = lf[b, n] / T
+                q = np.exp(x - x.max()) * (1.0 + rng.choice([-4e-6, 3e-6, 2e-3], V))
+            else:
+                q = np.zeros(V)
+                q[int(rng.integers(V))] = 1.0
+            pd[b, n] = (q / q.sum()).astype(np.float32)
+        if temp[b] == 0:
+            drafts[b] = sdsynth.greedy_drafts(tt[b:b + 1], K, V, seed + b)[0] if K else drafts[b]
+        elif K:
+            drafts[b] = sdsynth.sample_drafts(pd[b:b + 1], seed + b)[0]
+        if K and rng.random() < 0.15:
+            drafts[b, int(rng.integers(K)):] = -1
+    ua = sdsynth.philox_uniforms(700 + seed, B, Q, 0)
+    us = sdsynth.philox_uniforms(700 + seed, B, Q, 1)
+    ref = oracle.accept(lgh, drafts, temp, top_p, pd, ua, us)
+    t = lambda x: torch.tensor(x, device=DEV)
+    gpu = run_accept(lg.to(DEV), t(drafts), t(temp), t(top_p), t(pd), t(ua), t(us))
+    assert gpu["dev_error"] == 0
+    print(f"seed {seed}: B={B} K={K} V={V} {dtype}", flush=True)
+    n_excl = compare_accept(gpu, ref, where=f"random batch seed {seed}")
+    assert n_excl <= max(1, B // 8), n_excl
+
+
 def test_accept_is_deterministic():
     B, K, V = 16, 5, 4096
     lg = _logits(B, K + 1, V, torch.bfloat16, seed=21)
