@@ -385,6 +385,36 @@ def test_accept_random_mixed_batches(seed):
     assert n_excl <= max(1, B // 8), n_excl
 
 
+def test_accept_chains_longer_than_a_wave():
+    """K = 70 drafts: the decision takes a wave's 64 lanes and then the next
+    64 (greedy chains that match past lane 63, sampled chains with a -1 past
+    it), against the oracle."""
+    B, K, V = 6, 70, 1000
+    Q = K + 1
+    lg = _logits(B, Q, V, torch.bfloat16, seed=77)
+    lgh = host(lg)
+    lf = oracle.bf16_to_f64(lgh)
+    tt, _ = oracle.argmax(lgh)
+    temp = np.array([0, 0, 0, 1.0, 0.8, 1.2], np.float32)
+    pd = sdsynth.draft_probs(lf[:, :K], 77, 0.05, 1.0)
+    drafts = sdsynth.sample_drafts(pd, 77)
+    drafts[0] = tt[0, :K]                   # greedy: all 70 accepted
+    drafts[1] = tt[1, :K]
+    drafts[1, 66] = (tt[1, 66] + 1) % V     # greedy: the mismatch in the second 64
+    drafts[2] = tt[2, :K]
+    drafts[2, 65:] = -1                     # greedy: the chain ends in the second 64
+    drafts[4, 68:] = -1                     # sampled: ends in the second 64
+    ua = np.full((B, Q), 1e-6, np.float32)  # sampled drafts accepted unless p_t is tiny
+    us = sdsynth.philox_uniforms(77, B, Q, 1)
+    ref = oracle.accept(lgh, drafts, temp, None, pd, ua, us)
+    t = lambda x: torch.tensor(x, device=DEV)
+    gpu = run_accept(lg.to(DEV), t(drafts), t(temp), None, t(pd), t(ua), t(us))
+    assert gpu["dev_error"] == 0
+    compare_accept(gpu, ref, where="K = 70")
+    assert list(ref["num_accepted"][:3]) == [70, 66, 65]
+    assert ref["num_accepted"][3:].max() > 63
+
+
 def test_accept_is_deterministic():
     B, K, V = 16, 5, 4096
     lg = _logits(B, K + 1, V, torch.bfloat16, seed=21)
