@@ -353,6 +353,7 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     __shared__ float s_q[256];
     __shared__ float s_e[256];
     __shared__ float s_red[256];
+    __shared__ int s_pg[256 / kPage];  // the tile's physical pages
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const size_t oi = (((size_t)b * NQ + i) * Hq + h) * D;
@@ -374,10 +375,15 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     const int dd = tid % D, grp = tid / D;
     float m = -INFINITY, l = 0.f, acc = 0.f;
     for (int t0 = 0; t0 < n; t0 += 256) {
+        // The tile's page-table entries, read once (they are the only
+        // dependent loads in front of the key and value reads).
+        if (tid < 256 / kPage && t0 + kPage * tid < n)
+            s_pg[tid] = page_table[(size_t)b * max_pages + t0 / kPage + tid];
+        __syncthreads();
         const int p = t0 + tid;
         float s = -INFINITY;
         if (p < n && (p < L || ((vis >> (p - L)) & 1ull))) {
-            const int pg = page_table[(size_t)b * max_pages + p / kPage];
+            const int pg = s_pg[tid / kPage];
             const float* kp = k_cache + (((size_t)pg * Hkv + kvh) * kPage + p % kPage) * D;
             float dot = 0.f;
             for (int d = 0; d < D; ++d) dot += s_q[d] * kp[d];
@@ -403,12 +409,22 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
         l = l * alpha + s_red[0];
         m = mnew;
         acc *= alpha;
+        // Values of the tile's keys, eight loads in flight; the sum runs over
+        // the keys in order.
         const int cnt = min(256, n - t0);
-        for (int k = grp; k < cnt; k += NG) {
-            const int pk = t0 + k;
-            const int pg = page_table[(size_t)b * max_pages + pk / kPage];
-            acc += s_e[k] * v_cache[(((size_t)pg * Hkv + kvh) * kPage + pk % kPage) * D + dd];
+        int k = grp;
+        for (; k + 7 * NG < cnt; k += 8 * NG) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int kk = k + u * NG;
+                v[u] = v_cache[(((size_t)s_pg[kk / kPage] * Hkv + kvh) * kPage + kk % kPage) * D + dd];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += s_e[k + u * NG] * v[u];
         }
+        for (; k < cnt; k += NG)
+            acc += s_e[k] * v_cache[(((size_t)s_pg[k / kPage] * Hkv + kvh) * kPage + k % kPage) * D + dd];
         __syncthreads();
     }
     s_red[tid] = acc;
