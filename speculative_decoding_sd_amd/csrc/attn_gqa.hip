@@ -585,6 +585,344 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
     }
 }
 
+// E4M3 cache, head dim 128, 33..48 query rows per (request, kv head): the
+// same tile stream with 16x16x32 MFMA blocks, so the rows pad to 48 instead
+// of 64 (a quarter less MFMA and softmax work per tile) and the wave's state
+// fits two waves per SIMD (two workgroups per CU, a 20 KiB ring per wave):
+// one wave's softmax, conversions and DMA issue overlap the other's MFMAs.
+// Operand layouts (lane l, g = l / 16): A row l%16, k = 8g..8g+7; B column
+// l%16, same k; result: lane l holds column l%16, rows 4g..4g+3.
+//   S^T block kb (kb = 0, 1) of a tile: MFMA row i is key 8(i/4) + 4kb + i%4,
+//     so lane group g holds keys 8g..8g+7 of its query row (slot e = 4kb + r
+//     is key 8g + e), which is the k order of the P^T operand of O^T += V^T P^T;
+//   k-steps 2j and 2j+1 (j = 0, 1) of lane group g run over dims
+//     16(4j + g) .. +7 and +8 .. +15: one 16-byte read of a K row, Q following.
+// Swizzle (128-byte rows, row parity picks the bank half): the 16 rows of a
+// K read pass are 8q + 4kb + r (fixed bit 2) and those of a V read pass
+// (ds_read_b64_tr_b8, lane groups 2p and 2p+1) are 16p .. 16p+15 (fixed bit
+// 4); f = 4 b3 + 2 b1 + (b2 ^ b4) is a bijection on the 8 rows of one parity
+// in either pass.
+__device__ __forceinline__ int gqa16_xor(int row) {
+    return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | (((row >> 2) ^ (row >> 4)) & 1);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row of a
+// 16x16 result), the same value in all four lanes.
+__device__ __forceinline__ float quads_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return halves_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quads_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return halves_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+template <int NB>
+__global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
+    const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ first,
+    float* __restrict__ part_o, float2* __restrict__ part_ml, float* __restrict__ out,
+    uint16_t* __restrict__ out_lowp, int B, int NQ, int Hq, int Hkv, int G, int R, int max_pages,
+    float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const uint64_t* __restrict__ anc) {
+    constexpr int D = 128;
+    using T = GqaTile<D, true, 3>;
+    static_assert(T::kRingBytes * 8 <= 160 * 1024, "two workgroups of four rings per CU");
+    constexpr int NDB = D / 16;  // 16-dim blocks of O^T
+    __shared__ __attribute__((aligned(1024))) char s_ring[4][T::kRingBytes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int nw = gridDim.x * 4;
+    char* ring = s_ring[wave];
+
+    int goff[T::kDmaHalf];
+#pragma unroll
+    for (int j = 0; j < T::kDmaHalf; ++j) {
+        const int n = 64 * j + lane;
+        const int row = n / T::kRowChunks;
+        goff[j] = row * T::kRowBytes + 16 * ((n % T::kRowChunks) ^ gqa16_xor(row));
+    }
+    const size_t head_bytes = (size_t)kPage * T::kRowBytes;
+    char* const k_ring = ring;
+    char* const v_ring = ring + T::kKStages * T::kHalfBytes;
+    auto load_pg = [&](TileCursor& c) {
+        if (c.g < c.hi) c.pg = page_table[(size_t)c.b * max_pages + (kTile * c.t) / kPage];
+    };
+    auto issue = [&](const char* __restrict__ cache, const TileCursor& c, const char* dst_p) {
+        const int ks = kTile * c.t;
+        const char* src = cache + ((size_t)c.pg * Hkv + c.kvh) * head_bytes +
+                          (size_t)(ks % kPage) * T::kRowBytes;
+        const uint32_t dst = lds_byte_addr(dst_p);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < T::kDmaHalf; ++j)
+            dma16(src + goff[j], __builtin_amdgcn_readfirstlane(dst + 1024u * j));
+    };
+
+    // K reads of block kb, k-step pair j: key 8(li/4) + 4kb + li%4, logical
+    // chunk 4j + lg.
+    int koff[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = 8 * (li >> 2) + 4 * kb + (li & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            koff[kb][j] = key * T::kRowBytes + 16 * ((4 * j + lg) ^ gqa16_xor(key));
+    }
+    // V reads of dim block db (ds_read_b64_tr_b8: lane t of a 16-lane group
+    // receives byte t%8 of the reads of lanes t/8 + 2e as byte e): lane li
+    // reads key 8lg + li/2, dims 16db + 8(li&1) .. +7, so lane t receives dim
+    // 16db + t of keys 8lg .. 8lg+7 in slot order.
+    const int vkey = 8 * lg + (li >> 1);
+    const int vbase = vkey * T::kRowBytes + 8 * (li & 1), vx = gqa16_xor(vkey);
+
+    const int Th = first[B];
+    const long n_tiles = (long)Th * Hkv;
+    const int gw = blockIdx.x * 4 + wave;
+    const int nwe = (int)min((long)nw, n_tiles);
+    TileCursor kc;
+    if (gw < nwe)
+        cursor_begin(kc, (int)(n_tiles * gw / nwe), (int)(n_tiles * (gw + 1) / nwe), B, Th, first,
+                     seq_lens);
+    else
+        kc.g = kc.hi = 0;
+    load_pg(kc);
+    TileCursor vc = kc, cc = kc;
+    int nk = 0, nv = 0;
+    auto issue_k = [&]() {
+        if (kc.g < kc.hi) {
+            issue(k_cache, kc, k_ring + (nk % T::kKStages) * T::kHalfBytes);
+            ++nk;
+            cursor_next(kc, B, first, seq_lens);
+        }
+    };
+    auto issue_v = [&]() {
+        if (vc.g < vc.hi) {
+            issue(v_cache, vc, v_ring + (nv % T::kVStages) * T::kHalfBytes);
+            ++nv;
+            cursor_next(vc, B, first, seq_lens);
+        }
+    };
+    auto wait_groups = [&](int g) { wait_halves<T::kDmaHalf>(g); };
+    issue_k();
+    load_pg(kc);
+#pragma unroll
+    for (int i = 1; i < T::kKStages; ++i) {
+        issue_k();
+        load_pg(kc);
+        issue_v();
+        load_pg(vc);
+    }
+    int cseq = 0;
+
+    u32x4 qf[NB][4];
+    float m_r[NB], l_r[NB];
+    float sl2 = scale_log2, vsc = 1.f;
+    f32x4 o[NB][NDB];
+    int seg_t0 = 0;
+    bool first_seg = true;
+    while (cc.g < cc.hi) {
+        wait_groups((nk - 1 - cseq) + (nv - max(cseq - 1, 0)));
+        const int cend = cc.L + NQ;
+        if (cc.t == 0 || cseq == 0) {
+            seg_t0 = cc.t;
+            sl2 = scale_log2 * k_scale[cc.kvh];
+            vsc = v_scale[cc.kvh];
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) {
+                const int row = rb * 16 + li;
+                if (row < R) {
+                    const int i = row / G, gq = row - i * G;
+                    const uint16_t* qp = q + (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D +
+                                         16 * lg;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        qf[rb][s] = *(const u32x4*)(qp + 64 * (s >> 1) + 8 * (s & 1));
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) qf[rb][s] = u32x4{0, 0, 0, 0};
+                }
+                m_r[rb] = -INFINITY;
+                l_r[rb] = 0.f;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            wait_vmcnt<0>();
+        }
+        const char* ktile = k_ring + (cseq % T::kKStages) * T::kHalfBytes;
+        char* vtile = v_ring + (cseq % T::kVStages) * T::kHalfBytes;
+        const int ks = kTile * cc.t;
+
+        // S^T = K Q^T: NB x 2 independent accumulators, four k-steps each.
+        f32x4 sacc[NB][2];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 raw[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) raw[kb][j] = *(const u32x4*)(ktile + koff[kb][j]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 k0 = e4m3x8_to_bf16(raw[kb][j][0], raw[kb][j][1]);
+                const u32x4 k1 = e4m3x8_to_bf16(raw[kb][j][2], raw[kb][j][3]);
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) sacc[rb][kb] = mfma_16x16x32(k0, qf[rb][2 * j], sacc[rb][kb]);
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb)
+                    sacc[rb][kb] = mfma_16x16x32(k1, qf[rb][2 * j + 1], sacc[rb][kb]);
+            }
+        load_pg(kc);
+        load_pg(vc);
+
+        // Online softmax; lane (li, lg) holds keys 8lg .. 8lg+7 of query row
+        // 16rb + li (slot e = 4kb + r).
+        const bool unmasked = ks + kTile <= cend && ks + kTile - 1 <= cc.L;
+        u32x4 pb[NB], pbl[NB];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb) {
+            float sv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sv[e] = sacc[rb][e >> 2][e & 3] * sl2;
+            if (!unmasked) {
+                // The row's position (padding rows see every key of the
+                // pair) and, for a draft tree, its node's visibility mask,
+                // read here: masked tiles are at most two per pair.
+                const int row = rb * 16 + li;
+                const int i = row < R ? row / G : NQ - 1;
+                const uint64_t vis = (anc && row < R) ? anc[(size_t)cc.b * NQ + i] : ~0ull;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int key = ks + 8 * lg + e;
+                    const int a = key - cc.L;
+                    const bool seen = anc ? (a < 0 || (a < 64 && ((vis >> a) & 1u) != 0))
+                                          : key <= cc.L + i;
+                    if (key >= cend || !seen) sv[e] = -INFINITY;
+                }
+            }
+            float tmax = sv[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
+            tmax = quads_max(tmax);
+            const bool raise = tmax > m_r[rb] + kRescaleSlack;
+            if (__any(raise)) {
+                const float mnew = raise ? tmax : m_r[rb];
+                const float alpha = raise ? __builtin_amdgcn_exp2f(m_r[rb] - mnew) : 1.f;
+                l_r[rb] *= alpha;
+                m_r[rb] = mnew;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
+            }
+            const float msafe = (m_r[rb] == -INFINITY) ? 0.f : m_r[rb];
+            float psum = 0.f;
+            uint32_t pk[4], pl[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(sv[e] - msafe);
+                const float p1 = __builtin_amdgcn_exp2f(sv[e + 1] - msafe);
+                const uint32_t hi = cvt_pk_bf16(p0, p1);
+                psum += p0 + p1;
+                pk[e >> 1] = hi;
+                pl[e >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
+                                         p1 - __uint_as_float(hi & 0xffff0000u));
+            }
+            l_r[rb] += quads_sum(psum);
+            pb[rb] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            pbl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+        }
+
+        wait_groups((nv - 1 - cseq) + max(0, nk - (cseq + 2)));
+        if (ks + kTile > cend) {
+            const int nvk = cend - ks;
+            for (int idx = lane; idx < (kTile - nvk) * T::kRowChunks; idx += 64) {
+                const int row = nvk + idx / T::kRowChunks, c = idx % T::kRowChunks;
+                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa16_xor(row))) =
+                    u32x4{0, 0, 0, 0};
+            }
+        }
+
+        // O^T += V^T P^T, every V fragment read before the first MFMA.
+        __builtin_amdgcn_sched_barrier(0);
+        u32x2 vr[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vr[db] = lds_read_tr8(vtile + vbase + 16 * (db ^ vx));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const u32x4 a = e4m3x8_to_bf16(vr[db].x, vr[db].y);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32(a, pb[rb], o[rb][db]);
+#pragma unroll
+            for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32(a, pbl[rb], o[rb][db]);
+        }
+
+        issue_k();
+        issue_v();
+        const bool last_of_pair = cc.t == cc.P - 1;
+        if (last_of_pair || cc.g + 1 >= cc.hi) {
+            if (seg_t0 == 0 && last_of_pair) {
+                // Lane (li, lg) holds dims 16db + 4lg .. +3 of row 16rb + li.
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const int row = rb * 16 + li;
+                    if (row >= R) continue;
+                    const int i = row / G, gq = row - i * G;
+                    const size_t oi = (((size_t)cc.b * NQ + i) * Hq + cc.kvh * G + gq) * D;
+                    const float inv = vsc / l_r[rb];
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const int d = db * 16 + 4 * lg;
+                        const f32x4 v = o[rb][db] * inv;
+                        *(f32x4*)(out + oi + d) = v;
+                        if (out_lowp) {
+                            u32x2 w;
+                            w.x = pack_bf16x2(v[0], v[1]);
+                            w.y = pack_bf16x2(v[2], v[3]);
+                            *(u32x2*)(out_lowp + oi + d) = w;
+                        }
+                    }
+                }
+            } else {
+                const size_t pidx = 2 * (size_t)gw + (first_seg ? 0 : 1);
+                // Dim 16db + 4lg + r of row `row` at po[dim * R + row].  R
+                // passes through an empty asm here so that the compiler
+                // computes these offsets in this (rare) block instead of
+                // hoisting 32 of them out of the tile loop into registers.
+                int Ro = R;
+                asm volatile("" : "+s"(Ro));
+                float* po = part_o + pidx * D * Ro + 4 * lg * Ro;
+#pragma unroll
+                for (int rb = 0; rb < NB; ++rb) {
+                    const int row = rb * 16 + li;
+                    if (row >= Ro) continue;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            po[(db * 16 + r) * Ro + row] = o[rb][db][r] * vsc;
+                    if (lg == 0) part_ml[pidx * Ro + row] = make_float2(m_r[rb], l_r[rb]);
+                }
+            }
+            first_seg = false;
+        }
+        cursor_next(cc, B, first, seq_lens);
+        ++cseq;
+    }
+}
+
 // first[b] = number of 32-key tiles of the valid requests before b (exclusive
 // prefix sum), first[B] = their total.  One block.
 __global__ __launch_bounds__(1024) void attn_items(const int32_t* __restrict__ seq_lens,
@@ -629,8 +967,12 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, cons
     const int G = d->n_q_heads / d->n_kv_heads;
     const bool f8 = d->kv_format == SD_KV_E4M3;
     // gqa_groups_per_cu of the variant launched (it does not depend on D)
-    const int groups = (f8 && R <= 32) ? gqa_groups_per_cu<128, 1, true>()
-                                       : gqa_groups_per_cu<128, 2, false>();
+    // 33..48 rows with an E4M3 cache at head dim 128: 16-row blocks
+    // (attn_gqa_f8_r16, two workgroups per CU).
+    const bool r16 = f8 && d->d_qk == 128 && R > 32 && R <= 48;
+    const int groups = r16 ? 2
+                       : (f8 && R <= 32) ? gqa_groups_per_cu<128, 1, true>()
+                                         : gqa_groups_per_cu<128, 2, false>();
     const int grid = std::min(num_cus * groups, max_waves / 4);
     *nw = 4 * grid;
 #define SDV_LAUNCH_GQA(DD, RBB, F8)                                                              \
@@ -640,7 +982,17 @@ int gqa_launch(const sd_attn_desc* d, const int32_t* valid, int32_t* first, cons
         d->n_q_heads, d->n_kv_heads, G, R, d->max_pages, scale_log2, d->k_scale, d->v_scale, anc)
     if (d->d_qk == 128) {
         if (f8) {
-            if (R <= 32) SDV_LAUNCH_GQA(128, 1, true); else SDV_LAUNCH_GQA(128, 2, true);
+            if (R <= 32) {
+                SDV_LAUNCH_GQA(128, 1, true);
+            } else if (r16) {
+                attn_gqa_f8_r16<3><<<grid, 256, 0, s>>>(
+                    (const uint16_t*)d->q, (const char*)d->k_cache, (const char*)d->v_cache,
+                    d->page_table, d->seq_lens, first, po, pml, d->out, (uint16_t*)d->out_lowp,
+                    d->batch, d->num_q, d->n_q_heads, d->n_kv_heads, G, R, d->max_pages,
+                    scale_log2, d->k_scale, d->v_scale, anc);
+            } else {
+                SDV_LAUNCH_GQA(128, 2, true);
+            }
         } else {
             if (R <= 32) SDV_LAUNCH_GQA(128, 1, false); else SDV_LAUNCH_GQA(128, 2, false);
         }

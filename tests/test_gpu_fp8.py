@@ -61,7 +61,9 @@ def _oracle(wl, sel=None, append=True):
 @pytest.mark.parametrize("B,K,Hq,Hkv,D,lens", [
     (3, 5, 16, 4, 128, [0, 61, 1300]),      # 24 rows/kv head; L=0; page-straddling append
     (2, 7, 10, 2, 64, [5, 700]),            # 40 rows/kv head (two row blocks), head dim 64
-    (2, 7, 40, 8, 128, [3000, 1000]),       # long-context head layout, two row blocks
+    (2, 7, 40, 8, 128, [3000, 1000]),       # long-context head layout: 40 rows, 16-row blocks
+    (2, 10, 6, 2, 128, [0, 200]),           # 33 rows (fewest in 16-row blocks); L = 0
+    (3, 7, 12, 2, 128, [17, 64, 2049]),     # 48 rows (most in 16-row blocks)
     (4, 4, 32, 8, 128, [512, 4097, 777, 64]),  # serving head layout, ragged
     (1, 0, 4, 1, 64, [33]),                 # K = 0: plain single-token decode
     (3, 3, 8, 1, 64, [95, 1, 2000]),        # one kv head, 32 rows, tails of 1..31 keys

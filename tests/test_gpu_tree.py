@@ -70,6 +70,7 @@ def _oracle_attention(wl, par):
     ("as_dtype", "bf16", 2, 9, 20, 4, 64, [5, 2000]),             # 50 rows: two row blocks
     ("e4m3", "bf16", 4, 7, 16, 4, 128, [3, 64, 999, 4100]),
     ("e4m3", "bf16", 3, 15, 8, 2, 128, [10, 127, 3000]),          # 16 nodes, 64 rows
+    ("e4m3", "bf16", 3, 11, 12, 4, 128, [5, 400, 2100]),          # 36 rows: 16-row blocks
     ("as_dtype", "f32", 2, 5, 4, 2, 64, [7, 130]),                # float32 path
     ("as_dtype", "bf16", 2, 63, 2, 2, 64, [17, 500]),             # 64 nodes: the largest tree
 ])
