@@ -43,7 +43,7 @@ WORKLOAD_NAMES = {1: "c1_tiny_fp32", 2: "c2_gqa_stochastic", 3: "c3_mla_greedy",
                   4: "c4_long_context", 5: "c5_ragged_serving"}
 # Source files whose contents a kernel's PMC traffic figure is tied to.
 KERNEL_SOURCES = {"lm_head_stream": "lm_head.hip", "lm_head_ring": "lm_head.hip",
-                  "attn_gqa_stream": "attn_gqa.hip",
+                  "attn_gqa_stream": "attn_gqa.hip", "attn_gqa_f8_r16": "attn_gqa.hip",
                   "attn_mla_bf16": "attn_mla.hip"}
 
 
@@ -69,6 +69,21 @@ def lm_head_kernel(M, hidden, vocab, dtype, cus):
     if M > 128 and ((M + 255) // 256) * ((vocab + 255) // 256) >= cus:
         return "lm_head_ring"
     return "lm_head_stream"
+
+
+def attention_kernel(mla, dtype, kv_cache, n_q_heads, n_kv_heads, num_q, d_qk):
+    """Name of the attention kernel sd_verify_attn launches for this shape (its
+    dispatch rule: the MLA kernel; for GQA with an E4M3 cache at head dim 128
+    and 33..48 query rows per kv head the 16-row-block kernel, else the
+    streaming kernel), or None for the float32 path."""
+    if mla:
+        return "attn_mla_bf16"
+    if dtype != "bf16":
+        return None
+    rows = (n_q_heads // n_kv_heads) * num_q
+    if kv_cache == "e4m3" and d_qk == 128 and 32 < rows <= 48:
+        return "attn_gqa_f8_r16"
+    return "attn_gqa_stream"
 
 
 def profiled_fields(kernel, workload):
@@ -508,7 +523,8 @@ def main():
         cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
         dom_kernel = lm_head_kernel(cfg.batch * cfg.num_q, cfg.hidden, cfg.vocab, cfg.dtype, cus)
     else:
-        dom_kernel = "attn_mla_bf16" if cfg.mla else ("attn_gqa_stream" if cfg.dtype == "bf16" else None)
+        dom_kernel = attention_kernel(cfg.mla, cfg.dtype, cfg.kv_cache, cfg.n_q_heads,
+                                      cfg.n_kv_heads, cfg.num_q, cfg.d_qk)
     traffic = profiled_traffic(dom_kernel, workload) if dom_kernel else None
     counters = profiled_counters(dom_kernel, workload) if dom_kernel else None
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],

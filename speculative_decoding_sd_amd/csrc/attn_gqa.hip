@@ -21,7 +21,8 @@
 //                  max is raised only when a tile exceeds it by more than 2^8;
 //   O^T += V^T P^T A = V^T fragments by ds_read_b64_tr_b16 (bf16) or
 //                  ds_read_b64_tr_b8 + conversion (E4M3) from the row-major V
-//                  tile, P in bf16 hi + lo halves (two MFMAs).
+//                  tile; bf16 cache: P in bf16 hi + lo halves (two MFMAs);
+//                  E4M3 cache: V exact in fp16, P rounded to fp16 (one MFMA).
 // A wave's tiles of one pair form a segment, written once at its end: to the
 // output when it covers the whole pair, else as an unnormalised partial
 // (O^T, m, l) that attn_combine merges.
@@ -96,6 +97,38 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+
+// With an E4M3 cache the value codes convert to fp16 exactly (E4M3 values lie
+// in fp16's range with at most 4 significant bits), so O^T += V^T P^T runs as
+// one fp16 MFMA per fragment with P rounded to fp16 (relative error at most
+// 2^-11 per weight, fp32 accumulation) instead of the bf16 hi + lo pair of the
+// bf16 cache.  P = exp2(s - m) <= 2^8 is scaled by 2^7 before the rounding, so
+// that weights down to 2^-31 of the reference stay representable (fp16
+// subnormals start at 2^-24); the value scale absorbs the 2^-7.
+constexpr float kPScale = 128.f, kPScaleInv = 1.f / 128.f;
+
+__device__ __forceinline__ u32x4 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+    return u32x4{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 (lo in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, f16x2_t));
+}
+
+// The fp16 form of mfma_32x32x16 (same operand and result layouts).
+__device__ __forceinline__ f32x16 mfma_32x32x16_h(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // The work is the sequence of 32-key tiles of every (kv head, request) pair,
@@ -341,7 +374,7 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
             seg_t0 = cc.t;
             if constexpr (F8) {
                 sl2 = scale_log2 * k_scale[cc.kvh];
-                vsc = v_scale[cc.kvh];
+                vsc = v_scale[cc.kvh] * kPScaleInv;
             }
             // New segment: Q fragments (B operand; column = query row, k = d;
             // E4M3: the dims of k-step s are 32(s/2) + 16lh + 8(s%2) .. +7).
@@ -470,11 +503,16 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(sacc[rb][r] - msafe);
                 const float p1 = __builtin_amdgcn_exp2f(sacc[rb][r + 1] - msafe);
-                const uint32_t hi = cvt_pk_bf16(p0, p1);
                 psum += p0 + p1;
-                pk[r >> 1] = hi;
-                pl[r >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
-                                         p1 - __uint_as_float(hi & 0xffff0000u));
+                if constexpr (F8) {
+                    pk[r >> 1] = cvt_pk_f16(p0 * kPScale, p1 * kPScale);
+                    pl[r >> 1] = 0u;
+                } else {
+                    const uint32_t hi = cvt_pk_bf16(p0, p1);
+                    pk[r >> 1] = hi;
+                    pl[r >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
+                                             p1 - __uint_as_float(hi & 0xffff0000u));
+                }
             }
             psum = halves_sum(psum);
             l_r[rb] += psum;
@@ -519,11 +557,18 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x4 a = F8 ? e4m3x8_to_bf16(vf[tt][db][0], vf[tt][db][1]) : vf[tt][db];
+                if constexpr (F8) {
+                    const u32x4 a = e4m3x8_to_f16(vf[tt][db][0], vf[tt][db][1]);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    o[rb][db] = mfma_32x32x16(a, pb[rb][tt], o[rb][db]);
-                    o[rb][db] = mfma_32x32x16(a, pbl[rb][tt], o[rb][db]);
+                    for (int rb = 0; rb < RB; ++rb)
+                        o[rb][db] = mfma_32x32x16_h(a, pb[rb][tt], o[rb][db]);
+                } else {
+                    const u32x4 a = vf[tt][db];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        o[rb][db] = mfma_32x32x16(a, pb[rb][tt], o[rb][db]);
+                        o[rb][db] = mfma_32x32x16(a, pbl[rb][tt], o[rb][db]);
+                    }
                 }
             }
 
@@ -564,18 +609,26 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
                 // Partial rows in the wave's slot: 2w for its first segment,
                 // 2w + 1 for its last.
                 const size_t pidx = 2 * (size_t)gw + (first_seg ? 0 : 1);
-                float* po = part_o + pidx * D * R;
+                // Dim d of row `row` at po[d * R + row], d = 32db + 8(r/4) +
+                // 4lh + r%4: the lane's part (4lh) in the base pointer, the
+                // rest a wave-uniform index.  R passes through an empty asm
+                // so that the compiler computes the offsets in this (rare)
+                // block instead of hoisting them out of the tile loop, where
+                // they would be kept in (or spilled from) registers.
+                int Ro = R;
+                asm volatile("" : "+s"(Ro));
+                float* po = part_o + pidx * D * Ro + 4 * lh * Ro;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     const int row = rb * 32 + ln;
-                    if (row >= R) continue;
+                    if (row >= Ro) continue;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            po[(size_t)(db * 32 + mfma_row(r, lane)) * R + row] =
+                            po[(db * 32 + 8 * (r >> 2) + (r & 3)) * Ro + row] =
                                 F8 ? o[rb][db][r] * vsc : o[rb][db][r];
-                    if (lh == 0) part_ml[pidx * R + row] = make_float2(m_r[rb], l_r[rb]);
+                    if (lh == 0) part_ml[pidx * Ro + row] = make_float2(m_r[rb], l_r[rb]);
                 }
             }
             first_seg = false;
@@ -609,6 +662,11 @@ __device__ __forceinline__ int gqa16_xor(int row) {
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32_h(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 // max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row of a
@@ -737,7 +795,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
         if (cc.t == 0 || cseq == 0) {
             seg_t0 = cc.t;
             sl2 = scale_log2 * k_scale[cc.kvh];
-            vsc = v_scale[cc.kvh];
+            vsc = v_scale[cc.kvh] * kPScaleInv;
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) {
                 const int row = rb * 16 + li;
@@ -792,7 +850,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
         // Online softmax; lane (li, lg) holds keys 8lg .. 8lg+7 of query row
         // 16rb + li (slot e = 4kb + r).
         const bool unmasked = ks + kTile <= cend && ks + kTile - 1 <= cc.L;
-        u32x4 pb[NB], pbl[NB];
+        u32x4 pb[NB];
 #pragma unroll
         for (int rb = 0; rb < NB; ++rb) {
             float sv[8];
@@ -829,20 +887,16 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
             }
             const float msafe = (m_r[rb] == -INFINITY) ? 0.f : m_r[rb];
             float psum = 0.f;
-            uint32_t pk[4], pl[4];
+            uint32_t pk[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(sv[e] - msafe);
                 const float p1 = __builtin_amdgcn_exp2f(sv[e + 1] - msafe);
-                const uint32_t hi = cvt_pk_bf16(p0, p1);
                 psum += p0 + p1;
-                pk[e >> 1] = hi;
-                pl[e >> 1] = cvt_pk_bf16(p0 - __uint_as_float(hi << 16),
-                                         p1 - __uint_as_float(hi & 0xffff0000u));
+                pk[e >> 1] = cvt_pk_f16(p0 * kPScale, p1 * kPScale);
             }
             l_r[rb] += quads_sum(psum);
             pb[rb] = u32x4{pk[0], pk[1], pk[2], pk[3]};
-            pbl[rb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
         }
 
         wait_groups((nv - 1 - cseq) + max(0, nk - (cseq + 2)));
@@ -862,11 +916,9 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
         for (int db = 0; db < NDB; ++db) vr[db] = lds_read_tr8(vtile + vbase + 16 * (db ^ vx));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const u32x4 a = e4m3x8_to_bf16(vr[db].x, vr[db].y);
+            const u32x4 a = e4m3x8_to_f16(vr[db].x, vr[db].y);
 #pragma unroll
-            for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32(a, pb[rb], o[rb][db]);
-#pragma unroll
-            for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32(a, pbl[rb], o[rb][db]);
+            for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32_h(a, pb[rb], o[rb][db]);
         }
 
         issue_k();
@@ -897,10 +949,8 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
                 }
             } else {
                 const size_t pidx = 2 * (size_t)gw + (first_seg ? 0 : 1);
-                // Dim 16db + 4lg + r of row `row` at po[dim * R + row].  R
-                // passes through an empty asm here so that the compiler
-                // computes these offsets in this (rare) block instead of
-                // hoisting 32 of them out of the tile loop into registers.
+                // Dim 16db + 4lg + r of row `row` at po[dim * R + row]; R
+                // passes through an empty asm as in attn_gqa_stream.
                 int Ro = R;
                 asm volatile("" : "+s"(Ro));
                 float* po = part_o + pidx * D * Ro + 4 * lg * Ro;

@@ -71,6 +71,19 @@ def test_lm_head_kernel_follows_the_dispatch_rule():
     assert k(130, 200, 333, "bf16", 256) is None                   # hidden not a multiple of 128
 
 
+def test_attention_kernel_follows_the_dispatch_rule():
+    k = bench.attention_kernel
+    assert k(True, "bf16", "as_dtype", 128, 1, 4, 576) == "attn_mla_bf16"         # C3
+    assert k(False, "bf16", "as_dtype", 40, 8, 8, 128) == "attn_gqa_stream"       # C4
+    assert k(False, "bf16", "e4m3", 40, 8, 8, 128) == "attn_gqa_f8_r16"           # C4, E4M3: 40 rows
+    assert k(False, "bf16", "e4m3", 32, 8, 5, 128) == "attn_gqa_stream"           # C5, E4M3: 20 rows
+    assert k(False, "bf16", "e4m3", 6, 2, 11, 128) == "attn_gqa_f8_r16"           # 33 rows
+    assert k(False, "bf16", "e4m3", 12, 2, 8, 128) == "attn_gqa_f8_r16"           # 48 rows
+    assert k(False, "bf16", "e4m3", 8, 2, 16, 128) == "attn_gqa_stream"           # 64 rows
+    assert k(False, "bf16", "e4m3", 10, 2, 8, 64) == "attn_gqa_stream"            # head dim 64
+    assert k(False, "f32", "as_dtype", 4, 4, 4, 64) is None                       # C1
+
+
 def test_multi_gpu_run_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
