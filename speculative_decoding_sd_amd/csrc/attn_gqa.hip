@@ -553,6 +553,22 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
                     vf[tt][db] = u32x4{v0.x, v0.y, v1.x, v1.y};
                 }
             }
+        // This tile's stages are read (K in S^T; the V fragments above, which
+        // the lgkmcnt wait below completes): refill them kKStages (K) and
+        // kVStages (V) tiles ahead in the wave's stream, the DMA ops
+        // interleaved with the V^T blocks (K ops in key half 0, V ops in key
+        // half 1) so that their issue stalls overlap this wave's MFMAs.  The
+        // issue order is unchanged (K before V), so the vmcnt waits hold.
+        constexpr int OPB = T::kDmaHalf / NDB;  // DMA ops per V^T block
+        static_assert(OPB * NDB == T::kDmaHalf, "refill ops split evenly over the blocks");
+        const bool dk = kc.g < kc.hi, dv = vc.g < vc.hi;
+        const char* ksrc = k_cache + ((size_t)kc.pg * Hkv + kc.kvh) * head_bytes +
+                           (size_t)((kTile * kc.t) % kPage) * T::kRowBytes;
+        const char* vsrc = v_cache + ((size_t)vc.pg * Hkv + vc.kvh) * head_bytes +
+                           (size_t)((kTile * vc.t) % kPage) * T::kRowBytes;
+        const uint32_t kdst = lds_byte_addr(k_ring + (nk % T::kKStages) * T::kHalfBytes);
+        const uint32_t vdst = lds_byte_addr(v_ring + (nv % T::kVStages) * T::kHalfBytes);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -570,12 +586,26 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
                         o[rb][db] = mfma_32x32x16(a, pbl[rb][tt], o[rb][db]);
                     }
                 }
+#pragma unroll
+                for (int u = 0; u < OPB; ++u) {
+                    const int j = db * OPB + u;
+                    if (tt == 0) {
+                        if (dk)
+                            dma16(ksrc + goff[j], __builtin_amdgcn_readfirstlane(kdst + 1024u * j));
+                    } else if (dv) {
+                        dma16(vsrc + goff[j], __builtin_amdgcn_readfirstlane(vdst + 1024u * j));
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-
-        // This tile's stages are read: refill them kKStages (K) and
-        // kVStages (V) tiles ahead in the wave's stream.
-        issue_k();
-        issue_v();
+        if (dk) {
+            ++nk;
+            cursor_next(kc, B, first, seq_lens);
+        }
+        if (dv) {
+            ++nv;
+            cursor_next(vc, B, first, seq_lens);
+        }
         const bool last_of_pair = cc.t == cc.P - 1;
         if (last_of_pair || cc.g + 1 >= cc.hi) {
             if (seg_t0 == 0 && last_of_pair) {
@@ -839,7 +869,8 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
                 const u32x4 k0 = e4m3x8_to_bf16(raw[kb][j][0], raw[kb][j][1]);
                 const u32x4 k1 = e4m3x8_to_bf16(raw[kb][j][2], raw[kb][j][3]);
 #pragma unroll
-                for (int rb = 0; rb < NB; ++rb) sacc[rb][kb] = mfma_16x16x32(k0, qf[rb][2 * j], sacc[rb][kb]);
+                for (int rb = 0; rb < NB; ++rb)
+                    sacc[rb][kb] = mfma_16x16x32(k0, qf[rb][2 * j], sacc[rb][kb]);
 #pragma unroll
                 for (int rb = 0; rb < NB; ++rb)
                     sacc[rb][kb] = mfma_16x16x32(k1, qf[rb][2 * j + 1], sacc[rb][kb]);
@@ -914,15 +945,38 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
         u32x2 vr[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) vr[db] = lds_read_tr8(vtile + vbase + 16 * (db ^ vx));
+        // Refills of this tile's stages, one DMA op after each V^T block (as in
+        // attn_gqa_stream: K ops first, then V).
+        const bool dk = kc.g < kc.hi, dv = vc.g < vc.hi;
+        const char* ksrc = k_cache + ((size_t)kc.pg * Hkv + kc.kvh) * head_bytes +
+                           (size_t)((kTile * kc.t) % kPage) * T::kRowBytes;
+        const char* vsrc = v_cache + ((size_t)vc.pg * Hkv + vc.kvh) * head_bytes +
+                           (size_t)((kTile * vc.t) % kPage) * T::kRowBytes;
+        const uint32_t kdst = lds_byte_addr(k_ring + (nk % T::kKStages) * T::kHalfBytes);
+        const uint32_t vdst = lds_byte_addr(v_ring + (nv % T::kVStages) * T::kHalfBytes);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const u32x4 a = e4m3x8_to_f16(vr[db].x, vr[db].y);
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) o[rb][db] = mfma_16x16x32_h(a, pb[rb], o[rb][db]);
+            static_assert(NDB == 2 * T::kDmaHalf, "one refill op per V^T block");
+            if (db < T::kDmaHalf) {
+                if (dk) dma16(ksrc + goff[db], __builtin_amdgcn_readfirstlane(kdst + 1024u * db));
+            } else if (dv) {
+                const int j = db - T::kDmaHalf;
+                dma16(vsrc + goff[j], __builtin_amdgcn_readfirstlane(vdst + 1024u * j));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-
-        issue_k();
-        issue_v();
+        if (dk) {
+            ++nk;
+            cursor_next(kc, B, first, seq_lens);
+        }
+        if (dv) {
+            ++nv;
+            cursor_next(vc, B, first, seq_lens);
+        }
         const bool last_of_pair = cc.t == cc.P - 1;
         if (last_of_pair || cc.g + 1 >= cc.hi) {
             if (seg_t0 == 0 && last_of_pair) {
