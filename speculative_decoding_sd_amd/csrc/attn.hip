@@ -189,7 +189,10 @@ __global__ void attn_validate_append(const int32_t* __restrict__ seq_lens,
 constexpr int kCombineRows = 64;
 constexpr int kCombineCache = 12288;  // split weights cached per block (48 KiB)
 
-// grid (kv head, request, 64-row block).
+// grid (kv head, request, 64-row block x dsplit): block z covers rows
+// 64 (z / dsplit) .. +63 and the head dims D/dsplit * (z % dsplit) .. of
+// them (the split gives small batches of long requests enough blocks; every
+// block computes its rows' weights itself).
 // mode 1 (MLA): slot k of request b is its key chunk k; requests whose keys
 //   fit one chunk were written by the attention kernel already.
 // mode 2 (GQA): n = min(nw, T) of the streaming kernel's nw waves split the
@@ -206,17 +209,19 @@ __global__ __launch_bounds__(256) void attn_combine(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     const int32_t* __restrict__ first, float* __restrict__ out, uint16_t* __restrict__ out_lowp,
-    int NQ, int Hq, int Hkv, int G, int R, int D, int chunk, int max_splits, int nw, int mode) {
+    int NQ, int Hq, int Hkv, int G, int R, int D, int chunk, int max_splits, int nw, int mode,
+    int dsplit) {
     __shared__ float s_m[kCombineRows], s_inv[kCombineRows];
     __shared__ float s_red[4][kCombineRows];
     __shared__ __attribute__((aligned(16))) float s_w[kCombineCache];
     const int kvh = blockIdx.x, b = blockIdx.y;
-    const int r0 = blockIdx.z * kCombineRows;
+    const int r0 = (blockIdx.z / dsplit) * kCombineRows;
+    const int Dc = D / dsplit, d0 = Dc * (blockIdx.z % dsplit);
     const int nr = min(kCombineRows, R - r0);
     if (nr <= 0) return;
     if (!valid[b]) {
-        for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-            const int row = r0 + idx % nr, d = idx / nr;
+        for (int idx = threadIdx.x; idx < nr * Dc; idx += blockDim.x) {
+            const int row = r0 + idx % nr, d = d0 + idx / nr;
             const int i = row / G, g = row - i * G;
             const size_t oi = (((size_t)b * NQ + i) * Hq + kvh * G + g) * D + d;
             out[oi] = NAN;
@@ -298,8 +303,8 @@ __global__ __launch_bounds__(256) void attn_combine(
         // Four consecutive rows per thread (16-byte loads), eight slots in
         // flight per step.
         const int nq = nr >> 2;
-        for (int idx = threadIdx.x; idx < nq * D; idx += blockDim.x) {
-            const int dl = idx / nq, lq = 4 * (idx - dl * nq);
+        for (int idx = threadIdx.x; idx < nq * Dc; idx += blockDim.x) {
+            const int dl = d0 + idx / nq, lq = 4 * (idx % nq);
             const float* po = part_o + (size_t)dl * R + r0 + lq;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             int k = 0;
@@ -319,9 +324,9 @@ __global__ __launch_bounds__(256) void attn_combine(
         }
         return;
     }
-    for (int idx = threadIdx.x; idx < nr * D; idx += blockDim.x) {
-        const int dl = idx / nr, lr = idx - dl * nr;
-        const int row = r0 + lr, d = dl;
+    for (int idx = threadIdx.x; idx < nr * Dc; idx += blockDim.x) {
+        const int lr = idx % nr;
+        const int row = r0 + lr, d = d0 + idx / nr;
         const float* po = part_o + (size_t)d * R + row;
         float acc = 0.f;
         for (int k = 0; k < np; ++k) {
@@ -336,6 +341,17 @@ __global__ __launch_bounds__(256) void attn_combine(
         }
         emit(row, d, acc);
     }
+}
+
+// Head-dim split of the combine: doubled while the blocks number fewer than
+// two per CU, keeping at least 32 dims per block.
+static int combine_dsplit(int blocks, int D, int* ds) {
+    int cus = 0;
+    const int rc = cu_count("sd_verify_attn", &cus);
+    if (rc != SD_OK) return rc;
+    *ds = 1;
+    while (D % (*ds * 2) == 0 && D / (*ds * 2) >= 32 && (long)blocks * *ds < 2L * cus) *ds *= 2;
+    return SD_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -608,10 +624,12 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
         if ((rc = mla_launch(d, valid, flags, po, pml, p.chunk, p.max_splits, scale, s)) != SD_OK)
             return rc;
         if (p.max_splits == 1) return SD_OK;
-        attn_combine<<<dim3(1, B, (p.R + kCombineRows - 1) / kCombineRows),
-                       256, 0, s>>>(
+        const int rblocks = (p.R + kCombineRows - 1) / kCombineRows;
+        int ds = 1;
+        if ((rc = combine_dsplit(B * rblocks, d->d_v, &ds)) != SD_OK) return rc;
+        attn_combine<<<dim3(1, B, rblocks * ds), 256, 0, s>>>(
             po, pml, d->seq_lens, valid, nullptr, d->out, (uint16_t*)d->out_lowp, NQ,
-            d->n_q_heads, 1, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0, 1);
+            d->n_q_heads, 1, p.G, p.R, d->d_v, p.chunk, p.max_splits, 0, 1, ds);
         return check_launch("attn_combine");
     }
     int32_t* first = (int32_t*)(ws + p.off_first);
@@ -619,10 +637,11 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     if ((rc = gqa_launch(d, valid, first, d->tree_parent ? anc : nullptr, po, pml, p.R,
                          p.max_waves, scale_log2, &nw, s)) != SD_OK)
         return rc;
-    attn_combine<<<dim3(d->n_kv_heads, B,
-                        (p.R + kCombineRows - 1) / kCombineRows),
-                   256, 0, s>>>(
+    const int rblocks = (p.R + kCombineRows - 1) / kCombineRows;
+    int ds = 1;
+    if ((rc = combine_dsplit(d->n_kv_heads * B * rblocks, d->d_v, &ds)) != SD_OK) return rc;
+    attn_combine<<<dim3(d->n_kv_heads, B, rblocks * ds), 256, 0, s>>>(
         po, pml, d->seq_lens, valid, first, d->out, (uint16_t*)d->out_lowp, NQ, d->n_q_heads,
-        d->n_kv_heads, p.G, p.R, d->d_v, 0, 0, nw, 2);
+        d->n_kv_heads, p.G, p.R, d->d_v, 0, 0, nw, 2, ds);
     return check_launch("attn_combine");
 }
