@@ -680,14 +680,11 @@ __global__ __launch_bounds__(256, (gqa_groups_per_cu<D, RB, F8>())) void attn_gq
 //     is key 8g + e), which is the k order of the P^T operand of O^T += V^T P^T;
 //   k-steps 2j and 2j+1 (j = 0, 1) of lane group g run over dims
 //     16(4j + g) .. +7 and +8 .. +15: one 16-byte read of a K row, Q following.
-// Swizzle (128-byte rows, row parity picks the bank half): the 16 rows of a
-// K read pass are 8q + 4kb + r (fixed bit 2) and those of a V read pass
-// (ds_read_b64_tr_b8, lane groups 2p and 2p+1) are 16p .. 16p+15 (fixed bit
-// 4); f = 4 b3 + 2 b1 + (b2 ^ b4) is a bijection on the 8 rows of one parity
-// in either pass.
-__device__ __forceinline__ int gqa16_xor(int row) {
-    return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | (((row >> 2) ^ (row >> 4)) & 1);
-}
+// Swizzle: the 32-row kernels' E4M3 one (gqa_xor<128, true>).  Measured
+// with SQ_LDS_BANK_CONFLICT on the two read patterns alone, it leaves both
+// free of bank conflicts, while two swizzles derived for K-read passes of 16
+// consecutive lanes (every lane group reads the same 16 rows at its own
+// chunk) conflicted on 40% of the K-read cycles.
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -738,7 +735,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
     for (int j = 0; j < T::kDmaHalf; ++j) {
         const int n = 64 * j + lane;
         const int row = n / T::kRowChunks;
-        goff[j] = row * T::kRowBytes + 16 * ((n % T::kRowChunks) ^ gqa16_xor(row));
+        goff[j] = row * T::kRowBytes + 16 * ((n % T::kRowChunks) ^ gqa_xor<D, true>(row));
     }
     const size_t head_bytes = (size_t)kPage * T::kRowBytes;
     char* const k_ring = ring;
@@ -765,14 +762,14 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
         const int key = 8 * (li >> 2) + 4 * kb + (li & 3);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            koff[kb][j] = key * T::kRowBytes + 16 * ((4 * j + lg) ^ gqa16_xor(key));
+            koff[kb][j] = key * T::kRowBytes + 16 * ((4 * j + lg) ^ gqa_xor<D, true>(key));
     }
     // V reads of dim block db (ds_read_b64_tr_b8: lane t of a 16-lane group
     // receives byte t%8 of the reads of lanes t/8 + 2e as byte e): lane li
     // reads key 8lg + li/2, dims 16db + 8(li&1) .. +7, so lane t receives dim
     // 16db + t of keys 8lg .. 8lg+7 in slot order.
     const int vkey = 8 * lg + (li >> 1);
-    const int vbase = vkey * T::kRowBytes + 8 * (li & 1), vx = gqa16_xor(vkey);
+    const int vbase = vkey * T::kRowBytes + 8 * (li & 1), vx = gqa_xor<D, true>(vkey);
 
     const int Th = first[B];
     const long n_tiles = (long)Th * Hkv;
@@ -935,7 +932,7 @@ __global__ __launch_bounds__(256, 2) void attn_gqa_f8_r16(
             const int nvk = cend - ks;
             for (int idx = lane; idx < (kTile - nvk) * T::kRowChunks; idx += 64) {
                 const int row = nvk + idx / T::kRowChunks, c = idx % T::kRowChunks;
-                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa16_xor(row))) =
+                *(u32x4*)(vtile + row * T::kRowBytes + 16 * (c ^ gqa_xor<D, true>(row))) =
                     u32x4{0, 0, 0, 0};
             }
         }
