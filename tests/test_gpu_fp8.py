@@ -172,13 +172,14 @@ def test_rollback_poison_e4m3_cache():
     assert np.array_equal(kc.cpu().numpy(), kch) and np.array_equal(vc.cpu().numpy(), vch)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
-def test_attention_ragged_batch_with_invalid_requests(kv):
+@pytest.mark.parametrize("kv,K", [("bf16", 3), ("e4m3", 3), ("e4m3", 9)])
+def test_attention_ragged_batch_with_invalid_requests(kv, K):
     """Many requests of mixed lengths (zero included), one with a bad page
     entry: the waves' equal tile ranges cut pairs at arbitrary tiles, and the
-    combine must find every pair's partials (and skip the invalid request)."""
+    combine must find every pair's partials (and skip the invalid request).
+    K = 9 gives 40 query rows per kv head (the 16-row-block E4M3 kernel)."""
     rng = np.random.default_rng(31)
-    B, K, Hq, Hkv, D = 37, 3, 16, 4, 128
+    B, Hq, Hkv, D = 37, 16, 4, 128
     lens = rng.integers(0, 3000, B)
     lens[[0, 5, 9]] = [0, 1, 2999]
     if kv == "e4m3":
@@ -199,7 +200,7 @@ def test_attention_ragged_batch_with_invalid_requests(kv):
     assert err & sdv.SD_DERR_PAGE
     assert np.isnan(o[bad]).all()
     keep = np.arange(B) != bad
-    check_attention(o[keep], ref[keep], where=f"ragged batch {kv}")
+    check_attention(o[keep], ref[keep], where=f"ragged batch {kv} K={K}")
 
 
 def _oracle_bf16(wl):
