@@ -166,7 +166,12 @@ int sd_get_device_error(const int32_t* dev_error, int32_t* code, void* stream);
  * rounded; ties to the even code; magnitudes above 448, infinities
  * included, saturate to 448; NaN -> 0x7F).  q, k_new, v_new, out_lowp stay
  * bf16.  The attention computes with the exact code values (every E4M3
- * value is a bf16 value) and applies the scales in float32.
+ * value is a bf16 and an fp16 value) and applies the scales in float32; the
+ * softmax weights meet the values rounded to fp16 (relative error at most
+ * 2^-11 per weight), so an output element may differ from exact arithmetic
+ * on the codes by up to 2^-11 of the weighted mean of |v| (measured: below
+ * 6e-4 of the row's largest output; the bf16 cache path is exact to about
+ * 1e-5).
  *
  * Supported: page_size 64; GQA bf16 (bf16 or E4M3 cache) with d_qk = d_v in
  * {64, 128} and (n_q_heads/n_kv_heads)*(K+1) <= 64; GQA f32 with d_qk = d_v
