@@ -228,3 +228,29 @@ def _run_gpu_bf16(wl):
     sdv.verify_attn(d)
     torch.cuda.synchronize()
     return out, int(err.item())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 4, 5, 6, 8])   # seeds with distinct (G, K)
+def test_attention_e4m3_random_16row_shapes(seed):
+    """Seeded random shapes with 33..48 query rows per kv head (the 16-row-
+    block kernel): group size, draft count, kv heads and ragged lengths
+    (zero, page edges and a long request) drawn per seed; every row against
+    the oracle, the appended cache bytes bit-exact."""
+    rng = np.random.default_rng(900 + seed)
+    while True:
+        G = int(rng.integers(2, 13))
+        K = int(rng.integers(0, 24))
+        if 32 < G * (K + 1) <= 48:
+            break
+    Hkv = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(2, 7))
+    lens = rng.integers(0, 1500, B)
+    lens[0] = int(rng.choice([0, 63, 64, 65]))
+    lens[-1] = int(rng.integers(3000, 6000))
+    wl = _case(B, K, G * Hkv, Hkv, 128, lens, seed=910 + seed)
+    out, _, kc, vc, err = _run_gpu(wl)
+    ref, kc_ref, vc_ref = _oracle(wl)
+    assert err == 0
+    check_attention(out.cpu().numpy(), ref,
+                    where=f"e4m3 16-row seed {seed}: G={G} K={K} Hkv={Hkv} lens={list(lens)}")
+    assert np.array_equal(kc.cpu().numpy(), kc_ref) and np.array_equal(vc.cpu().numpy(), vc_ref)
