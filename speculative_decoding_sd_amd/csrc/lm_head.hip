@@ -12,6 +12,8 @@
 // M tile fastest and handed out so that each XCD (own L2) gets a contiguous
 // run of tiles: the M tiles sharing one W tile run on the same XCD, which
 // reads that slice of W from HBM once.
+#include <algorithm>
+
 #include "sdv_device.h"
 #include "sdv_internal.h"
 
@@ -415,16 +417,21 @@ template <int TN, int TM, int WN, int WM, int NST>
 __global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_stream(const uint16_t* __restrict__ H,
                                                              const uint16_t* __restrict__ W,
                                                              uint16_t* __restrict__ C, int M,
-                                                             int N, int K) {
+                                                             int N, int K, int nw) {
     using T = StreamTile<TN, TM, WN, WM, NST>;
     constexpr int FN = T::FN, FM = T::FM, OPS = T::kOps;
     constexpr uint32_t SB = T::kStageBytes;
     constexpr int C1 = OPS / 4, C2 = OPS / 2, C3 = 3 * OPS / 4;
+    // Block (tm, tn) covers vocabulary rows [tn nw, min((tn + 1) nw, N)):
+    // nw <= TN (a multiple of 8) is chosen by the launcher so that the
+    // blocks fill whole rounds of the CUs; rows of the TN-row tile past that
+    // range re-read its last row and are never stored.
     const int tiles_m = (M + TM - 1) / TM;
-    const int tiles_n = (N + TN - 1) / TN;
+    const int tiles_n = (N + nw - 1) / nw;
     const int tile = xcd_tile(blockIdx.x, tiles_m * tiles_n);
     const int tm = tile % tiles_m, tn = tile / tiles_m;
-    const int n0 = tn * TN, m0 = tm * TM;
+    const int n0 = tn * nw, m0 = tm * TM;
+    const int n_end = min(n0 + nw, N);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wn = wave % WN, wm = wave / WN;
     const int ln = lane & 31, lh = lane >> 5;
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_stream(const uint16_t
     for (int i = 0; i < OPS; ++i) {
         const int g = (i * T::NW + wave) * 64 + lane;
         const int row = g / 8, c = (g % 8) ^ ((row >> 1) & 7);
-        src[i] = row < TN ? W + (size_t)min(n0 + row, N - 1) * K + 8 * c
+        src[i] = row < TN ? W + (size_t)min(n0 + row, n_end - 1) * K + 8 * c
                           : H + (size_t)min(m0 + row - TN, M - 1) * K + 8 * c;
     }
     // Prologue: slices 0 .. NST-2 whole, the first quarter of slice NST-1;
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_stream(const uint16_t
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * (TN / WN) + i * 32 + 8 * g + 4 * lh;
                 const f32x16& a = acc[i][j];
-                if (vec && n + 3 < N) {
+                if (vec && n + 3 < n_end) {
                     u32x2 w;
                     w.x = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
                     w.y = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void lm_head_stream(const uint16_t
                 } else {
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        if (n + t < N) crow[n + t] = (uint16_t)f32_to_bf16_rne(a[4 * g + t]);
+                        if (n + t < n_end) crow[n + t] = (uint16_t)f32_to_bf16_rne(a[4 * g + t]);
                 }
             }
         }
@@ -565,15 +572,26 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         // 192 tiles (all rows, twice the W tiles), larger ones 128-row tiles
         // (the W tile is then read by two workgroups of one XCD).
         int TM = M > 128 ? 256 : (M > 64 ? 128 : 64);
-        if (TM == 256) {
-            int num_cus = 0;
-            const int rc = cu_count("sd_lm_head", &num_cus);
-            if (rc != SD_OK) return rc;
-            if ((long)((M + 255) / 256) * ((vocab + 255) / 256) < num_cus)
-                TM = M <= 192 ? 192 : 128;
-        }
+        int num_cus = 0;
+        const int rc = cu_count("sd_lm_head", &num_cus);
+        if (rc != SD_OK) return rc;
+        if (TM == 256 && (long)((M + 255) / 256) * ((vocab + 255) / 256) < num_cus)
+            TM = M <= 192 ? 192 : 128;
         const int TN = TM == 192 ? 128 : 256;
-        const long tiles = (long)((M + TM - 1) / TM) * ((vocab + TN - 1) / TN);
+        const long tiles_m = (M + TM - 1) / TM;
+        long tiles = tiles_m * ((vocab + TN - 1) / TN);
+        // Streaming tiles (one workgroup per CU at a time): narrow the
+        // vocabulary range per block so that the blocks fill whole rounds of
+        // the CUs (a 64 x 5120 x 152064 head: 594 tiles of 256 rows are 2.3
+        // rounds, 761 blocks of 200 rows 3 rounds), keeping a multiple of 8.
+        int nw = TN;
+        if (TM != 256) {
+            const long rounds = (tiles + num_cus - 1) / num_cus;
+            const long per_m = (rounds * num_cus + tiles_m - 1) / tiles_m;
+            const long w = ((vocab + per_m - 1) / per_m + 7) / 8 * 8;
+            nw = (int)std::min<long>(TN, std::max<long>(8, w));
+            tiles = tiles_m * ((vocab + nw - 1) / nw);
+        }
         if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");
         const uint16_t* h = (const uint16_t*)H;
         const uint16_t* w = (const uint16_t*)W;
@@ -582,13 +600,13 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
             lm_head_ring<<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab, hidden);
         else if (TM == 192)
             lm_head_stream<128, 192, 2, 2, 4><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
-                                                                              hidden);
+                                                                              hidden, nw);
         else if (TM == 128)
             lm_head_stream<256, 128, 2, 2, 3><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
-                                                                              hidden);
+                                                                              hidden, nw);
         else
             lm_head_stream<256, 64, 4, 1, 4><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
-                                                                             hidden);
+                                                                             hidden, nw);
         return check_launch(TM == 256 ? "lm_head_ring" : "lm_head_stream");
     }
     const long tiles = (long)((M + kBM - 1) / kBM) * ((vocab + kBN - 1) / kBN);
