@@ -13,8 +13,9 @@
 // filled by LDS DMA (S K stages and S - 1 V stages, as many as the LDS holds
 // up to S = 5: 40 KiB per wave for bf16 at head dim 128), so that S - 1
 // tiles per wave are in flight while one is computed, also across pair
-// boundaries.  One 4-wave workgroup per CU (two for E4M3 with one row block).
-// Per tile and 32-row block:
+// boundaries.  One 4-wave workgroup per CU (two for E4M3 with one row block,
+// and for attn_gqa_f8_r16: E4M3 with 33..48 rows in three 16-row blocks).
+// Per tile and 32-row block (attn_gqa_stream):
 //   S^T = K Q^T    A = K rows from LDS (ds_read_b128; E4M3 bytes converted to
 //                  bf16 exactly), B = Q^T in registers;
 //   online softmax lane-local (one query row per lane column); the running
@@ -23,7 +24,8 @@
 //                  ds_read_b64_tr_b8 + conversion (E4M3) from the row-major V
 //                  tile; bf16 cache: P in bf16 hi + lo halves (two MFMAs);
 //                  E4M3 cache: V exact in fp16, P rounded to fp16 (one MFMA).
-// A wave's tiles of one pair form a segment, written once at its end: to the
+// The refill DMAs of a tile's stages go out between its V^T blocks.  A
+// wave's tiles of one pair form a segment, written once at its end: to the
 // output when it covers the whole pair, else as an unnormalised partial
 // (O^T, m, l) that attn_combine merges.
 #include <math.h>
