@@ -144,6 +144,11 @@ def parse():
                          "breadth-first order")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests timed through the CPU oracle (0: sized for about 15 s)")
+    ap.add_argument("--lm-operands", choices=("random", "equal"), default="random",
+                    help="diagnostic: 'equal' fills W and the LM-head input with one value "
+                         "each (the same kernel on low-entropy operands, to show how its "
+                         "clock depends on the data it switches; not a benchmark of the "
+                         "workload)")
     ap.add_argument("--flush", action="store_true",
                     help="read a 1 GiB scratch buffer before every timed step, so that "
                          "neither the L2 caches nor the 256 MB MALL hold the step's inputs "
@@ -385,7 +390,8 @@ def main():
         tree = sdsynth.tree_parents(args.tree, cfg.num_q)
     seed = sdsynth.config_seed(args.config)
     workload = (WORKLOAD_NAMES[args.config] + ("_e4m3" if cfg.kv_cache == "e4m3" else "") +
-                ("_tree" if tree is not None else ""))
+                ("_tree" if tree is not None else "") +
+                ("_equal_operands" if args.lm_operands == "equal" else ""))
     dev = torch.device("cuda", 0)
     extra = (args.warmup + (2 if args.graph else 1) * args.steps + 4) * cfg.num_q
     wl = sdsynth.make_workload(cfg, seed, device=dev, extra_tokens=extra)
@@ -395,6 +401,10 @@ def main():
         sample = gather_sample(cfg, wl, n_cpu)
         sample["tree_parent"] = tree
     t = wl.tensors
+    if args.lm_operands == "equal":
+        t["W"].fill_(0.02)
+        if "H" in t:
+            t["H"].fill_(1.0)
     L0 = wl.seq_lens.copy()
     seq_lens = torch.tensor(wl.seq_lens, device=dev)
     page_table = torch.tensor(wl.page_table, device=dev)
@@ -546,6 +556,7 @@ def main():
                    "vocab": cfg.vocab, "sampling": sampling_modes(cfg),
                    "top_p": cfg.top_p, "page_size": cfg.page_size,
                    "l2_mall_flush": bool(args.flush),
+                   "lm_operands": args.lm_operands,
                    "kv_cache": "e4m3" if cfg.kv_cache == "e4m3" else cfg.dtype,
                    "drafts": (f"{args.tree} tree of {cfg.num_q} nodes" if tree is not None
                               else f"chain of {cfg.K}")},
