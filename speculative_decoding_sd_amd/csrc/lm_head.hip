@@ -173,6 +173,8 @@ __device__ __forceinline__ void wait_frags(u32x4 (&a)[NA], u32x4 (&b)[NB]) {
     else if constexpr (NA == 2 && NB == 3)
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]));
+    else if constexpr (NA == 1 && NB == 3)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]));
     else
         static_assert(NA < 0, "unsupported fragment counts");
 }
@@ -350,7 +352,9 @@ __global__ __launch_bounds__(512, 1) void lm_head_ring(const uint16_t* __restric
 // 128- and 64-row tiles (small batches, where the LM head streams W from HBM):
 // a ring of NST whole stages (W and H k-slices of 64, (TN + TM) rows each)
 // in the same 160 KB of LDS, three stages of 48 KB for 256 x 128 and four of
-// 40 KB for 256 x 64, so NST - 1 stages are in flight while one computes.
+// 40 KB for 256 x 64 and 128 x 192, so NST - 1 stages are in flight while one
+// computes.  WN x WM waves (the 128 x 192 tile: eight of 32 x 96, two per
+// SIMD, 3-5% faster than four of 64 x 96 on 129-192-row batches).
 // The refill of the stage buffer freed at a barrier is spread over the four
 // k-steps that follow it, a quarter of the ops per step, each interleaved with
 // the MFMAs and the next step's fragment reads.  Barrier B_kt at the start of
@@ -599,7 +603,7 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         if (TM == 256)
             lm_head_ring<<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab, hidden);
         else if (TM == 192)
-            lm_head_stream<128, 192, 2, 2, 4><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
+            lm_head_stream<128, 192, 4, 2, 4><<<(unsigned)tiles, 512, 0, s>>>(h, w, c, M, vocab,
                                                                               hidden, nw);
         else if (TM == 128)
             lm_head_stream<256, 128, 2, 2, 3><<<(unsigned)tiles, 256, 0, s>>>(h, w, c, M, vocab,
