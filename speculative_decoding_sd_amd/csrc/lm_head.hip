@@ -587,13 +587,15 @@ extern "C" int sd_lm_head(int M, int hidden, int vocab, int dtype, const void* H
         // Streaming tiles (one workgroup per CU at a time): narrow the
         // vocabulary range per block so that the blocks fill whole rounds of
         // the CUs (a 64 x 5120 x 152064 head: 594 tiles of 256 rows are 2.3
-        // rounds, 761 blocks of 200 rows 3 rounds), keeping a multiple of 8.
+        // rounds, 761 blocks of 200 rows 3 rounds), keeping a multiple of 8
+        // and at least half the tile: every block streams all of its M tile's
+        // H rows, so narrower blocks would multiply those reads.
         int nw = TN;
         if (TM != 256) {
             const long rounds = (tiles + num_cus - 1) / num_cus;
             const long per_m = (rounds * num_cus + tiles_m - 1) / tiles_m;
             const long w = ((vocab + per_m - 1) / per_m + 7) / 8 * 8;
-            nw = (int)std::min<long>(TN, std::max<long>(8, w));
+            nw = (int)std::min<long>(TN, std::max<long>(TN / 2, w));
             tiles = tiles_m * ((vocab + nw - 1) / nw);
         }
         if (tiles > 0x7fffffffL) return fail(SD_EUNSUPPORTED, "sd_lm_head: too many tiles");
