@@ -48,14 +48,19 @@ KERNEL_SOURCES = {"lm_head_stream": "lm_head.hip", "lm_head_ring": "lm_head.hip"
 
 
 def kernel_source_hash(kernel):
+    """SHA-256 over the kernel's source file, the shared device headers and
+    the hipcc flags that file is compiled with."""
     import hashlib
+    from speculative_decoding_sd_amd import build as sdv_build
     h = hashlib.sha256()
+    src = KERNEL_SOURCES[kernel]
     csrc = os.path.join(ROOT, "speculative_decoding_sd_amd", "csrc")
-    for f in (os.path.join(csrc, KERNEL_SOURCES[kernel]), os.path.join(csrc, "sdv_device.h"),
-              os.path.join(csrc, "sdv_lds.h"), os.path.join(csrc, "sdv_internal.h"),
-              os.path.join(ROOT, "speculative_decoding_sd_amd", "build.py")):
+    for f in (os.path.join(csrc, src), os.path.join(csrc, "sdv_device.h"),
+              os.path.join(csrc, "sdv_lds.h"), os.path.join(csrc, "sdv_internal.h")):
         with open(f, "rb") as fh:
             h.update(fh.read())
+    flags = sdv_build.HIPCC_FLAGS + sdv_build.EXTRA_FLAGS.get(src, [])
+    h.update(" ".join(f for f in flags if not os.path.isabs(f)).encode())
     return h.hexdigest()
 
 
@@ -149,6 +154,10 @@ def parse():
                          "each (the same kernel on low-entropy operands, to show how its "
                          "clock depends on the data it switches; not a benchmark of the "
                          "workload)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="diagnostic: time the register-operand bf16 MFMA probe "
+                         "(csrc/probe_mfma.hip) with random and with equal operands and "
+                         "print its rates instead of running the verify step")
     ap.add_argument("--flush", action="store_true",
                     help="read a 1 GiB scratch buffer before every timed step, so that "
                          "neither the L2 caches nor the 256 MB MALL hold the step's inputs "
@@ -360,8 +369,64 @@ def cpu_sample_size(cfg, seq_lens, budget_s=15.0):
     return n
 
 
+def mfma_ceiling(warmup, steps):
+    """The sustained bf16 MFMA rate of the device when only the matrix pipes
+    work (csrc/probe_mfma.hip: register-resident operands, the LM head's MFMA
+    order, eight waves per CU), once with random operands and once with
+    equal ones.  The gap between the two is the clock the chip gives up to
+    its power limit on random data; the random-operand rate is the ceiling
+    any bf16 GEMM on random data meets on this device."""
+    import ctypes
+    import torch
+    from speculative_decoding_sd_amd import build as sdv_build
+
+    L = ctypes.CDLL(sdv_build.PROBE_LIB_PATH)
+    L.sdv_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    flops = blocks * 8 * iters * 16 * 32768.0
+    n = 12 * 512 * 8  # bf16 operand values: 12 fragments x 512 threads x 8
+    gen = torch.Generator().manual_seed(7)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {"metric": "bf16 MFMA rate, register-resident operands", "unit": "TFLOP/s",
+           "peak": MFMA_BF16_PEAK_TFS, "blocks": blocks, "waves_per_cu": 8,
+           "mfma_per_launch": blocks * 8 * iters * 16, "steps": steps}
+    for name, host in (("random", torch.randn(n, generator=gen).to(torch.bfloat16)),
+                       ("equal", torch.full((n,), 1.0, dtype=torch.bfloat16))):
+        ops = host.to("cuda")
+
+        def launch():
+            rc = L.sdv_probe_mfma_bf16(ops.data_ptr(), ops.numel() * 2, sink.data_ptr(),
+                                       sink.numel(), blocks, iters, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("sdv_probe_mfma_bf16 failed")
+
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = sorted(ms)[len(ms) // 2]
+        out[f"{name}_operands"] = {"tflops": flops / (t * 1e-3) / 1e12, "ms_per_launch": t,
+                                   "frac_of_peak": flops / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.mfma_ceiling:
+        import torch  # noqa: F401 (initialises the device for the probe)
+        mfma_ceiling(args.warmup, args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "the verify-step benchmark runs on one GPU only; the "
                                    "kernels shard by request, kv head or vocabulary, but "

@@ -1,4 +1,5 @@
-"""Builds libsdv.so (the gfx950 verify-step library) in-tree with hipcc."""
+"""Builds libsdv.so (the gfx950 verify-step library) and libsdv_probe.so (a
+measurement probe that bench.py alone loads) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libsdv.so")
 SOURCES = ["sdv_abi.cpp", "attn.hip", "attn_gqa.hip", "attn_mla.hip", "lm_head.hip", "accept.hip", "rollback.hip"]
+PROBE_LIB_PATH = os.path.join(HERE, "libsdv_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 ARCH = "gfx950"
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops keeps the compiler from
@@ -44,12 +47,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = _hipcc()
     procs = []
     objs = []
-    for src in SOURCES:
+    probe_objs = []
+    for src in SOURCES + PROBE_SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
         obj = os.path.join(BUILD_DIR, src + ".o")
-        objs.append(obj)
+        (probe_objs if src in PROBE_SOURCES else objs).append(obj)
         cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -69,12 +73,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             print(msg)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    for lib_path, lib_objs in ((LIB_PATH, objs), (PROBE_LIB_PATH, probe_objs)):
+        tmp = lib_path + ".tmp"
+        cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *lib_objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib_path)
     return LIB_PATH
 
 

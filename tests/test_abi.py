@@ -206,3 +206,22 @@ def test_noalloc_accept_rejects_batches_beyond_its_scratch():
     with pytest.raises(sdv.SdvError) as e:      # pointers are checked first
         sdv.sd_accept_noalloc(d, 0)
     assert e.value.code == sdv.SD_EINVAL
+
+
+def test_probe_library_rejects_bad_arguments():
+    """The measurement probe bench.py --mfma-ceiling loads is built beside the
+    library and checks its sizes on the host before launching."""
+    from speculative_decoding_sd_amd import build as sdv_build
+    assert os.path.exists(sdv_build.PROBE_LIB_PATH), "run build() first"
+    P = ctypes.CDLL(sdv_build.PROBE_LIB_PATH)
+    f = P.sdv_probe_mfma_bf16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    buf = ctypes.create_string_buffer(16)
+    ok_ops, ok_sink = 12 * 512 * 16, 512
+    assert f(None, ok_ops, buf, ok_sink, 1, 1, None) == -1            # no operands
+    assert f(buf, ok_ops, None, ok_sink, 1, 1, None) == -1            # no sink
+    assert f(buf, ok_ops - 16, buf, ok_sink, 1, 1, None) == -1        # operands too small
+    assert f(buf, ok_ops, buf, ok_sink - 1, 1, 1, None) == -1         # sink too small
+    assert f(buf, ok_ops, buf, ok_sink, 0, 1, None) == -1             # no blocks
+    assert f(buf, ok_ops, buf, ok_sink, 1, 0, None) == -1             # no iterations
