@@ -44,7 +44,7 @@ WORKLOAD_NAMES = {1: "c1_tiny_fp32", 2: "c2_gqa_stochastic", 3: "c3_mla_greedy",
 # Source files whose contents a kernel's PMC traffic figure is tied to.
 KERNEL_SOURCES = {"lm_head_stream": "lm_head.hip", "lm_head_ring": "lm_head.hip",
                   "attn_gqa_stream": "attn_gqa.hip", "attn_gqa_f8_r16": "attn_gqa.hip",
-                  "attn_mla_bf16": "attn_mla.hip"}
+                  "attn_mla_bf16": "attn_mla.hip", "probe_mfma_bf16": "probe_mfma.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -126,6 +126,16 @@ def profiled_counters(kernel, workload):
     try:
         return {"mfma_busy": float(f["mfma_busy"]), "clock_ghz": float(f["clock_ghz"]),
                 "source": f"profiles/{kernel}_{workload}.md"}
+    except (KeyError, ValueError):
+        return None
+
+
+def mfma_ceiling_on_record():
+    """The register-operand bf16 MFMA rate on random operands from the
+    committed probe summary (bench.py --mfma-ceiling), TFLOP/s, or None."""
+    f = profiled_fields("probe_mfma_bf16", "register_operands")
+    try:
+        return float(f["ceiling_random_tflops"])
     except (KeyError, ValueError):
         return None
 
@@ -605,6 +615,13 @@ def main():
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],
             "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": traffic,
             "counters": counters}
+    ceiling = mfma_ceiling_on_record() if roof["bound"] == "mfma" else None
+    if ceiling is not None:
+        roof["power_ceiling"] = {
+            "achieved_frac": roof["achieved"] / ceiling, "tflops": ceiling,
+            "what": "bf16 MFMA rate with register-resident random operands on this device "
+                    "(no memory traffic; the chip's clock under its power limit)",
+            "source": "profiles/probe_mfma_bf16_register_operands.md"}
     line = {
         "metric": "verified positions/sec", "value": pos_per_s, "unit": "positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,

@@ -90,3 +90,23 @@ def test_multi_gpu_run_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_committed_profiles_match_the_sources():
+    """Every committed PMC summary with machine-readable lines still hashes
+    to its kernel's sources and flags (else bench.py would report null
+    traffic), and the MFMA ceiling probe's figure is on record."""
+    import glob
+    import os
+    n = 0
+    for path in glob.glob(os.path.join(bench.ROOT, "profiles", "*.md")):
+        name = os.path.basename(path)[:-3]
+        if "source_sha256: " not in open(path).read():
+            continue  # a summary without machine-readable lines (not read by bench.py)
+        for kernel in bench.KERNEL_SOURCES:
+            if name.startswith(kernel + "_"):
+                fields = bench.profiled_fields(kernel, name[len(kernel) + 1:])
+                assert fields, f"{name}: source hash is stale"
+                n += 1
+    assert n >= 10
+    assert 1000.0 < bench.mfma_ceiling_on_record() < bench.MFMA_BF16_PEAK_TFS
