@@ -356,24 +356,42 @@ static int combine_dsplit(int blocks, int D, int* ds) {
 
 // ---------------------------------------------------------------------------
 // Plain fp32 verify attention: one block per (position i, query head h,
-// request).  Keys in tiles of 256 (one score per thread); thread t
-// accumulates output element t % D over keys k of the tile with
-// k % (256 / D) == t / D.  Used for float32 caches (small problems).
+// request), 256 threads.  Keys in tiles of 256 (one score per thread, the
+// key row read VW floats at a time); the tile's max and sum by wave
+// reductions and one exchange of the four waves' results.  Values: D / VW
+// threads cover one value row (VW dims each), so 256 VW / D groups of
+// threads take keys k % groups = group, every load of a thread's keys in
+// flight at once (up to 16); the groups' partial sums are added in group
+// order at the end.  Used for float32 caches (small problems, latency-bound).
 // ---------------------------------------------------------------------------
+template <int VW>
 __global__ __launch_bounds__(256) void attn_f32_rows(
     const float* __restrict__ q, const float* __restrict__ k_cache,
     const float* __restrict__ v_cache, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ valid,
     float* __restrict__ out, float* __restrict__ out_lowp, int NQ, int Hq, int Hkv, int D,
     int max_pages, float scale, const uint64_t* __restrict__ anc) {
+    typedef float vec_t __attribute__((ext_vector_type(VW)));
+    constexpr int kMaxLoads = 16;  // value loads in flight per thread
     __shared__ float s_q[256];
     __shared__ float s_e[256];
-    __shared__ float s_red[256];
+    __shared__ float s_red[256 * VW];
+    __shared__ float s_w[2][4];
     __shared__ int s_pg[256 / kPage];  // the tile's physical pages
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const size_t oi = (((size_t)b * NQ + i) * Hq + h) * D;
-    if (!valid[b]) {
+    // The request's scalars, its query element and its first page-table
+    // entries are all loaded before any of them is waited for (D <= 256).
+    const int ok = valid[b];
+    const int L = seq_lens[b];
+    const uint64_t vis = anc ? anc[(size_t)b * NQ + i] : ~0ull;  // new keys visible to node i
+    const float qv = tid < D ? q[oi + tid] : 0.f;
+    const int n = L + i + 1;
+    int pg0 = 0;
+    if (ok && tid < 256 / kPage && kPage * tid < n)
+        pg0 = page_table[(size_t)b * max_pages + tid];
+    if (!ok) {
         for (int d = tid; d < D; d += blockDim.x) {
             out[oi + d] = NAN;
             if (out_lowp) out_lowp[oi + d] = NAN;
@@ -382,68 +400,80 @@ __global__ __launch_bounds__(256) void attn_f32_rows(
     }
     const int G = Hq / Hkv;
     const int kvh = h / G;
-    const int L = seq_lens[b];
-    const int n = L + i + 1;
-    const uint64_t vis = anc ? anc[(size_t)b * NQ + i] : ~0ull;  // new keys visible to node i
-    for (int d = tid; d < D; d += blockDim.x) s_q[d] = q[oi + d];
-    __syncthreads();
-    const int NG = 256 / D;
-    const int dd = tid % D, grp = tid / D;
-    float m = -INFINITY, l = 0.f, acc = 0.f;
+    if (tid < D) s_q[tid] = qv;
+    const int row_lanes = D / VW;   // threads per value row
+    const int NG = 256 / row_lanes;  // key groups
+    const int dv = (tid % row_lanes) * VW, grp = tid / row_lanes;
+    float m = -INFINITY, l = 0.f;
+    vec_t acc = {};
     for (int t0 = 0; t0 < n; t0 += 256) {
         // The tile's page-table entries, read once (they are the only
         // dependent loads in front of the key and value reads).
         if (tid < 256 / kPage && t0 + kPage * tid < n)
-            s_pg[tid] = page_table[(size_t)b * max_pages + t0 / kPage + tid];
+            s_pg[tid] = t0 == 0 ? pg0 : page_table[(size_t)b * max_pages + t0 / kPage + tid];
         __syncthreads();
         const int p = t0 + tid;
         float s = -INFINITY;
         if (p < n && (p < L || ((vis >> (p - L)) & 1ull))) {
             const int pg = s_pg[tid / kPage];
             const float* kp = k_cache + (((size_t)pg * Hkv + kvh) * kPage + p % kPage) * D;
+            // The row in batches of 16 vector loads, all in flight before the
+            // products (summed over the dims in order).
             float dot = 0.f;
-            for (int d = 0; d < D; ++d) dot += s_q[d] * kp[d];
+            for (int d0 = 0; d0 < D; d0 += 16 * VW) {
+                vec_t kv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (d0 + u * VW < D) kv[u] = *(const vec_t*)(kp + d0 + u * VW);
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (d0 + u * VW < D)
+#pragma unroll
+                        for (int e = 0; e < VW; ++e) dot += s_q[d0 + u * VW + e] * kv[u][e];
+            }
             s = dot * scale;
         }
-        s_red[tid] = s;
+        float wm = s;
+#pragma unroll
+        for (int mk = 32; mk >= 1; mk >>= 1) wm = fmaxf(wm, shfl_xor(wm, mk));
+        if ((tid & 63) == 0) s_w[0][wave] = wm;
         __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-            __syncthreads();
-        }
-        const float mnew = fmaxf(m, s_red[0]);
+        const float tmax = fmaxf(fmaxf(s_w[0][0], s_w[0][1]), fmaxf(s_w[0][2], s_w[0][3]));
+        const float mnew = fmaxf(m, tmax);
         const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
         const float e = (s != -INFINITY) ? expf(s - mnew) : 0.f;
-        __syncthreads();
         s_e[tid] = e;
-        s_red[tid] = e;
+        float ws = e;
+#pragma unroll
+        for (int mk = 32; mk >= 1; mk >>= 1) ws += shfl_xor(ws, mk);
+        if ((tid & 63) == 0) s_w[1][wave] = ws;
         __syncthreads();
-        for (int w = 128; w > 0; w >>= 1) {
-            if (tid < w) s_red[tid] += s_red[tid + w];
-            __syncthreads();
-        }
-        l = l * alpha + s_red[0];
+        l = l * alpha + (((s_w[1][0] + s_w[1][1]) + s_w[1][2]) + s_w[1][3]);
         m = mnew;
         acc *= alpha;
-        // Values of the tile's keys, eight loads in flight; the sum runs over
-        // the keys in order.
+        // Values of this thread's keys (k = grp, grp + NG, ...), all loads of a
+        // batch in flight, then summed over the keys in order.
         const int cnt = min(256, n - t0);
-        int k = grp;
-        for (; k + 7 * NG < cnt; k += 8 * NG) {
-            float v[8];
+        for (int k0 = grp; k0 < cnt; k0 += kMaxLoads * NG) {
+            vec_t v[kMaxLoads];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int kk = k + u * NG;
-                v[u] = v_cache[(((size_t)s_pg[kk / kPage] * Hkv + kvh) * kPage + kk % kPage) * D + dd];
+            for (int u = 0; u < kMaxLoads; ++u) {
+                const int kk = k0 + u * NG;
+                if (kk < cnt)
+                    v[u] = *(const vec_t*)(v_cache +
+                                           (((size_t)s_pg[kk / kPage] * Hkv + kvh) * kPage +
+                                            kk % kPage) * D + dv);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc += s_e[k + u * NG] * v[u];
+            for (int u = 0; u < kMaxLoads; ++u) {
+                const int kk = k0 + u * NG;
+                if (kk < cnt) acc += s_e[kk] * v[u];
+            }
         }
-        for (; k < cnt; k += NG)
-            acc += s_e[k] * v_cache[(((size_t)s_pg[k / kPage] * Hkv + kvh) * kPage + k % kPage) * D + dd];
         __syncthreads();
     }
-    s_red[tid] = acc;
+#pragma unroll
+    for (int u = 0; u < VW; ++u) s_red[grp * D + dv + u] = acc[u];
     __syncthreads();
     if (tid < D) {
         float sum = 0.f;
@@ -610,10 +640,20 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {
-        attn_f32_rows<<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
-            (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
-            d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ, d->n_q_heads,
-            d->n_kv_heads, d->d_qk, d->max_pages, scale, d->tree_parent ? anc : nullptr);
+        // Rows of a head dim divisible by 4 are read 16 bytes at a time (the
+        // caches are 16-byte aligned).
+        if (d->d_qk % 4 == 0)
+            attn_f32_rows<4><<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
+                (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
+                d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ,
+                d->n_q_heads, d->n_kv_heads, d->d_qk, d->max_pages, scale,
+                d->tree_parent ? anc : nullptr);
+        else
+            attn_f32_rows<1><<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
+                (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
+                d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ,
+                d->n_q_heads, d->n_kv_heads, d->d_qk, d->max_pages, scale,
+                d->tree_parent ? anc : nullptr);
         return check_launch("attn_f32_rows");
     }
     float* po = (float*)(ws + p.off_po);
