@@ -44,7 +44,8 @@ WORKLOAD_NAMES = {1: "c1_tiny_fp32", 2: "c2_gqa_stochastic", 3: "c3_mla_greedy",
 # Source files whose contents a kernel's PMC traffic figure is tied to.
 KERNEL_SOURCES = {"lm_head_stream": "lm_head.hip", "lm_head_ring": "lm_head.hip",
                   "attn_gqa_stream": "attn_gqa.hip", "attn_gqa_f8_r16": "attn_gqa.hip",
-                  "attn_mla_bf16": "attn_mla.hip", "probe_mfma_bf16": "probe_mfma.hip"}
+                  "attn_mla_bf16": "attn_mla.hip", "probe_mfma_bf16": "probe_mfma.hip",
+                  "probe_hbm_read": "probe_hbm.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -140,6 +141,16 @@ def mfma_ceiling_on_record():
         return None
 
 
+def hbm_ceiling_on_record():
+    """The streaming read bandwidth of the committed probe summary (bench.py
+    --hbm-ceiling), GB/s, or None."""
+    f = profiled_fields("probe_hbm_read", "streaming")
+    try:
+        return float(f["ceiling_read_gbs"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +179,10 @@ def parse():
                     help="diagnostic: time the register-operand bf16 MFMA probe "
                          "(csrc/probe_mfma.hip) with random and with equal operands and "
                          "print its rates instead of running the verify step")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="diagnostic: time the streaming HBM read probe "
+                         "(csrc/probe_hbm.hip) over a 4 GiB buffer and print its bandwidth "
+                         "instead of running the verify step")
     ap.add_argument("--flush", action="store_true",
                     help="read a 1 GiB scratch buffer before every timed step, so that "
                          "neither the L2 caches nor the 256 MB MALL hold the step's inputs "
@@ -431,8 +446,62 @@ def mfma_ceiling(warmup, steps):
     print(json.dumps(out), flush=True)
 
 
+def hbm_ceiling(warmup, steps):
+    """The read bandwidth a plain streaming kernel sustains from HBM
+    (csrc/probe_hbm.hip: contiguous 32 KB tiles per workgroup, eight 16-byte
+    loads in flight per thread, over a 4 GiB buffer that no cache holds), for
+    three grid sizes;
+    the best is the practical ceiling of the HBM-bound calls."""
+    import ctypes
+    import torch
+    from speculative_decoding_sd_amd import build as sdv_build
+
+    L = ctypes.CDLL(sdv_build.PROBE_LIB_PATH)
+    L.sdv_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_bytes = 4 << 30
+    buf = torch.ones(n_bytes // 4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {"metric": "HBM read bandwidth, streaming kernel", "unit": "GB/s",
+           "peak": HBM_PEAK_GBS, "bytes_per_launch": n_bytes, "steps": steps, "grids": {}}
+    best = 0.0
+    for per_cu in (8, 32, 64):
+        blocks = cus * per_cu
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+        def launch():
+            rc = L.sdv_probe_hbm_read(buf.data_ptr(), n_bytes, sink.data_ptr(), sink.numel(),
+                                      blocks, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("sdv_probe_hbm_read failed")
+
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = sorted(ms)[len(ms) // 2]
+        gbs = n_bytes / (t * 1e-3) / 1e9
+        out["grids"][f"{blocks} blocks"] = {"ms_per_launch": t, "gbs": gbs}
+        best = max(best, gbs)
+    out["best_gbs"] = best
+    out["best_frac_of_peak"] = best / HBM_PEAK_GBS
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.hbm_ceiling:
+        import torch  # noqa: F401 (initialises the device for the probe)
+        hbm_ceiling(args.warmup, args.steps)
+        return
     if args.mfma_ceiling:
         import torch  # noqa: F401 (initialises the device for the probe)
         mfma_ceiling(args.warmup, args.steps)
@@ -615,6 +684,13 @@ def main():
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": roof["achieved"],
             "peak": roof["peak"], "unit": roof["unit"], "frac": roof["frac"], "traffic": traffic,
             "counters": counters}
+    hbm_ceil = hbm_ceiling_on_record() if roof["bound"] == "hbm" else None
+    if hbm_ceil is not None:
+        roof["hbm_ceiling"] = {
+            "achieved_frac": roof["achieved"] / hbm_ceil, "gbs": hbm_ceil,
+            "what": "read bandwidth of a plain streaming kernel over a 4 GiB buffer on this "
+                    "device",
+            "source": "profiles/probe_hbm_read_streaming.md"}
     ceiling = mfma_ceiling_on_record() if roof["bound"] == "mfma" else None
     if ceiling is not None:
         roof["power_ceiling"] = {

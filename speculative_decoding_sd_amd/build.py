@@ -12,7 +12,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libsdv.so")
 SOURCES = ["sdv_abi.cpp", "attn.hip", "attn_gqa.hip", "attn_mla.hip", "lm_head.hip", "accept.hip", "rollback.hip"]
 PROBE_LIB_PATH = os.path.join(HERE, "libsdv_probe.so")
-PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_SOURCES = ["probe_mfma.hip", "probe_hbm.hip"]
 ARCH = "gfx950"
 
 # -Xclang -target-feature -Xclang -packed-fp32-ops keeps the compiler from

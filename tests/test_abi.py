@@ -225,3 +225,20 @@ def test_probe_library_rejects_bad_arguments():
     assert f(buf, ok_ops, buf, ok_sink - 1, 1, 1, None) == -1         # sink too small
     assert f(buf, ok_ops, buf, ok_sink, 0, 1, None) == -1             # no blocks
     assert f(buf, ok_ops, buf, ok_sink, 1, 0, None) == -1             # no iterations
+
+
+def test_hbm_probe_rejects_bad_arguments():
+    """The streaming-read probe bench.py --hbm-ceiling loads checks its sizes
+    on the host before launching."""
+    from speculative_decoding_sd_amd import build as sdv_build
+    P = ctypes.CDLL(sdv_build.PROBE_LIB_PATH)
+    f = P.sdv_probe_hbm_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_int, ctypes.c_void_p]
+    buf = ctypes.create_string_buffer(16)
+    assert f(None, 1 << 20, buf, 256, 1, None) == -1       # no source
+    assert f(buf, 1 << 20, None, 256, 1, None) == -1       # no sink
+    assert f(buf, 0, buf, 256, 1, None) == -1              # nothing to read
+    assert f(buf, (1 << 20) + 8, buf, 256, 1, None) == -1  # not whole 16-byte words
+    assert f(buf, 1 << 20, buf, 255, 1, None) == -1        # sink too small
+    assert f(buf, 1 << 20, buf, 256, 0, None) == -1        # no blocks

@@ -110,3 +110,4 @@ def test_committed_profiles_match_the_sources():
                 n += 1
     assert n >= 10
     assert 1000.0 < bench.mfma_ceiling_on_record() < bench.MFMA_BF16_PEAK_TFS
+    assert 3000.0 < bench.hbm_ceiling_on_record() < bench.HBM_PEAK_GBS
