@@ -357,7 +357,8 @@ static int combine_dsplit(int blocks, int D, int* ds) {
 // ---------------------------------------------------------------------------
 // Plain fp32 verify attention: one block per (position i, query head h,
 // request), 256 threads.  Keys in tiles of 256 (one score per thread, the
-// key row read VW floats at a time); the tile's max and sum by wave
+// key row read VW floats at a time: head rows are whole 16-byte units, so
+// VW = 4); the tile's max and sum by wave
 // reductions and one exchange of the four waves' results.  Values: D / VW
 // threads cover one value row (VW dims each), so 256 VW / D groups of
 // threads take keys k % groups = group, every load of a thread's keys in
@@ -640,20 +641,12 @@ extern "C" int sd_verify_attn(const sd_attn_desc* d, void* workspace, size_t ws_
     if ((rc = check_launch("attn_validate_append")) != SD_OK) return rc;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->d_qk);
     if (p.path == 1) {
-        // Rows of a head dim divisible by 4 are read 16 bytes at a time (the
-        // caches are 16-byte aligned).
-        if (d->d_qk % 4 == 0)
-            attn_f32_rows<4><<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
-                (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
-                d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ,
-                d->n_q_heads, d->n_kv_heads, d->d_qk, d->max_pages, scale,
-                d->tree_parent ? anc : nullptr);
-        else
-            attn_f32_rows<1><<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
-                (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
-                d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ,
-                d->n_q_heads, d->n_kv_heads, d->d_qk, d->max_pages, scale,
-                d->tree_parent ? anc : nullptr);
+        // Head rows are whole 16-byte units (checked above) in 16-byte aligned
+        // caches: rows are read four floats at a time.
+        attn_f32_rows<4><<<dim3(NQ, d->n_q_heads, B), 256, 0, s>>>(
+            (const float*)d->q, (const float*)d->k_cache, (const float*)d->v_cache,
+            d->page_table, d->seq_lens, valid, d->out, (float*)d->out_lowp, NQ, d->n_q_heads,
+            d->n_kv_heads, d->d_qk, d->max_pages, scale, d->tree_parent ? anc : nullptr);
         return check_launch("attn_f32_rows");
     }
     float* po = (float*)(ws + p.off_po);

@@ -108,6 +108,24 @@ def test_attention_f32_tiny_config():
     assert np.array_equal(lowp.cpu().numpy().reshape(out.shape), out.cpu().numpy())
 
 
+@pytest.mark.parametrize("B,K,Hq,Hkv,D,lens", [
+    (2, 3, 4, 2, 128, [300, 700]),   # several 256-key tiles, later tiles' page entries
+    (3, 2, 2, 1, 256, [0, 255, 513]),  # widest head dim (4 threads per value row), tile edges
+    (2, 4, 8, 4, 16, [40, 260]),     # 64 key groups of the value pass
+    (2, 1, 2, 2, 4, [3, 290]),       # head dim 4: one thread per value row, 256 groups
+])
+def test_attention_f32_shapes(B, K, Hq, Hkv, D, lens):
+    """The float32 path at head dims 4..256 (rows of whole 16-byte units) and
+    lengths spanning several 256-key tiles."""
+    wl = _gqa_case(B, K, Hq, Hkv, D, lens, "f32", seed=70 + D)
+    out, lowp, kc, vc, err = _run_gpu_attention(wl)
+    ref, kc_ref, vc_ref = _oracle_attention(wl)
+    assert err == 0
+    rel = check_attention(out.cpu().numpy(), ref, where=f"f32 D={D}")
+    assert rel < 1e-5
+    assert np.array_equal(kc.cpu().numpy(), kc_ref) and np.array_equal(vc.cpu().numpy(), vc_ref)
+
+
 def test_attention_preappended_cache():
     """k_new = NULL: the cache already holds the step's positions."""
     wl = _gqa_case(2, 3, 8, 2, 128, [100, 300], "bf16", seed=5)
