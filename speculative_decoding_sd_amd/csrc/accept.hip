@@ -1334,11 +1334,16 @@ __global__ __launch_bounds__(1024) void accept_pack(const int32_t* __restrict__ 
     for (int k = total + tid; k < B * Q; k += blockDim.x) packed[k] = -1;
 }
 
-// Slices per row for the row statistics: enough blocks to fill the chip
-// (about 2048 of 256 threads), slices of at least 2048 ids, at most 32.
-// span is a multiple of 8 ids so every slice starts on a 16-byte vector.
+// Slices per row for the row statistics: slices of at least 2048 ids, at
+// most 32 per row.  span is a multiple of 8 ids so every slice starts on a
+// 16-byte vector.
 void row_split(int rows, int V, int* splits, int* span) {
-    int sp = (2048 + rows - 1) / rows;
+    // About 1024 blocks in all (measured: 1152 blocks of 5336 ids beat 2112
+    // of 2912 at 192 x 32000, 1024 beat 2048 at 256 x 129280), but at least
+    // two slices per row of a long vocabulary (2560 blocks beat 1280 at
+    // 1280 x 129280).
+    int sp = (1024 + rows - 1) / rows;
+    if (V >= 65536) sp = std::max(sp, 2);
     sp = std::min(sp, std::max(1, V / 2048));
     sp = std::max(1, std::min(sp, 32));
     int sn = (V + sp - 1) / sp;
