@@ -14,11 +14,15 @@ on a bounded sample of the same workload on the host cores.
 Workloads (--config): 1 tiny fp32 greedy, 2 GQA bf16 sampling, 3 MLA-shaped
 greedy, 4 long-context top-p, 5 ragged paged serving batch (default; the
 largest configuration and the one the attention/LM-head roofline targets are
-stated on).  The draft
-model is out of scope: drafts are synthesised from the step's own target
-logits the way the workload recipe states (greedy requests copy the target
-argmax for a truncated-geometric prefix, sampled requests draw from
-softmax((logits + N(0, 0.5^2)) / T)).
+stated on).  The draft model is out of scope: drafts are synthesised from the
+step's own target logits the way the workload recipe states (greedy requests
+copy the target argmax for a truncated-geometric prefix, sampled requests
+draw from softmax((logits + N(0, 0.5^2)) / T)).
+
+Other modes: --graph (the step as one HIP graph), --kv-cache e4m3, --tree
+binary, --flush (caches cleared before each step), --lm-operands equal (a
+power diagnostic), and the two device probes --hbm-ceiling and
+--mfma-ceiling, which print their own line instead of running the step.
 """
 from __future__ import annotations
 
