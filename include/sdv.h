@@ -175,7 +175,8 @@ int sd_get_device_error(const int32_t* dev_error, int32_t* code, void* stream);
  *
  * Supported: page_size 64; GQA bf16 (bf16 or E4M3 cache) with d_qk = d_v in
  * {64, 128} and (n_q_heads/n_kv_heads)*(K+1) <= 64; GQA f32 with d_qk = d_v
- * <= 256; MLA bf16 with d_qk = 576, d_v = 512.  Others return
+ * a divisor of 256 and a multiple of 4 (whole 16-byte rows); MLA bf16 with
+ * d_qk = 576, d_v = 512 and n_q_heads a multiple of 32.  Others return
  * SD_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct sd_attn_desc {
